@@ -1,0 +1,397 @@
+"""SageAttention2 quantized attention forward: plain, slow CPU oracle.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the benchmark's CPU
+baseline may import this module.  It shares no code with the GPU path and imports nothing
+from it; the GPU path never calls it.
+
+Pages cited (titles as they appear on the pages):
+  [SA2]   "SageAttention2: Efficient Attention with Thorough Outlier Smoothing and Per-thread
+          INT4 Quantization" (mlsanity.com paper page for arXiv 2411.10958), section
+          "Abstract (arXiv)".
+  [SA2c]  zhaifeiyue.github.io commentary on arXiv 2411.10958 (SageAttention2): the analysis
+          paragraphs on the paper's Sec. 3.4 (FP22 accumulator, two-level accumulation), on
+          per-thread quantization bound to the NVIDIA mma layout, and on smoothing.
+  [SA2pp] pith.science verdict on arXiv 2505.21136 (SageAttention2++), JSON keys
+          "key_machinery" (delta_P = max(P~)/P_r, per-channel delta_V = max|V|/V_r),
+          "core_discovery" (P_r, V_r ranges) and "supporting_citations" (online softmax,
+          FlashAttention tiling).
+
+What is computed, per (batch b, query head h); kv(h) = h div (H / Hkv):
+
+  O1  exact means.  Every fp16 value is an integer multiple of 2**-24, so x * 2**24 is an
+      exact int64 and the column sums are exact and order-free.  mean = RN32(RN64(sum) /
+      (n * 2**24)).  mu_K over all N keys; mu_Q over the valid rows of each Q block of bq rows.
+  O2  smoothing [SA2 abstract: smooth Q; title: outlier smoothing; SA2c: smoothing of K]:
+      gamma_K = RN32(K - mu_K), gamma_Q = RN32(Q - mu_Q[block]).
+  O3  K groups and codes [SA2 abstract: thread-level granularity; SA2c: the grouping follows
+      the matrix-instruction layout]: one scale per group; codes = clamp(rint(RN32(gamma *
+      RN32(R / amax))), -R, R), delta = RN32(amax / R); R = 127 (8-bit) or 7 (4-bit range).
+  O4  Q groups and codes: same rule with the Q grouping.
+  O5  Delta_S[qb, j] = sum_c mu_Q[qb, c] * gamma_K[j, c]  (fp64): Q smoothing moves the
+      mean of the block's queries out of the quantized product; this term adds it back.
+  O6  S_int = codes_Q . codes_K^T, exact integer.
+  O7  logits z = (S_int * delta_Q(i) * delta_K(j) + Delta_S[qb(i), j]) / sqrt(d); -inf above
+      the diagonal when causal (top-left aligned).
+  O8  V: per-channel amax over all N keys; delta_V = RN32(amax / V_r);
+      V_q = E4M3sat(RN32(V * RN32(V_r / amax))) [SA2pp key_machinery].
+  O9  online softmax over KV blocks of bk keys (FlashAttention tiling with the online
+      normalizer [SA2pp supporting_citations]): m' = max(m, blockmax z); alpha = e^(m - m');
+      p = e^(z - m'); l = l * alpha + sum p (unquantized p);
+      P~_q = E4M3sat(RN32(p * P_r)) (static range: within a block max p <= 1, so
+      delta_P = 1 / P_r [SA2pp key_machinery]); two-level accumulation [SA2 abstract;
+      SA2c on Sec. 3.4]: local = sum_j P~_q * V_q over the block (exact), acc = acc * alpha +
+      local.
+  O10 O = acc * delta_V[c] / (P_r * l).
+
+Readings where the pages are silent are listed with each function.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+from . import fp8
+
+F32 = np.float32
+F64 = np.float64
+
+
+# --------------------------------------------------------------------------------------
+# geometry
+# --------------------------------------------------------------------------------------
+@dataclass(frozen=True)
+class Geometry:
+    """Block sizes and quantization-group shapes.
+
+    A quantization group of rows (queries or keys) is the set of rows that share
+    (row div slice, (row mod period) div run); a group spans all d channels.
+    The defaults are the ones of the gfx950 kernel (one scale per MFMA lane):
+      * Q: per query row (slice 1) -- in S^T = K Q^T on the 32x32 integer MFMA every lane
+        column is one query;
+      * K: (KV block, (j mod 8) div 4) -- the 16 keys a lane accumulates per 32-key tile
+        are j = 8a + 4*(lane div 32) + r, so each lane sees one half of the block's keys.
+    """
+
+    bq: int = 128            # Q block: Q-smoothing block and workgroup tile
+    bk: int = 128            # KV block: online-softmax block and K quantization slice
+    q_slice: int = 1
+    q_period: int = 1
+    q_run: int = 1
+    k_slice: int = 128
+    k_period: int = 8
+    k_run: int = 4
+    p_range: float = 448.0   # P_r
+    v_range: float = 448.0   # V_r
+
+
+DEFAULT = Geometry()
+
+
+def qk_range(qk_bits: int) -> int:
+    """R: 127 for INT8 codes, 7 for INT4-range codes carried in int8 lanes [SA2 abstract]."""
+    if qk_bits == 8:
+        return 127
+    if qk_bits == 4:
+        return 7
+    raise ValueError("qk_bits must be 4 or 8")
+
+
+def group_ids(n: int, slice_: int, period: int, run: int) -> np.ndarray:
+    """Group id of rows 0..n-1: rows with equal (i div slice, (i mod period) div run)."""
+    i = np.arange(n, dtype=np.int64)
+    return (i // slice_) * period + (i % period) // run
+
+
+# --------------------------------------------------------------------------------------
+# O1 / O2: exact means and smoothing
+# --------------------------------------------------------------------------------------
+def fixed_point_colsum(x16: np.ndarray) -> np.ndarray:
+    """Exact column sums of an fp16 [n, d] array, in units of 2**-24, as int64."""
+    x16 = np.asarray(x16)
+    assert x16.dtype == np.float16
+    xi = (x16.astype(F64) * 2.0 ** 24).astype(np.int64)   # exact: |x * 2**24| < 2**40
+    return xi.sum(axis=0, dtype=np.int64)
+
+
+def exact_mean(x16: np.ndarray) -> np.ndarray:
+    """O1: RN32(RN64(exact column sum) / (n * 2**24)) of an fp16 [n, d] array.
+
+    Reading: the pages fix neither the order nor the precision of the mean; this rule makes
+    the result independent of summation order, so a parallel reduction can match it bit
+    for bit.
+    """
+    n = x16.shape[0]
+    s = fixed_point_colsum(x16)
+    return (s.astype(F64) / F64(n * 2.0 ** 24)).astype(F32)
+
+
+def smooth(x16: np.ndarray, mu: np.ndarray) -> np.ndarray:
+    """O2: gamma = RN32(fp32(x) - mu)."""
+    return (x16.astype(F32) - np.asarray(mu, dtype=F32)).astype(F32)
+
+
+# --------------------------------------------------------------------------------------
+# O3 / O4: grouped symmetric quantization
+# --------------------------------------------------------------------------------------
+def quantize_groups(gamma: np.ndarray, gid: np.ndarray, R: int):
+    """Symmetric per-group quantization of gamma [n, d] (fp32) to integer codes in [-R, R].
+
+    Returns (codes int8 [n, d], delta_row fp32 [n], amax_row fp32 [n]) where delta_row[i]
+    is the scale of row i's group.
+
+    Readings (pages silent): delta = RN32(amax / R); codes use the fp32 reciprocal
+    RN32(R / amax), then an fp32 product, then round-half-even, clamped to +-R.
+    A group whose amax is 0 gets delta = 0 and all-zero codes.
+    """
+    gamma = np.asarray(gamma, dtype=F32)
+    n = gamma.shape[0]
+    uniq, inv_idx = np.unique(gid, return_inverse=True)
+    row_amax = np.abs(gamma).max(axis=1) if gamma.shape[1] else np.zeros(n, F32)
+    gmax = np.zeros(len(uniq), dtype=F32)
+    np.maximum.at(gmax, inv_idx, row_amax.astype(F32))
+    delta_g = (gmax / F32(R)).astype(F32)
+    with np.errstate(divide="ignore"):
+        inv_g = np.where(gmax > 0, F32(R) / np.where(gmax > 0, gmax, F32(1)), F32(0)).astype(F32)
+    inv_row = inv_g[inv_idx]
+    prod = (gamma * inv_row[:, None]).astype(F32)
+    codes = np.clip(np.rint(prod), -R, R).astype(np.int8)
+    return codes, delta_g[inv_idx].astype(F32), gmax[inv_idx].astype(F32)
+
+
+# --------------------------------------------------------------------------------------
+# O8: V per-channel FP8
+# --------------------------------------------------------------------------------------
+def quantize_v(v16: np.ndarray, v_range: float):
+    """O8: per-channel FP8 E4M3 quantization of V [n, d] (fp16).
+
+    Returns (codes uint8 [n, d], delta_v fp32 [d], amax fp32 [d]).
+    """
+    vf = v16.astype(F32)
+    amax = np.abs(vf).max(axis=0) if vf.shape[0] else np.zeros(vf.shape[1], F32)
+    delta = (amax / F32(v_range)).astype(F32)
+    with np.errstate(divide="ignore"):
+        inv = np.where(amax > 0, F32(v_range) / np.where(amax > 0, amax, F32(1)), F32(0)).astype(F32)
+    prod = (vf * inv[None, :]).astype(F32)
+    codes = fp8.encode_sat(prod)
+    return codes, delta, amax.astype(F32)
+
+
+# --------------------------------------------------------------------------------------
+# prologue: everything that does not depend on the (query block, key block) pair
+# --------------------------------------------------------------------------------------
+@dataclass
+class Prologue:
+    B: int
+    H: int
+    Hkv: int
+    N: int
+    d: int
+    causal: bool
+    qk_bits: int
+    geom: Geometry
+    quant_qk: bool
+    quant_pv: bool
+    smooth_q: bool
+    smooth_k: bool
+    # per (b, kv head)
+    mu_k: np.ndarray = field(repr=False)       # f32 [B, Hkv, d]
+    gamma_k: np.ndarray = field(repr=False)    # f32 [B, Hkv, N, d]
+    k_codes: np.ndarray = field(repr=False)    # i8  [B, Hkv, N, d]
+    k_delta: np.ndarray = field(repr=False)    # f32 [B, Hkv, N]  (scale of each key's group)
+    v_codes: np.ndarray = field(repr=False)    # u8  [B, Hkv, N, d]
+    v_delta: np.ndarray = field(repr=False)    # f32 [B, Hkv, d]
+    v_amax: np.ndarray = field(repr=False)     # f32 [B, Hkv, d]
+    v16: np.ndarray = field(repr=False)        # original V (for the unquantized-PV mode)
+    # per (b, q head)
+    mu_q: np.ndarray = field(repr=False)       # f32 [B, H, nqb, d]
+    gamma_q: np.ndarray = field(repr=False)    # f32 [B, H, N, d]
+    q_codes: np.ndarray = field(repr=False)    # i8  [B, H, N, d]
+    q_delta: np.ndarray = field(repr=False)    # f32 [B, H, N]
+
+    @property
+    def nqb(self) -> int:
+        return -(-self.N // self.geom.bq)
+
+    @property
+    def nkb(self) -> int:
+        return -(-self.N // self.geom.bk)
+
+    def kv_head(self, h: int) -> int:
+        return h // (self.H // self.Hkv)
+
+
+def prologue(q, k, v, causal: bool = False, qk_bits: int = 8, geom: Geometry = DEFAULT, *,
+             quant_qk: bool = True, quant_pv: bool = True, smooth_q: bool = True,
+             smooth_k: bool = True) -> Prologue:
+    """Steps O1-O4 and O8 on fp16 inputs q [B,H,N,d], k/v [B,Hkv,N,d] (numpy float16).
+
+    The switches turn parts of the method off; they exist so that tests can reduce the
+    oracle to textbook attention (all off) and check each part against it.
+    """
+    q = np.asarray(q)
+    k = np.asarray(k)
+    v = np.asarray(v)
+    assert q.dtype == np.float16 and k.dtype == np.float16 and v.dtype == np.float16
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    assert k.shape == (B, Hkv, N, d) and v.shape == (B, Hkv, N, d) and H % Hkv == 0
+    R = qk_range(qk_bits)
+    g = geom
+    nqb = -(-N // g.bq)
+
+    mu_k = np.zeros((B, Hkv, d), F32)
+    gamma_k = np.zeros((B, Hkv, N, d), F32)
+    k_codes = np.zeros((B, Hkv, N, d), np.int8)
+    k_delta = np.zeros((B, Hkv, N), F32)
+    v_codes = np.zeros((B, Hkv, N, d), np.uint8)
+    v_delta = np.zeros((B, Hkv, d), F32)
+    v_amax = np.zeros((B, Hkv, d), F32)
+    kgid = group_ids(N, g.k_slice, g.k_period, g.k_run)
+    for b in range(B):
+        for hk in range(Hkv):
+            if smooth_k:
+                mu_k[b, hk] = exact_mean(k[b, hk])
+            gamma_k[b, hk] = smooth(k[b, hk], mu_k[b, hk])
+            k_codes[b, hk], k_delta[b, hk], _ = quantize_groups(gamma_k[b, hk], kgid, R)
+            v_codes[b, hk], v_delta[b, hk], v_amax[b, hk] = quantize_v(v[b, hk], g.v_range)
+
+    mu_q = np.zeros((B, H, nqb, d), F32)
+    gamma_q = np.zeros((B, H, N, d), F32)
+    q_codes = np.zeros((B, H, N, d), np.int8)
+    q_delta = np.zeros((B, H, N), F32)
+    qgid = group_ids(N, g.q_slice, g.q_period, g.q_run)
+    for b in range(B):
+        for h in range(H):
+            for qb in range(nqb):
+                r0, r1 = qb * g.bq, min(N, (qb + 1) * g.bq)
+                if smooth_q:
+                    mu_q[b, h, qb] = exact_mean(q[b, h, r0:r1])
+                gamma_q[b, h, r0:r1] = smooth(q[b, h, r0:r1], mu_q[b, h, qb])
+            q_codes[b, h], q_delta[b, h], _ = quantize_groups(gamma_q[b, h], qgid, R)
+
+    return Prologue(B, H, Hkv, N, d, bool(causal), qk_bits, g, quant_qk, quant_pv, smooth_q,
+                    smooth_k, mu_k, gamma_k, k_codes, k_delta, v_codes, v_delta, v_amax, v,
+                    mu_q, gamma_q, q_codes, q_delta)
+
+
+# --------------------------------------------------------------------------------------
+# O5 / O6 / O7
+# --------------------------------------------------------------------------------------
+def delta_s(pro: Prologue, b: int, h: int, qb: int) -> np.ndarray:
+    """O5: Delta_S[qb, :] = mu_Q[qb] . gamma_K^T over all N keys, fp64 [N]."""
+    hk = pro.kv_head(h)
+    return pro.gamma_k[b, hk].astype(F64) @ pro.mu_q[b, h, qb].astype(F64)
+
+
+def scores_int(pro: Prologue, b: int, h: int, rows: slice, keys: slice) -> np.ndarray:
+    """O6: exact integer S_int[rows, keys] = codes_Q . codes_K^T (int64).
+
+    The fp64 product is exact: every partial sum is an integer below 127*127*d < 2**53.
+    """
+    hk = pro.kv_head(h)
+    qc = pro.q_codes[b, h, rows].astype(F64)
+    kc = pro.k_codes[b, hk, keys].astype(F64)
+    return (qc @ kc.T).astype(np.int64)
+
+
+def logits(pro: Prologue, b: int, h: int, qb: int) -> np.ndarray:
+    """O7: fp64 logits of the rows of Q block qb against all N keys (masked with -inf)."""
+    g = pro.geom
+    hk = pro.kv_head(h)
+    r0, r1 = qb * g.bq, min(pro.N, (qb + 1) * g.bq)
+    if pro.quant_qk:
+        s = scores_int(pro, b, h, slice(r0, r1), slice(0, pro.N)).astype(F64)
+        s = s * pro.q_delta[b, h, r0:r1].astype(F64)[:, None] * pro.k_delta[b, hk].astype(F64)[None, :]
+    else:
+        s = pro.gamma_q[b, h, r0:r1].astype(F64) @ pro.gamma_k[b, hk].astype(F64).T
+    z = (s + delta_s(pro, b, h, qb)[None, :]) / math.sqrt(pro.d)
+    if pro.causal:
+        i = np.arange(r0, r1)[:, None]
+        j = np.arange(pro.N)[None, :]
+        z = np.where(j > i, -np.inf, z)
+    return z
+
+
+# --------------------------------------------------------------------------------------
+# O9 / O10
+# --------------------------------------------------------------------------------------
+def attend_block(pro: Prologue, b: int, h: int, qb: int, return_state: bool = False):
+    """O9-O10 for the rows of Q block qb: output fp64 [rows, d].
+
+    Reading (pages silent): the row sum l accumulates the unquantized p; only the PV
+    operand is quantized.  Blocks are visited in ascending key order.
+    """
+    g = pro.geom
+    hk = pro.kv_head(h)
+    z = logits(pro, b, h, qb)
+    rows = z.shape[0]
+    d = pro.d
+    if pro.quant_pv:
+        vq = fp8.decode(pro.v_codes[b, hk])            # exact fp64 values of the codes
+        p_r = F64(g.p_range)
+        vscale = pro.v_delta[b, hk].astype(F64)
+    else:
+        vq = pro.v16[b, hk].astype(F64)
+        p_r = F64(1.0)
+        vscale = np.ones(d, F64)
+    m = np.full(rows, -np.inf)
+    l = np.zeros(rows)
+    acc = np.zeros((rows, d))
+    for kb in range(pro.nkb):
+        c0, c1 = kb * g.bk, min(pro.N, (kb + 1) * g.bk)
+        zb = z[:, c0:c1]
+        m_new = np.maximum(m, zb.max(axis=1))
+        finite = np.isfinite(m_new)
+        alpha = np.where(np.isfinite(m), np.exp(m - np.where(finite, m_new, 0.0)), 0.0)
+        p = np.where(finite[:, None], np.exp(zb - np.where(finite, m_new, 0.0)[:, None]), 0.0)
+        l = l * alpha + p.sum(axis=1)
+        if pro.quant_pv:
+            pt = fp8.round_sat((p * p_r).astype(F32))     # P~_q = E4M3sat(RN32(p * P_r))
+        else:
+            pt = p
+        local = pt @ vq[c0:c1]                             # block-local accumulation
+        acc = acc * alpha[:, None] + local                 # global accumulation
+        m = m_new
+    out = acc * vscale[None, :] / (p_r * l[:, None])
+    if return_state:
+        return out, m, l
+    return out
+
+
+def sage_attention(q, k, v, causal: bool = False, qk_bits: int = 8, geom: Geometry = DEFAULT,
+                   **switches) -> np.ndarray:
+    """Whole forward pass: fp64 O [B, H, N, d] (the GPU rounds it to fp16)."""
+    pro = prologue(q, k, v, causal, qk_bits, geom, **switches)
+    out = np.zeros((pro.B, pro.H, pro.N, pro.d))
+    for b in range(pro.B):
+        for h in range(pro.H):
+            for qb in range(pro.nqb):
+                r0, r1 = qb * geom.bq, min(pro.N, (qb + 1) * geom.bq)
+                out[b, h, r0:r1] = attend_block(pro, b, h, qb)
+    return out
+
+
+# --------------------------------------------------------------------------------------
+# accuracy reference
+# --------------------------------------------------------------------------------------
+def exact_attention(q, k, v, causal: bool = False) -> np.ndarray:
+    """softmax(Q K^T / sqrt(d)) V in fp64 (two-pass softmax), GQA by h div (H / Hkv)."""
+    q = np.asarray(q).astype(F64)
+    k = np.asarray(k).astype(F64)
+    v = np.asarray(v).astype(F64)
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    out = np.zeros((B, H, N, d))
+    for b in range(B):
+        for h in range(H):
+            hk = h // (H // Hkv)
+            s = q[b, h] @ k[b, hk].T / math.sqrt(d)
+            if causal:
+                s = np.where(np.arange(N)[None, :] > np.arange(N)[:, None], -np.inf, s)
+            s = s - s.max(axis=1, keepdims=True)
+            e = np.exp(s)
+            out[b, h] = (e / e.sum(axis=1, keepdims=True)) @ v[b, hk]
+    return out

@@ -1,0 +1,91 @@
+"""Seeded synthetic inputs for the quantized attention forward.
+
+This module only draws random tensors: it holds none of the method's arithmetic, and both
+the CPU oracle's tests and the GPU path's tests/benchmark take their inputs from here.
+
+The shapes and value structure stand in for the workloads the pages describe (the real
+models' activations are not available): LLM prefill with long causal context and outlier
+channels in Q/K, video-DiT attention with a short text prefix and a long video sequence,
+and a kernel sweep at N = 8K, d = 128.  Recipe (all configs):
+
+  rng = numpy.random.default_rng(seed)        (PCG64)
+  draw order: q, k, v base ~ N(0, 1) (float32, BHND); then row scaling (text prefix);
+  then the per-(head, channel) K bias; then the per-(head, channel) Q bias; then the
+  outlier (head, channel) mask; finally cast to fp16 with round-to-nearest-even.
+  Biases have shape [1, heads, 1, d]: shared by batch and tokens.  V gets no bias.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    Hkv: int
+    N: int
+    d: int
+    causal: bool
+    qk_bits: int
+    k_bias_std: float = 4.0
+    q_bias_std: float = 0.0
+    text_tokens: int = 0          # leading rows drawn with std text_std instead of 1
+    text_std: float = 1.0
+    outlier_frac: float = 0.0     # fraction of (head, channel) pairs of Q and K scaled
+    outlier_scale: float = 1.0
+
+    @property
+    def ops(self) -> float:
+        """Numerator of the effective-TOPS metric: 4*B*H*N^2*d, halved when causal."""
+        o = 4.0 * self.B * self.H * self.N * self.N * self.d
+        return o / 2 if self.causal else o
+
+
+WORKLOADS = {
+    # small parity case: non-causal MHA, K outlier channels, INT8 QK + FP8 PV
+    "tiny": Workload("tiny", 1, 2, 2, 256, 64, False, 8),
+    # kernel sweep point: N = 8K, d = 128, K and Q channel biases
+    "bench": Workload("bench", 1, 16, 16, 8192, 128, False, 8, q_bias_std=1.0),
+    # LLM prefill: causal, 1% of (head, channel) pairs of Q and K scaled x10, INT4-range QK
+    "llm": Workload("llm", 1, 32, 32, 16384, 128, True, 4, q_bias_std=1.0,
+                    outlier_frac=0.01, outlier_scale=10.0),
+    # video DiT: 226 text tokens (std 2) then 17550 video tokens (std 1), d = 64
+    "dit": Workload("dit", 2, 30, 30, 17776, 64, False, 8, text_tokens=226, text_std=2.0),
+    # long-context causal GQA: 32 query heads over 8 kv heads, N = 96K
+    "gqa": Workload("gqa", 1, 32, 8, 98304, 128, True, 8),
+}
+
+
+def custom(B, H, Hkv, N, d, causal=False, qk_bits=8, **kw) -> Workload:
+    return Workload("custom", B, H, Hkv, N, d, causal, qk_bits, **kw)
+
+
+def make_inputs(w: Workload | str, seed: int = 0):
+    """q [B,H,N,d], k/v [B,Hkv,N,d] as numpy float16, drawn by the recipe above."""
+    if isinstance(w, str):
+        w = WORKLOADS[w]
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((w.B, w.H, w.N, w.d), dtype=np.float32)
+    k = rng.standard_normal((w.B, w.Hkv, w.N, w.d), dtype=np.float32)
+    v = rng.standard_normal((w.B, w.Hkv, w.N, w.d), dtype=np.float32)
+    if w.text_tokens:
+        t = min(w.text_tokens, w.N)
+        for x in (q, k, v):
+            x[:, :, :t, :] *= np.float32(w.text_std)
+    if w.k_bias_std:
+        k += (w.k_bias_std * rng.standard_normal((1, w.Hkv, 1, w.d))).astype(np.float32)
+    if w.q_bias_std:
+        q += (w.q_bias_std * rng.standard_normal((1, w.H, 1, w.d))).astype(np.float32)
+    if w.outlier_frac:
+        n_pairs = int(round(w.outlier_frac * w.H * w.d))
+        pick = rng.choice(w.H * w.d, n_pairs, replace=False)
+        for p in pick:
+            h, c = divmod(int(p), w.d)
+            q[:, h, :, c] *= np.float32(w.outlier_scale)
+            k[:, h * w.Hkv // w.H, :, c] *= np.float32(w.outlier_scale)
+    return q.astype(np.float16), k.astype(np.float16), v.astype(np.float16)

@@ -1,0 +1,134 @@
+/*
+ * sage_attn.h -- C ABI of the MI355X (gfx950) SageAttention2 quantized attention forward.
+ *
+ * Pages cited:
+ *   [SA2]   "SageAttention2: Efficient Attention with Thorough Outlier Smoothing and
+ *           Per-thread INT4 Quantization" (mlsanity.com page for arXiv 2411.10958),
+ *           section "Abstract (arXiv)".
+ *   [SA2c]  zhaifeiyue.github.io commentary on arXiv 2411.10958: the paragraphs on the
+ *           paper's Sec. 3.4 (two-level accumulation) and on per-thread quantization.
+ *   [SA2pp] pith.science verdict on arXiv 2505.21136 (SageAttention2++), JSON keys
+ *           "key_machinery" and "supporting_citations".
+ *   [BLOG]  "SageAttention：大模型量化注意力加速实践指南" (blog.gitcode.com), sections on the
+ *           core API call and precision control: the method is a drop-in for PyTorch's
+ *           scaled_dot_product_attention selected by a head_dim / is_causal / quant mode.
+ *
+ * What the library computes: O = softmax(Q K^T / sqrt(d)) V, approximated as in [SA2]:
+ * K is smoothed by its per-channel mean over tokens, Q by its per-block mean with the
+ * mean(Q) . gamma(K)^T term added back in fp32; smoothed Q and K are quantized to INT8
+ * (qk_bits = 8, codes in [-127, 127]) or to INT4-range values (qk_bits = 4, codes in
+ * [-7, 7] carried in int8 lanes) with one scale per MFMA lane group; QK^T runs on the
+ * integer MFMA with exact int32 accumulation; an online softmax produces P~, which is
+ * quantized to FP8 E4M3 with the static range P_r = 448; V is quantized per channel to
+ * FP8 E4M3 with V_r = 448 [SA2pp key_machinery]; P~V runs on the FP8 MFMA, each KV block
+ * into a zeroed block-local accumulator that is then folded into a global fp32
+ * accumulator [SA2], [SA2c].
+ *
+ * Tensors (all device pointers, caller-owned, never freed or retained by the library):
+ *   q, o : fp16, contiguous [B, H, N, d]           (o is overwritten)
+ *   k, v : fp16, contiguous [B, Hkv, N, d]; query head h reads kv head h / (H / Hkv)
+ *   causal: 0 or 1; 1 masks key j > query i (top-left aligned, N_q == N_k)
+ *   d    : 64 or 128; softmax scale 1/sqrt(d)
+ *   workspace: device memory of at least sage_attn_workspace_bytes(...) bytes, 256-byte
+ *          aligned; its contents on entry are ignored.
+ *   stream: a hipStream_t (NULL = the legacy default stream).  Every call is stream
+ *          ordered and returns after enqueueing; the library makes no device
+ *          synchronisation, allocates no memory and keeps no state between calls, so
+ *          concurrent calls with distinct workspaces are safe.
+ *
+ * Errors: every argument check happens before anything is enqueued; on error nothing is
+ * enqueued and a negative status is returned.  SAGE_ERR_HIP reports a failed HIP call or
+ * launch; sage_last_error() then holds the HIP message for the calling thread.
+ */
+#ifndef SAGE_ATTN_H
+#define SAGE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SAGE_OK 0
+#define SAGE_ERR_INVALID_ARG (-1) /* null pointer, size < 1, H % Hkv != 0, size overflow  */
+#define SAGE_ERR_UNSUPPORTED (-2) /* d not in {64, 128}, qk_bits not in {4, 8}, N > 2^23  */
+#define SAGE_ERR_WORKSPACE (-3)   /* workspace missing, too small or not 256-byte aligned */
+#define SAGE_ERR_HIP (-4)         /* a HIP runtime call or kernel launch failed          */
+
+/*
+ * Compile-time constants of this build.  The CPU oracle takes its geometry from here.
+ *   bq      : query rows per workgroup and per Q-smoothing block (mu_Q is per bq rows)
+ *   bk      : keys per KV block: online-softmax block, block-local PV accumulation span,
+ *             and the slice of K sharing quantization scales
+ *   A quantization group of rows is the set sharing (row / slice, (row % period) / run):
+ *   q_*     : Q groups; (1, 1, 1) = one scale per query row.  In S^T = K Q^T on the
+ *             32x32 integer MFMA each lane holds one query column [SA2 thread granularity].
+ *   k_*     : K groups; (bk, 8, 4): keys 8a + 4h + r (r < 4) of a KV block share the
+ *             scale of lane half h, the keys one lane accumulates.
+ *   p_range, v_range : static FP8 ranges P_r, V_r
+ *   fp8_format : 1 = OCP E4M3FN (max 448, RNE)
+ */
+typedef struct sage_config {
+  int version;
+  int bq, bk;
+  int q_slice, q_period, q_run;
+  int k_slice, k_period, k_run;
+  float p_range, v_range;
+  int fp8_format;
+} sage_config_t;
+
+int sage_get_config(sage_config_t* out);
+
+/* Bytes of workspace sage_attn_fwd needs for this problem (written to *bytes). */
+int sage_attn_workspace_bytes(int B, int H, int Hkv, int N, int d, int causal, int qk_bits,
+                              size_t* bytes);
+
+/*
+ * The whole forward pass: quantize/smooth prologue kernels, then the fused attention
+ * kernel, all enqueued on `stream`.  Replaces F.scaled_dot_product_attention(q, k, v,
+ * is_causal=causal) for fp16 inputs [BLOG core API; SA2].
+ */
+int sage_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, int Hkv,
+                  int N, int d, int causal, int qk_bits, void* workspace,
+                  size_t workspace_bytes, void* stream);
+
+/*
+ * Test/debug: run the prologue only and copy its results, in plain layouts, to the
+ * caller's device buffers (any pointer may be NULL to skip it):
+ *   mu_k     fp32 [B, Hkv, d]            mean of K over all N keys
+ *   k_codes  int8 [B, Hkv, N, d]         quantized smoothed K
+ *   k_scales fp32 [B, Hkv, N]            scale of each key's group
+ *   v_codes  uint8 [B, Hkv, N, d]        FP8 E4M3 codes of V
+ *   v_scales fp32 [B, Hkv, d]            delta_V = max|V[:, c]| / V_r
+ *   mu_q     fp32 [B, H, ceil(N/bq), d]  per-block mean of Q
+ *   q_codes  int8 [B, H, N, d]           quantized smoothed Q
+ *   q_scales fp32 [B, H, N]              scale of each query's group
+ *   delta_s  fp32 [B, H, ceil(N/bq), N] mu_Q . gamma_K^T (natural units, not log2)
+ * Same tensor/workspace/stream rules as sage_attn_fwd.
+ */
+int sage_quant_debug(const void* q, const void* k, const void* v, int B, int H, int Hkv, int N,
+                     int d, int causal, int qk_bits, void* workspace, size_t workspace_bytes,
+                     void* stream, void* mu_k, void* k_codes, void* k_scales, void* v_codes,
+                     void* v_scales, void* mu_q, void* q_codes, void* q_scales, void* delta_s);
+
+/*
+ * Test/debug: run the prologue, then the attention kernel's own integer-MFMA QK^T code
+ * path for query block qb of (b, h) against KV block kb, and copy the raw int32
+ * accumulators to tile_out (device, int32 [bq, bk], row = query, column = key; rows
+ * past N and keys past N hold the products of the zero padding codes).
+ */
+int sage_qk_tile_debug(const void* q, const void* k, const void* v, int B, int H, int Hkv, int N,
+                       int d, int causal, int qk_bits, void* workspace, size_t workspace_bytes,
+                       void* stream, int b, int h, int qb, int kb, int32_t* tile_out);
+
+/* Static text for a status code. */
+const char* sage_status_string(int status);
+
+/* Detail of the last SAGE_ERR_HIP on the calling thread ("" if none). */
+const char* sage_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SAGE_ATTN_H */

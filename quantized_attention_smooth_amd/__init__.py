@@ -1,0 +1,186 @@
+"""MI355X (gfx950) SageAttention2 quantized attention forward.
+
+A thin Python binding over the C ABI in include/sage_attn.h (libsage_mi355x.so, built by
+quantized_attention_smooth_amd.build).  Every step of the computation runs in the library's
+HIP kernels; this module only checks arguments, allocates the output and the workspace with
+torch, and passes raw device pointers and the current stream.  There is no fallback: if the
+library is missing or fails to load, importing this package raises ImportError.
+
+    from quantized_attention_smooth_amd import sageattn
+    o = sageattn(q, k, v, is_causal=True, qk_bits=8)   # like F.scaled_dot_product_attention
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["sageattn", "fwd", "workspace_bytes", "get_config", "quant_debug", "qk_tile_debug",
+           "LIB_PATH", "SageError"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsage_mi355x.so")
+
+SAGE_OK = 0
+SAGE_ERR_INVALID_ARG = -1
+SAGE_ERR_UNSUPPORTED = -2
+SAGE_ERR_WORKSPACE = -3
+SAGE_ERR_HIP = -4
+
+#: every symbol include/sage_attn.h declares
+EXPORTS = ("sage_get_config", "sage_attn_workspace_bytes", "sage_attn_fwd", "sage_quant_debug",
+           "sage_qk_tile_debug", "sage_status_string", "sage_last_error")
+
+
+class SageConfig(ctypes.Structure):
+    _fields_ = [("version", ctypes.c_int), ("bq", ctypes.c_int), ("bk", ctypes.c_int),
+                ("q_slice", ctypes.c_int), ("q_period", ctypes.c_int), ("q_run", ctypes.c_int),
+                ("k_slice", ctypes.c_int), ("k_period", ctypes.c_int), ("k_run", ctypes.c_int),
+                ("p_range", ctypes.c_float), ("v_range", ctypes.c_float), ("fp8_format", ctypes.c_int)]
+
+
+class SageError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m quantized_attention_smooth_amd.build`")
+    try:
+        lib = ctypes.CDLL(LIB_PATH)
+    except OSError as e:
+        raise ImportError(f"cannot load {LIB_PATH}: {e}") from e
+    P, I, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.sage_get_config.argtypes = [ctypes.POINTER(SageConfig)]
+    lib.sage_attn_workspace_bytes.argtypes = [I, I, I, I, I, I, I, ctypes.POINTER(S)]
+    lib.sage_attn_fwd.argtypes = [P, P, P, P, I, I, I, I, I, I, I, P, S, P]
+    lib.sage_quant_debug.argtypes = [P, P, P, I, I, I, I, I, I, I, P, S, P] + [P] * 9
+    lib.sage_qk_tile_debug.argtypes = [P, P, P, I, I, I, I, I, I, I, P, S, P, I, I, I, I, P]
+    lib.sage_status_string.argtypes = [I]
+    lib.sage_status_string.restype = ctypes.c_char_p
+    lib.sage_last_error.argtypes = []
+    lib.sage_last_error.restype = ctypes.c_char_p
+    for name in ("sage_get_config", "sage_attn_workspace_bytes", "sage_attn_fwd", "sage_quant_debug",
+                 "sage_qk_tile_debug"):
+        getattr(lib, name).restype = ctypes.c_int
+    return lib
+
+
+_lib = _load()
+
+
+def _check(status: int) -> None:
+    if status == SAGE_OK:
+        return
+    text = _lib.sage_status_string(status).decode()
+    if status == SAGE_ERR_HIP:
+        raise SageError(status, f"{text}: {_lib.sage_last_error().decode()}")
+    if status == SAGE_ERR_UNSUPPORTED:
+        raise NotImplementedError(text)
+    raise ValueError(text)
+
+
+def get_config() -> dict:
+    cfg = SageConfig()
+    _check(_lib.sage_get_config(ctypes.byref(cfg)))
+    return {name: getattr(cfg, name) for name, _ in SageConfig._fields_}
+
+
+def workspace_bytes(B: int, H: int, Hkv: int, N: int, d: int, causal: bool, qk_bits: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(_lib.sage_attn_workspace_bytes(B, H, Hkv, N, d, int(causal), qk_bits, ctypes.byref(n)))
+    return n.value
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t) -> ctypes.c_void_p:
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _shapes(q, k, v):
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [B, heads, N, d]")
+    if q.dtype != torch.float16 or k.dtype != torch.float16 or v.dtype != torch.float16:
+        raise ValueError("q, k, v must be float16")
+    if not (q.is_cuda and k.is_cuda and v.is_cuda) or not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must be on the same GPU")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous (layout [B, heads, N, d])")
+    B, H, N, d = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[2] != N or k.shape[3] != d:
+        raise ValueError(f"k/v shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
+    return B, H, k.shape[1], N, d
+
+
+def alloc_workspace(nbytes: int, device) -> torch.Tensor:
+    """A uint8 device tensor whose data pointer is 256-byte aligned."""
+    buf = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+    off = (-buf.data_ptr()) % 256
+    return buf[off:off + nbytes]
+
+
+def fwd(q, k, v, o, workspace, is_causal: bool = False, qk_bits: int = 8) -> None:
+    """sage_attn_fwd on caller-provided tensors (o and workspace are written)."""
+    B, H, Hkv, N, d = _shapes(q, k, v)
+    if o.shape != q.shape or o.dtype != torch.float16 or not o.is_contiguous() or o.device != q.device:
+        raise ValueError("o must be a contiguous float16 tensor shaped like q on q's device")
+    _check(_lib.sage_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, Hkv, N, d, int(is_causal), qk_bits,
+                              _ptr(workspace), workspace.numel(), _stream(q.device)))
+
+
+def sageattn(q, k, v, attn_mask=None, dropout_p: float = 0.0, is_causal: bool = False, scale=None,
+             qk_bits: int = 8, workspace=None):
+    """Quantized drop-in for F.scaled_dot_product_attention(q, k, v, is_causal=...).
+
+    q [B, H, N, d], k/v [B, Hkv, N, d], fp16, contiguous; d in {64, 128}; qk_bits 8 (INT8
+    codes) or 4 (INT4-range codes).  Grouped-query attention maps head h to kv head
+    h // (H // Hkv).  Returns fp16 [B, H, N, d].
+    """
+    if attn_mask is not None or dropout_p != 0.0 or scale is not None:
+        raise NotImplementedError("attn_mask, dropout and custom scale are not supported")
+    B, H, Hkv, N, d = _shapes(q, k, v)
+    nbytes = workspace_bytes(B, H, Hkv, N, d, is_causal, qk_bits)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = alloc_workspace(nbytes, q.device)
+    o = torch.empty_like(q)
+    fwd(q, k, v, o, workspace, is_causal, qk_bits)
+    return o
+
+
+def quant_debug(q, k, v, is_causal: bool = False, qk_bits: int = 8) -> dict:
+    """Prologue outputs in plain layouts (see sage_quant_debug in include/sage_attn.h)."""
+    B, H, Hkv, N, d = _shapes(q, k, v)
+    nqb = -(-N // get_config()["bq"])
+    dev = q.device
+    out = {
+        "mu_k": torch.empty(B, Hkv, d, dtype=torch.float32, device=dev),
+        "k_codes": torch.empty(B, Hkv, N, d, dtype=torch.int8, device=dev),
+        "k_scales": torch.empty(B, Hkv, N, dtype=torch.float32, device=dev),
+        "v_codes": torch.empty(B, Hkv, N, d, dtype=torch.uint8, device=dev),
+        "v_scales": torch.empty(B, Hkv, d, dtype=torch.float32, device=dev),
+        "mu_q": torch.empty(B, H, nqb, d, dtype=torch.float32, device=dev),
+        "q_codes": torch.empty(B, H, N, d, dtype=torch.int8, device=dev),
+        "q_scales": torch.empty(B, H, N, dtype=torch.float32, device=dev),
+        "delta_s": torch.empty(B, H, nqb, N, dtype=torch.float32, device=dev),
+    }
+    ws = alloc_workspace(workspace_bytes(B, H, Hkv, N, d, is_causal, qk_bits), dev)
+    names = ("mu_k", "k_codes", "k_scales", "v_codes", "v_scales", "mu_q", "q_codes", "q_scales", "delta_s")
+    _check(_lib.sage_quant_debug(_ptr(q), _ptr(k), _ptr(v), B, H, Hkv, N, d, int(is_causal), qk_bits, _ptr(ws),
+                                 ws.numel(), _stream(dev), *[_ptr(out[n]) for n in names]))
+    return out
+
+
+def qk_tile_debug(q, k, v, b: int, h: int, qb: int, kb: int, is_causal: bool = False, qk_bits: int = 8):
+    """Raw int32 S tile [bq, bk] of the attention kernel's integer MFMA path."""
+    B, H, Hkv, N, d = _shapes(q, k, v)
+    cfg = get_config()
+    tile = torch.empty(cfg["bq"], cfg["bk"], dtype=torch.int32, device=q.device)
+    ws = alloc_workspace(workspace_bytes(B, H, Hkv, N, d, is_causal, qk_bits), q.device)
+    _check(_lib.sage_qk_tile_debug(_ptr(q), _ptr(k), _ptr(v), B, H, Hkv, N, d, int(is_causal), qk_bits, _ptr(ws),
+                                   ws.numel(), _stream(q.device), b, h, qb, kb, _ptr(tile)))
+    return tile

@@ -1,0 +1,330 @@
+// Fused SageAttention2 attention kernel for gfx950 (CDNA4).
+//
+// Page "SageAttention2: Efficient Attention with Thorough Outlier Smoothing and Per-thread
+// INT4 Quantization" (mlsanity.com, arXiv 2411.10958), section "Abstract (arXiv)": QK^T on
+// low-bit integer codes with thread-granular scales, P~ and V in FP8, two-level accumulation
+// of P~V.  zhaifeiyue.github.io commentary on arXiv 2411.10958: the paper's Sec. 3.4 finds the
+// FP8 matrix-instruction accumulator narrower than fp32 and accumulates each block locally
+// before an fp32 global sum; per-thread scales must follow the matrix-instruction layout.
+// pith.science verdict on arXiv 2505.21136, keys "key_machinery" (static delta_P = 1/P_r
+// since max P~ = 1 per block; per-channel delta_V) and "supporting_citations" (online
+// softmax and FlashAttention tiling).
+//
+// Design (one workgroup = 128 queries of one (b, h); 4 waves x 32 queries):
+//   * S^T = K Q^T on v_mfma_i32_32x32x32_i8 (the full-rate int8 shape on gfx950): A = K tile
+//     from LDS, B = the wave's 32 query rows held in VGPRs for the whole KV loop.  Lane l owns
+//     query column i = l % 32 and keys 8a + 4(l / 32) + r of every 32-key tile, so one
+//     delta_Q * delta_K product dequantizes all of a lane's accumulators.
+//   * The S^T accumulators already sit in the B-operand layout of v_mfma_f32_32x32x64_f8f6f4
+//     (lane l: column l % 32, 32 consecutive k-slots): P~ goes from registers to the FP8 MFMA
+//     with no LDS round trip; V^T is pre-permuted by the prologue into the same k-slot order.
+//   * Each 128-key block's P~V accumulates from zero (two 64-deep MFMAs), then is folded
+//     into the fp32 output accumulator: O = O * alpha + local.  On gfx950 the FP8 MFMA also
+//     sums its products with reduced internal precision, so the block-local step bounds that
+//     error to one block, as on the hardware the pages target.
+//   * K/V code tiles stream HBM -> LDS with direct-to-LDS loads (global_load_lds_dwordx4),
+//     double buffered, 16-byte chunks XOR-swizzled against LDS bank conflicts.
+//   * Workgroup ids are remapped so each XCD (own L2) works through whole heads; causal
+//     grids start with the longest (diagonal-most) query blocks.
+#include "sage_internal.h"
+
+namespace sage {
+
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+constexpr float kLog2Pr = 8.807354922057604f;   // log2(448)
+
+struct AttnArgs {
+  const int8_t* qcodes;
+  const int8_t* kcodes;
+  const uint8_t* vcodes;
+  const float* qscale;
+  const float* kscale;
+  const float* vscale;
+  const float* ds;
+  __half* o;
+  int B, H, Hkv, N, Npad, nqb, nkb;
+  float k2;             // log2(e) / sqrt(d)
+  int dbg_b, dbg_h, dbg_qb, dbg_kb;
+  int32_t* dbg_out;
+};
+
+template <int D>
+struct Smem {
+  int8_t k[2][BK * D];       // K tile rows, 16-byte chunks swizzled
+  uint8_t v[2][BK * D];      // [64-key group][channel][64 slots], 16-byte chunks swizzled
+  float ds[2][BK];
+};
+
+// swizzle of the 16-byte chunk index inside a K row (row = key within the tile)
+template <int D>
+__device__ inline int kswz(int row) {
+  return D == 128 ? (row & 7) : ((row >> 1) & 3);
+}
+// swizzle of the 16-byte chunk inside a 64-byte V^T row (c = channel)
+__device__ inline int vswz(int c) { return (c >> 1) & 3; }
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int D>
+__device__ inline void issue_tile(const AttnArgs& a, Smem<D>& sm, int st, size_t bkv, size_t bh, int qb, int kb,
+                                  int w, int lane) {
+  constexpr int CPR = D / 16;                 // 16-byte chunks per K row
+  constexpr int NI = BK * D / 16 / 64 / WAVES; // direct-to-LDS instructions per wave per tile
+  const int8_t* kbase = a.kcodes + (bkv * a.Npad + (size_t)kb * BK) * D;
+  const uint8_t* vbase = a.vcodes + (bkv * (size_t)(a.Npad / VGROUP) + (size_t)kb * 2) * D * VGROUP;
+#pragma unroll
+  for (int m = 0; m < NI; ++m) {
+    const int blk = m * WAVES + w;            // which 1 KB of the tile this wave writes
+    const int p = blk * 64 + lane;            // 16-byte chunk index in LDS
+    {
+      const int row = p / CPR, pc = p % CPR;
+      const int lc = pc ^ kswz<D>(row);
+      __builtin_amdgcn_global_load_lds(kbase + (size_t)row * D + lc * 16,
+                                       (lds_void*)(sm.k[st] + blk * 1024), 16, 0, 0);
+    }
+    {
+      const int row = p >> 2, pc = p & 3;     // row = group * D + channel
+      const int c = row % D;
+      const int lc = pc ^ vswz(c);
+      __builtin_amdgcn_global_load_lds(vbase + (size_t)row * VGROUP + lc * 16,
+                                       (lds_void*)(sm.v[st] + blk * 1024), 16, 0, 0);
+    }
+  }
+  if (w == 0 && lane < BK / 4) {
+    const float* src = a.ds + (bh * a.nqb + qb) * (size_t)a.Npad + (size_t)kb * BK + lane * 4;
+    __builtin_amdgcn_global_load_lds(src, (lds_void*)sm.ds[st], 16, 0, 0);
+  }
+}
+
+__device__ inline void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// S^T tile t (32 keys) x the wave's 32 queries, exact int32
+template <int D>
+__device__ inline void qk_tiles(const Smem<D>& sm, int st, const v4i (&qreg)[D / 32], int col, int half,
+                                v16i (&sacc)[BK / 32]) {
+#pragma unroll
+  for (int t = 0; t < BK / 32; ++t) {
+    v16i acc = {};
+    const int row = 32 * t + col;
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) {
+      const int pc = (2 * s + half) ^ kswz<D>(row);
+      const v4i av = *reinterpret_cast<const v4i*>(sm.k[st] + row * D + pc * 16);
+      acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(av, qreg[s], acc, 0, 0, 0);
+    }
+    sacc[t] = acc;
+  }
+}
+
+__device__ inline int xcd_remap(int bid, int total) {
+  const int q = total / 8, r = total % 8;
+  const int x = bid % 8, k = bid / 8;
+  return x * q + min(x, r) + k;
+}
+
+template <int D, bool CAUSAL, bool DUMP>
+__global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
+  __shared__ Smem<D> sm;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, col = lane & 31, half = lane >> 5;
+
+  int b, h, qb;
+  if (DUMP) {
+    b = a.dbg_b; h = a.dbg_h; qb = a.dbg_qb;
+  } else {
+    const int total = a.B * a.H * a.nqb;
+    const int L = xcd_remap(blockIdx.x, total);
+    const int bhi = L / a.nqb, qi = L % a.nqb;
+    b = bhi / a.H; h = bhi % a.H;
+    qb = CAUSAL ? a.nqb - 1 - qi : qi;
+  }
+  const size_t bh = (size_t)b * a.H + h;
+  const size_t bkv = (size_t)b * a.Hkv + h / (a.H / a.Hkv);
+  const int il = w * QW + col;                  // query within the block
+  const int i = qb * BQ + il;
+
+  // the wave's 32 query rows as the B operand of S^T = K Q^T (16 bytes per k-step)
+  v4i qreg[D / 32];
+#pragma unroll
+  for (int s = 0; s < D / 32; ++s)
+    qreg[s] = *reinterpret_cast<const v4i*>(a.qcodes + (bh * a.Npad + i) * D + 32 * s + 16 * half);
+  const float qd = a.qscale[bh * a.Npad + i];
+
+  if (DUMP) {
+    issue_tile<D>(a, sm, 0, bkv, bh, qb, a.dbg_kb, w, lane);
+    wait_loads();
+    __syncthreads();
+    v16i sacc[BK / 32];
+    qk_tiles<D>(sm, 0, qreg, col, half, sacc);
+#pragma unroll
+    for (int t = 0; t < BK / 32; ++t)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int jl = 32 * t + 8 * (e >> 2) + 4 * half + (e & 3);
+        a.dbg_out[il * BK + jl] = sacc[t][e];
+      }
+    return;
+  }
+
+  const int nblk = CAUSAL ? qb + 1 : a.nkb;
+  float m_run = -INFINITY, l_part = 0.f;
+  v16f og[D / 32];
+#pragma unroll
+  for (int ct = 0; ct < D / 32; ++ct) og[ct] = (v16f){};
+
+  issue_tile<D>(a, sm, 0, bkv, bh, qb, 0, w, lane);
+  wait_loads();
+  __syncthreads();
+
+  for (int kb = 0; kb < nblk; ++kb) {
+    const int st = kb & 1;
+    if (kb + 1 < nblk) issue_tile<D>(a, sm, st ^ 1, bkv, bh, qb, kb + 1, w, lane);
+
+    v16i sacc[BK / 32];
+    qk_tiles<D>(sm, st, qreg, col, half, sacc);
+
+    // dequantize, add the Q-smoothing bias, mask; log2 domain
+    const float kd = a.kscale[(bkv * a.nkb + kb) * 2 + half];
+    const float cmul = qd * kd * a.k2;
+    float z[BK / 32][16];
+    float mloc = -INFINITY;
+    const bool diag = CAUSAL && kb == qb;
+    const bool tail = (kb + 1) * BK > a.N;
+#pragma unroll
+    for (int t = 0; t < BK / 32; ++t) {
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const int j0 = 32 * t + 8 * qq + 4 * half;
+        const float4 dsv = *reinterpret_cast<const float4*>(&sm.ds[st][j0]);
+        const float dsa[4] = {dsv.x, dsv.y, dsv.z, dsv.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float x = (float)sacc[t][4 * qq + r] * cmul + dsa[r];
+          if (diag && j0 + r > il) x = -INFINITY;
+          if (tail && kb * BK + j0 + r >= a.N) x = -INFINITY;
+          z[t][4 * qq + r] = x;
+          mloc = fmaxf(mloc, x);
+        }
+      }
+    }
+    // row max across the two lane halves holding the same query
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+    const float m_new = fmaxf(m_run, mloc);
+    // a row has a finite max from its first block on (key 0 is never masked); the guards only
+    // keep -inf - -inf out of the arithmetic
+    const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+    const float mo = (m_new == -INFINITY ? 0.f : m_new) - kLog2Pr;   // p * P_r = 2^(z - mo)
+    m_run = m_new;
+
+    // P~ = E4M3(p * P_r), packed straight into the FP8 MFMA B operand
+    v8i pb[BK / 64];
+    float lsum = 0.f;
+#pragma unroll
+    for (int t = 0; t < BK / 32; ++t) {
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        float p0 = __builtin_amdgcn_exp2f(z[t][4 * qq + 0] - mo);
+        float p1 = __builtin_amdgcn_exp2f(z[t][4 * qq + 1] - mo);
+        float p2 = __builtin_amdgcn_exp2f(z[t][4 * qq + 2] - mo);
+        float p3 = __builtin_amdgcn_exp2f(z[t][4 * qq + 3] - mo);
+        lsum += (p0 + p1) + (p2 + p3);
+        int word = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+        word = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, word, true);
+        pb[t >> 1][(t & 1) * 4 + qq] = word;
+      }
+    }
+    l_part = l_part * alpha + lsum;
+
+    // P~ V: block-local accumulation from zero, then the fp32 global accumulator
+#pragma unroll
+    for (int ct = 0; ct < D / 32; ++ct) {
+      v16f loc = {};
+      const int c = 32 * ct + col;
+#pragma unroll
+      for (int u = 0; u < BK / 64; ++u) {
+        const uint8_t* row = sm.v[st] + (u * D + c) * VGROUP;
+        const int sw = vswz(c);
+        const v4i lo = *reinterpret_cast<const v4i*>(row + ((2 * half) ^ sw) * 16);
+        const v4i hi = *reinterpret_cast<const v4i*>(row + ((2 * half + 1) ^ sw) * 16);
+        const v8i va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        loc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb[u], loc, 0, 0, 0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) og[ct][e] = fmaf(og[ct][e], alpha, loc[e]);
+    }
+
+    wait_loads();
+    __syncthreads();
+  }
+
+  // epilogue: O = acc * delta_V / l   (l counts p * P_r, so it carries the 1/P_r)
+  const float l = l_part + __shfl_xor(l_part, 32, 64);
+  const float inv_l = l > 0.f ? 1.f / l : 0.f;
+  if (i < a.N) {
+    __half* orow = a.o + (bh * a.N + i) * D;
+    const float* vs = a.vscale + bkv * D;
+#pragma unroll
+    for (int ct = 0; ct < D / 32; ++ct) {
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const int c0 = 32 * ct + 8 * qq + 4 * half;
+        const float4 sc = *reinterpret_cast<const float4*>(vs + c0);
+        union { __half hh[4]; uint2 u; } pk;
+        pk.hh[0] = __float2half_rn(og[ct][4 * qq + 0] * sc.x * inv_l);
+        pk.hh[1] = __float2half_rn(og[ct][4 * qq + 1] * sc.y * inv_l);
+        pk.hh[2] = __float2half_rn(og[ct][4 * qq + 2] * sc.z * inv_l);
+        pk.hh[3] = __float2half_rn(og[ct][4 * qq + 3] * sc.w * inv_l);
+        *reinterpret_cast<uint2*>(orow + c0) = pk.u;
+      }
+    }
+  }
+}
+
+AttnArgs make_args(const Dims& D, const Ptrs& P) {
+  AttnArgs a{};
+  a.qcodes = P.qcodes;
+  a.kcodes = P.kcodes;
+  a.vcodes = P.vcodes;
+  a.qscale = P.qscale;
+  a.kscale = P.kscale;
+  a.vscale = P.vscale;
+  a.ds = P.ds;
+  a.o = P.o;
+  a.B = D.B; a.H = D.H; a.Hkv = D.Hkv; a.N = D.N; a.Npad = D.Npad; a.nqb = D.nqb; a.nkb = D.nkb;
+  a.k2 = (float)(1.4426950408889634 / sqrt((double)D.d));
+  return a;
+}
+
+template <int DD>
+hipError_t launch_d(const Dims& D, const AttnArgs& a, hipStream_t s) {
+  const int grid = D.B * D.H * D.nqb;
+  if (D.causal)
+    attn_fwd<DD, true, false><<<grid, 256, 0, s>>>(a);
+  else
+    attn_fwd<DD, false, false><<<grid, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attention(const Dims& D, const Ptrs& P, hipStream_t s) {
+  const AttnArgs a = make_args(D, P);
+  return D.d == 128 ? launch_d<128>(D, a, s) : launch_d<64>(D, a, s);
+}
+
+hipError_t launch_qk_tile(const Dims& D, const Ptrs& P, int b, int h, int qb, int kb, int32_t* out, hipStream_t s) {
+  AttnArgs a = make_args(D, P);
+  a.dbg_b = b; a.dbg_h = h; a.dbg_qb = qb; a.dbg_kb = kb; a.dbg_out = out;
+  if (D.d == 128)
+    attn_fwd<128, false, true><<<1, 256, 0, s>>>(a);
+  else
+    attn_fwd<64, false, true><<<1, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace sage

@@ -1,0 +1,431 @@
+// Quantize/smooth prologue for the SageAttention2 forward on gfx950.
+//
+// Page "SageAttention2: Efficient Attention with Thorough Outlier Smoothing and Per-thread
+// INT4 Quantization" (mlsanity.com, arXiv 2411.10958), section "Abstract (arXiv)": K and Q are
+// smoothed and quantized to 4-bit (here also 8-bit) integers at thread granularity, V to FP8.
+// pith.science verdict on arXiv 2505.21136, key "key_machinery": per-channel V scale
+// max|V| / V_r.
+//
+// All kernels are HBM-streaming codec work: each reads its fp16 input once (K and V twice:
+// statistics, then quantization) and writes 1-byte codes plus a few scales.
+//
+// Bit-exactness: the channel means are exact fixed-point sums (every fp16 value is an integer
+// multiple of 2^-24, |x * 2^24| < 2^40), reduced with 64-bit integer adds in any order, then
+// one fp64 division and one rounding to fp32.  Smoothing is one fp32 subtraction; codes are
+// round-half-even of one fp32 product with the correctly rounded fp32 reciprocal R / amax;
+// scales are the correctly rounded fp32 quotient amax / R.  None of these depend on the
+// order of the parallel reduction, so codes and scales are reproducible bit for bit.
+#include "sage_internal.h"
+
+namespace sage {
+
+namespace {
+
+constexpr float kFix = 16777216.0f;   // 2^24
+
+struct Half8 {
+  __half h[8];
+};
+
+__device__ inline Half8 load8(const __half* p) {
+  Half8 r;
+  *reinterpret_cast<uint4*>(&r) = *reinterpret_cast<const uint4*>(p);
+  return r;
+}
+
+__device__ inline float wave_max(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m, 64));
+  return x;
+}
+
+// ---------------------------------------------------------------------------------------
+// zero the atomically reduced statistics
+// ---------------------------------------------------------------------------------------
+__global__ void init_stats(unsigned long long* ksum, unsigned int* vamax, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) {
+    ksum[i] = 0ull;
+    vamax[i] = 0u;
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// K channel sums (exact, int64 fixed point) and V channel abs-max, per (b, kv head).
+// grid (ceil(N / 256), B*Hkv), 256 threads; thread = (row slot, 8-channel chunk).
+// ---------------------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void kv_stats(const __half* __restrict__ k, const __half* __restrict__ v,
+                                                unsigned long long* __restrict__ ksum,
+                                                unsigned int* __restrict__ vamax, int N) {
+  constexpr int TPR = D / 8;      // threads per row
+  constexpr int RPP = 256 / TPR;  // rows per pass
+  constexpr int TOK = 256;        // tokens per workgroup
+  __shared__ long long ls[RPP][D];
+  __shared__ float lm[RPP][D];
+  const int tid = threadIdx.x, cq = tid % TPR, r0 = tid / TPR;
+  const size_t bh = blockIdx.y;
+  const __half* kb = k + bh * (size_t)N * D;
+  const __half* vb = v + bh * (size_t)N * D;
+  long long s[8];
+  float mx[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) { s[e] = 0; mx[e] = 0.f; }
+  const int tok0 = blockIdx.x * TOK;
+  for (int p = 0; p < TOK / RPP; ++p) {
+    const int row = tok0 + p * RPP + r0;
+    if (row < N) {
+      const Half8 kk = load8(kb + (size_t)row * D + cq * 8);
+      const Half8 vv = load8(vb + (size_t)row * D + cq * 8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        s[e] += (long long)(__half2float(kk.h[e]) * kFix);   // exact: 11 significant bits
+        mx[e] = fmaxf(mx[e], fabsf(__half2float(vv.h[e])));
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) { ls[r0][cq * 8 + e] = s[e]; lm[r0][cq * 8 + e] = mx[e]; }
+  __syncthreads();
+  for (int c = tid; c < D; c += 256) {
+    long long t = 0;
+    float m = 0.f;
+    for (int r = 0; r < RPP; ++r) { t += ls[r][c]; m = fmaxf(m, lm[r][c]); }
+    atomicAdd(&ksum[bh * D + c], (unsigned long long)t);          // two's complement: exact
+    atomicMax(&vamax[bh * D + c], __float_as_uint(m));            // order of non-negative floats
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// K smoothing + quantization and V FP8 quantization for one KV block of 128 keys.
+// grid (nkb, B*Hkv), 256 threads.
+// K group: keys 8a + 4h + r of the block share the scale of lane half h (one scale per
+// lane of the 32x32 integer MFMA accumulator that holds those keys).
+// V codes are written transposed per 64-key group in the FP8 MFMA k-slot order.
+// ---------------------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void kv_quant(const __half* __restrict__ k, const __half* __restrict__ v,
+                                                const unsigned long long* __restrict__ ksum,
+                                                const unsigned int* __restrict__ vamax,
+                                                int8_t* __restrict__ kcodes, uint8_t* __restrict__ vcodes,
+                                                float* __restrict__ kscale, float* __restrict__ muk_out,
+                                                float* __restrict__ vscale, int N, int Npad, int nkb, float R) {
+  constexpr int TPR = D / 8, RPP = 256 / TPR, PASSES = BK / RPP;
+  static_assert(RPP % 8 == 0, "a thread's rows must share (row % 8)");
+  __shared__ float red[WAVES][2];
+  __shared__ __attribute__((aligned(16))) uint8_t vt[2 * D * VGROUP];
+  const int tid = threadIdx.x, cq = tid % TPR, r0 = tid / TPR, lane = tid % 64, w = tid / 64;
+  const int kb = blockIdx.x;
+  const size_t bh = blockIdx.y;
+  const __half* kbase = k + bh * (size_t)N * D;
+  const __half* vbase = v + bh * (size_t)N * D;
+
+  float mu[8], vinv[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int c = cq * 8 + e;
+    const long long S = (long long)ksum[bh * D + c];
+    mu[e] = (float)((double)S / ((double)N * 16777216.0));
+    const float va = __uint_as_float(vamax[bh * D + c]);
+    vinv[e] = va > 0.f ? V_RANGE / va : 0.f;
+    if (kb == 0 && r0 == 0) {
+      muk_out[bh * D + c] = mu[e];
+      vscale[bh * D + c] = va / V_RANGE;
+    }
+  }
+
+  // gamma_K = RN32(K - mu_K); every row of this thread has the same (row % 8)
+  float g[PASSES][8];
+  float am = 0.f;
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int row = kb * BK + p * RPP + r0;
+    if (row < N) {
+      const Half8 kk = load8(kbase + (size_t)row * D + cq * 8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        g[p][e] = __half2float(kk.h[e]) - mu[e];
+        am = fmaxf(am, fabsf(g[p][e]));
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) g[p][e] = 0.f;
+    }
+  }
+  const int hgrp = (r0 & 7) >> 2;
+  float a0 = wave_max(hgrp == 0 ? am : 0.f);
+  float a1 = wave_max(hgrp == 1 ? am : 0.f);
+  if (lane == 0) { red[w][0] = a0; red[w][1] = a1; }
+  __syncthreads();
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < WAVES; ++i) amax = fmaxf(amax, red[i][hgrp]);
+  const float inv = amax > 0.f ? R / amax : 0.f;
+  if (tid < 2) {
+    float a = 0.f;
+    for (int i = 0; i < WAVES; ++i) a = fmaxf(a, red[i][tid]);
+    kscale[(bh * nkb + kb) * 2 + tid] = a / R;
+  }
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int row = kb * BK + p * RPP + r0;   // < Npad: rows past N get zero codes
+    union { int8_t c[8]; uint2 u; } out;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float x = rintf(g[p][e] * inv);
+      x = fminf(fmaxf(x, -R), R);
+      out.c[e] = (int8_t)(int)x;
+    }
+    *reinterpret_cast<uint2*>(kcodes + (bh * Npad + row) * D + cq * 8) = out.u;
+  }
+
+  // V: per-channel FP8, transposed into [group u][channel][slot] in LDS, then streamed out
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int jl = p * RPP + r0;               // key within the block
+    const int row = kb * BK + jl;
+    const int u = jl >> 6, jj = jl & 63;
+    const int pos = 32 * ((jj >> 2) & 1) + 16 * (jj >> 5) + 4 * ((jj >> 3) & 3) + (jj & 3);
+    if (row < N) {
+      const Half8 vv = load8(vbase + (size_t)row * D + cq * 8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float x = __half2float(vv.h[e]) * vinv[e];
+        x = fminf(fmaxf(x, -V_RANGE), V_RANGE);
+        vt[(u * D + cq * 8 + e) * VGROUP + pos] = (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(x, 0.f, 0, false) & 0xff);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) vt[(u * D + cq * 8 + e) * VGROUP + pos] = 0;
+    }
+  }
+  __syncthreads();
+  uint8_t* dst = vcodes + (bh * (size_t)(Npad / VGROUP) + (size_t)kb * 2) * D * VGROUP;
+  for (int ch = tid; ch < 2 * D * VGROUP / 16; ch += 256)
+    *reinterpret_cast<uint4*>(dst + ch * 16) = *reinterpret_cast<const uint4*>(vt + ch * 16);
+}
+
+// ---------------------------------------------------------------------------------------
+// Q smoothing (per 128-row block mean) + per-row quantization.
+// grid (nqb, B*H), 256 threads.
+// ---------------------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void q_quant(const __half* __restrict__ q, int8_t* __restrict__ qcodes,
+                                               float* __restrict__ qscale, float* __restrict__ muq,
+                                               int N, int Npad, int nqb, float R) {
+  constexpr int TPR = D / 8, RPP = 256 / TPR, PASSES = BQ / RPP;
+  __shared__ long long ls[RPP][D];
+  __shared__ float lmu[D];
+  const int tid = threadIdx.x, cq = tid % TPR, r0 = tid / TPR;
+  const int qb = blockIdx.x;
+  const size_t bh = blockIdx.y;
+  const __half* qbase = q + bh * (size_t)N * D;
+  const int nvalid = min(BQ, N - qb * BQ);
+
+  float x[PASSES][8];
+  long long s[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s[e] = 0;
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int row = qb * BQ + p * RPP + r0;
+    if (row < N) {
+      const Half8 qq = load8(qbase + (size_t)row * D + cq * 8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        x[p][e] = __half2float(qq.h[e]);
+        s[e] += (long long)(x[p][e] * kFix);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[p][e] = 0.f;
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ls[r0][cq * 8 + e] = s[e];
+  __syncthreads();
+  for (int c = tid; c < D; c += 256) {
+    long long t = 0;
+    for (int r = 0; r < RPP; ++r) t += ls[r][c];
+    const float m = (float)((double)t / ((double)nvalid * 16777216.0));
+    lmu[c] = m;
+    muq[(bh * nqb + qb) * D + c] = m;
+  }
+  __syncthreads();
+  float mu[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) mu[e] = lmu[cq * 8 + e];
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int row = qb * BQ + p * RPP + r0;
+    const bool valid = row < N;
+    float am = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      x[p][e] = valid ? x[p][e] - mu[e] : 0.f;   // gamma_Q = RN32(Q - mu_Q)
+      am = fmaxf(am, fabsf(x[p][e]));
+    }
+#pragma unroll
+    for (int m = TPR / 2; m >= 1; m >>= 1) am = fmaxf(am, __shfl_xor(am, m, 64));
+    const float inv = am > 0.f ? R / am : 0.f;
+    union { int8_t c[8]; uint2 u; } out;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float y = rintf(x[p][e] * inv);
+      y = fminf(fmaxf(y, -R), R);
+      out.c[e] = (int8_t)(int)y;
+    }
+    *reinterpret_cast<uint2*>(qcodes + (bh * Npad + row) * D + cq * 8) = out.u;
+    if (cq == 0) qscale[bh * Npad + row] = am / R;
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Delta_S[qb, j] = sum_c mu_Q[qb, c] * gamma_K[j, c], stored times log2(e)/sqrt(d).
+// Tiled fp32 GEMM: workgroup = 64 query blocks x 128 keys, channels in chunks of 32.
+// grid (Npad/128, ceil(nqb/64), B*H), 256 threads; thread = 4 query blocks x 8 keys.
+// ---------------------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void delta_s(const __half* __restrict__ k, const float* __restrict__ muk,
+                                               const float* __restrict__ muq, float* __restrict__ ds,
+                                               int H, int Hkv, int N, int Npad, int nqb, float k2) {
+  constexpr int QT = 64, KT = 128, CC = 32;
+  __shared__ float sq[QT][CC + 1];
+  __shared__ float sk[KT][CC + 1];
+  const int tid = threadIdx.x;
+  const int kt = blockIdx.x, qt = blockIdx.y;
+  const int bh = blockIdx.z, b = bh / H, h = bh % H, hk = h / (H / Hkv);
+  const size_t bkv = (size_t)b * Hkv + hk;
+  const __half* kbase = k + bkv * (size_t)N * D;
+  const int tq = tid / 16, tk = tid % 16;
+  float acc[4][8];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[a][e] = 0.f;
+  for (int c0 = 0; c0 < D; c0 += CC) {
+    for (int i = tid; i < QT * CC; i += 256) {
+      const int r = i / CC, c = i % CC, qb = qt * QT + r;
+      sq[r][c] = qb < nqb ? muq[((size_t)bh * nqb + qb) * D + c0 + c] : 0.f;
+    }
+    for (int i = tid; i < KT * CC; i += 256) {
+      const int r = i / CC, c = i % CC, j = kt * KT + r;
+      sk[r][c] = j < N ? __half2float(kbase[(size_t)j * D + c0 + c]) - muk[bkv * D + c0 + c] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int c = 0; c < CC; ++c) {
+      float qv[4], kv[8];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) qv[a] = sq[4 * tq + a][c];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) kv[e] = sk[tk + 16 * e][c];
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[a][e] = fmaf(qv[a], kv[e], acc[a][e]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    const int qb = qt * QT + 4 * tq + a;
+    if (qb >= nqb) continue;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int j = kt * KT + tk + 16 * e;
+      ds[((size_t)bh * nqb + qb) * Npad + j] = acc[a][e] * k2;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// debug: internal layouts -> plain layouts
+// ---------------------------------------------------------------------------------------
+__global__ void copy_rows_i8(const int8_t* __restrict__ src, int8_t* __restrict__ dst, int heads, int N,
+                             int Npad, int d) {
+  const size_t total = (size_t)heads * N * d;
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
+    const size_t hd = i / ((size_t)N * d), rem = i % ((size_t)N * d);
+    dst[i] = src[hd * Npad * d + rem];
+  }
+}
+__global__ void copy_rows_f32(const float* __restrict__ src, float* __restrict__ dst, size_t rows, int n,
+                              int npad, float mul) {
+  const size_t total = rows * n;
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
+    const size_t r = i / n, c = i % n;
+    dst[i] = src[r * npad + c] * mul;
+  }
+}
+__global__ void expand_kscale(const float* __restrict__ kscale, float* __restrict__ dst, int heads, int N, int nkb) {
+  const size_t total = (size_t)heads * N;
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
+    const size_t hd = i / N;
+    const int j = (int)(i % N);
+    dst[i] = kscale[(hd * nkb + j / BK) * 2 + ((j & 7) >> 2)];
+  }
+}
+__global__ void unpermute_v(const uint8_t* __restrict__ vc, uint8_t* __restrict__ dst, int heads, int N, int Npad,
+                            int d) {
+  const size_t total = (size_t)heads * N * d;
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
+    const size_t hd = i / ((size_t)N * d);
+    const int j = (int)((i / d) % N), c = (int)(i % d);
+    const int g = j / VGROUP, jj = j % VGROUP;
+    const int pos = 32 * ((jj >> 2) & 1) + 16 * (jj >> 5) + 4 * ((jj >> 3) & 3) + (jj & 3);
+    dst[i] = vc[((hd * (Npad / VGROUP) + g) * d + c) * VGROUP + pos];
+  }
+}
+
+template <int D>
+hipError_t launch_prologue_d(const Dims& Dm, const Ptrs& P, hipStream_t s) {
+  const float R = Dm.qk_bits == 4 ? 7.f : 127.f;
+  const int nkv = Dm.B * Dm.Hkv * D;
+  init_stats<<<(nkv + 255) / 256, 256, 0, s>>>(P.ksum, P.vamax, nkv);
+  kv_stats<D><<<dim3((Dm.N + 255) / 256, Dm.B * Dm.Hkv), 256, 0, s>>>(P.k, P.v, P.ksum, P.vamax, Dm.N);
+  kv_quant<D><<<dim3(Dm.nkb, Dm.B * Dm.Hkv), 256, 0, s>>>(P.k, P.v, P.ksum, P.vamax, P.kcodes, P.vcodes,
+                                                          P.kscale, P.muk, P.vscale, Dm.N, Dm.Npad, Dm.nkb, R);
+  q_quant<D><<<dim3(Dm.nqb, Dm.B * Dm.H), 256, 0, s>>>(P.q, P.qcodes, P.qscale, P.muq, Dm.N, Dm.Npad, Dm.nqb, R);
+  const float k2 = (float)(1.4426950408889634 / sqrt((double)D));
+  delta_s<D><<<dim3(Dm.Npad / 128, (Dm.nqb + 63) / 64, Dm.B * Dm.H), 256, 0, s>>>(
+      P.k, P.muk, P.muq, P.ds, Dm.H, Dm.Hkv, Dm.N, Dm.Npad, Dm.nqb, k2);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prologue(const Dims& D, const Ptrs& P, hipStream_t s) {
+  return D.d == 128 ? launch_prologue_d<128>(D, P, s) : launch_prologue_d<64>(D, P, s);
+}
+
+hipError_t launch_debug_copy(const Dims& D, const Ptrs& P, hipStream_t s, float* mu_k, int8_t* k_codes,
+                             float* k_scales, uint8_t* v_codes, float* v_scales, float* mu_q, int8_t* q_codes,
+                             float* q_scales, float* delta_s_out) {
+  const int hkv = D.B * D.Hkv, hq = D.B * D.H;
+  const int grid = 1024, blk = 256;
+  if (mu_k) {
+    hipError_t e = hipMemcpyAsync(mu_k, P.muk, (size_t)hkv * D.d * 4, hipMemcpyDeviceToDevice, s);
+    if (e != hipSuccess) return e;
+  }
+  if (v_scales) {
+    hipError_t e = hipMemcpyAsync(v_scales, P.vscale, (size_t)hkv * D.d * 4, hipMemcpyDeviceToDevice, s);
+    if (e != hipSuccess) return e;
+  }
+  if (mu_q) {
+    hipError_t e = hipMemcpyAsync(mu_q, P.muq, (size_t)hq * D.nqb * D.d * 4, hipMemcpyDeviceToDevice, s);
+    if (e != hipSuccess) return e;
+  }
+  if (k_codes) copy_rows_i8<<<grid, blk, 0, s>>>(P.kcodes, k_codes, hkv, D.N, D.Npad, D.d);
+  if (q_codes) copy_rows_i8<<<grid, blk, 0, s>>>(P.qcodes, q_codes, hq, D.N, D.Npad, D.d);
+  if (k_scales) expand_kscale<<<grid, blk, 0, s>>>(P.kscale, k_scales, hkv, D.N, D.nkb);
+  if (q_scales) copy_rows_f32<<<grid, blk, 0, s>>>(P.qscale, q_scales, (size_t)hq, D.N, D.Npad, 1.f);
+  if (v_codes) unpermute_v<<<grid, blk, 0, s>>>(P.vcodes, v_codes, hkv, D.N, D.Npad, D.d);
+  if (delta_s_out) {
+    const float inv_k2 = (float)(sqrt((double)D.d) / 1.4426950408889634);
+    copy_rows_f32<<<grid, blk, 0, s>>>(P.ds, delta_s_out, (size_t)hq * D.nqb, D.N, D.Npad, inv_k2);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace sage

@@ -1,0 +1,118 @@
+// Internal definitions shared by the gfx950 kernels and the C ABI host code.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sage {
+
+// ---- compile-time geometry (exported by sage_get_config) ----
+constexpr int BQ = 128;          // queries per workgroup (4 waves x 32) and per Q-mean block
+constexpr int BK = 128;          // keys per KV block
+constexpr int WAVES = 4;
+constexpr int QW = 32;           // queries per wave: one 32-wide MFMA column tile
+constexpr float P_RANGE = 448.0f;
+constexpr float V_RANGE = 448.0f;
+constexpr int VGROUP = 64;       // keys per FP8 MFMA k-step (32x32x64): V^T is stored per 64 keys
+constexpr size_t WS_ALIGN = 256;
+
+// ---- problem description ----
+struct Dims {
+  int B, H, Hkv, N, d, causal, qk_bits;
+  int Npad;   // N rounded up to a multiple of 128 (= BQ = BK)
+  int nqb;    // query blocks
+  int nkb;    // KV blocks
+};
+
+// ---- workspace carve-up (byte offsets, all WS_ALIGN aligned) ----
+//  kcodes : int8  [B][Hkv][Npad][d]           smoothed+quantized K, zero past N
+//  vcodes : uint8 [B][Hkv][Npad/64][d][64]    FP8 V, transposed per 64-key group; inside a
+//           group the byte at position 32*h + b of channel row c holds key
+//           32*(b/16) + 8*((b%16)/4) + 4*h + (b%4): the k-slot order of the FP8 MFMA
+//           B operand built from the S^T accumulators (see attention kernel)
+//  qcodes : int8  [B][H][Npad][d]
+//  kscale : fp32  [B][Hkv][nkb][2]            delta_K per (KV block, lane half)
+//  qscale : fp32  [B][H][Npad]                delta_Q per query row
+//  muk    : fp32  [B][Hkv][d]
+//  ksum   : int64 [B][Hkv][d]                 exact fixed-point K column sums (2^-24 units)
+//  vamax  : u32   [B][Hkv][d]                 bits of max|V| per channel (non-negative floats)
+//  vscale : fp32  [B][Hkv][d]                 delta_V
+//  muq    : fp32  [B][H][nqb][d]
+//  ds     : fp32  [B][H][nqb][Npad]           Delta_S * log2(e) / sqrt(d)
+struct Layout {
+  size_t kcodes, vcodes, qcodes, kscale, qscale, muk, ksum, vamax, vscale, muq, ds, total;
+};
+
+inline size_t align_up(size_t x) { return (x + WS_ALIGN - 1) / WS_ALIGN * WS_ALIGN; }
+
+inline Layout make_layout(const Dims& D) {
+  Layout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
+  const size_t B = D.B, H = D.H, Hkv = D.Hkv, Np = D.Npad, d = D.d;
+  L.kcodes = take(B * Hkv * Np * d);
+  L.vcodes = take(B * Hkv * Np * d);
+  L.qcodes = take(B * H * Np * d);
+  L.kscale = take(B * Hkv * (size_t)D.nkb * 2 * 4);
+  L.qscale = take(B * H * Np * 4);
+  L.muk = take(B * Hkv * d * 4);
+  L.ksum = take(B * Hkv * d * 8);
+  L.vamax = take(B * Hkv * d * 4);
+  L.vscale = take(B * Hkv * d * 4);
+  L.muq = take(B * H * (size_t)D.nqb * d * 4);
+  L.ds = take(B * H * (size_t)D.nqb * Np * 4);
+  L.total = off;
+  return L;
+}
+
+struct Ptrs {
+  const __half* q;
+  const __half* k;
+  const __half* v;
+  __half* o;
+  int8_t* kcodes;
+  uint8_t* vcodes;
+  int8_t* qcodes;
+  float* kscale;
+  float* qscale;
+  float* muk;
+  unsigned long long* ksum;
+  unsigned int* vamax;
+  float* vscale;
+  float* muq;
+  float* ds;
+};
+
+inline Ptrs carve(void* ws, const Layout& L, const void* q, const void* k, const void* v, void* o) {
+  char* w = static_cast<char*>(ws);
+  Ptrs p;
+  p.q = static_cast<const __half*>(q);
+  p.k = static_cast<const __half*>(k);
+  p.v = static_cast<const __half*>(v);
+  p.o = static_cast<__half*>(o);
+  p.kcodes = reinterpret_cast<int8_t*>(w + L.kcodes);
+  p.vcodes = reinterpret_cast<uint8_t*>(w + L.vcodes);
+  p.qcodes = reinterpret_cast<int8_t*>(w + L.qcodes);
+  p.kscale = reinterpret_cast<float*>(w + L.kscale);
+  p.qscale = reinterpret_cast<float*>(w + L.qscale);
+  p.muk = reinterpret_cast<float*>(w + L.muk);
+  p.ksum = reinterpret_cast<unsigned long long*>(w + L.ksum);
+  p.vamax = reinterpret_cast<unsigned int*>(w + L.vamax);
+  p.vscale = reinterpret_cast<float*>(w + L.vscale);
+  p.muq = reinterpret_cast<float*>(w + L.muq);
+  p.ds = reinterpret_cast<float*>(w + L.ds);
+  return p;
+}
+
+// ---- launchers (return the hipError_t of the launch) ----
+hipError_t launch_prologue(const Dims& D, const Ptrs& P, hipStream_t s);
+hipError_t launch_attention(const Dims& D, const Ptrs& P, hipStream_t s);
+hipError_t launch_qk_tile(const Dims& D, const Ptrs& P, int b, int h, int qb, int kb, int32_t* out,
+                          hipStream_t s);
+hipError_t launch_debug_copy(const Dims& D, const Ptrs& P, hipStream_t s, float* mu_k, int8_t* k_codes,
+                             float* k_scales, uint8_t* v_codes, float* v_scales, float* mu_q,
+                             int8_t* q_codes, float* q_scales, float* delta_s);
+
+}  // namespace sage

@@ -1,0 +1,106 @@
+"""C ABI checks that need no GPU: the library loads, exports every symbol the header
+declares, reports its configuration, sizes workspaces, and rejects bad arguments before
+making any HIP call (the host has no GPU, so only calls that fail validation are made)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from oracle import sage as oracle_sage
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sage_attn.h")
+
+
+@pytest.fixture(scope="module")
+def pkg():
+    from quantized_attention_smooth_amd import build as b
+    if not os.path.exists(b.LIB):
+        b.build()
+    import quantized_attention_smooth_amd as p
+    return p
+
+
+def _declared():
+    text = open(HEADER).read()
+    return set(re.findall(r"^(?:int|const char\*)\s+(sage_\w+)\s*\(", text, flags=re.M))
+
+
+def test_exports_every_declared_symbol(pkg):
+    declared = _declared()
+    assert declared == set(pkg.EXPORTS)
+    lib = ctypes.CDLL(pkg.LIB_PATH)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_config_matches_oracle_geometry(pkg):
+    cfg = pkg.get_config()
+    g = oracle_sage.DEFAULT
+    assert cfg["version"] == 1 and cfg["fp8_format"] == 1
+    for f in ("bq", "bk", "q_slice", "q_period", "q_run", "k_slice", "k_period", "k_run"):
+        assert cfg[f] == getattr(g, f), f
+    assert cfg["p_range"] == g.p_range and cfg["v_range"] == g.v_range
+
+
+def test_workspace_bytes(pkg):
+    n1 = pkg.workspace_bytes(1, 2, 2, 256, 64, False, 8)
+    assert n1 > 0 and n1 % 256 == 0
+    # codes (K, V, Q) + Delta_S dominate: 3 * 256*64*2 + 2*2*256*4 bytes at least
+    assert n1 >= 3 * 256 * 64 * 2 + 2 * 2 * 256 * 4
+    assert pkg.workspace_bytes(1, 2, 2, 257, 64, False, 8) > n1           # one more 128-row block
+    assert pkg.workspace_bytes(1, 32, 8, 98304, 128, True, 8) > 9 * 2 ** 30
+
+
+@pytest.mark.parametrize("args,status", [
+    ((0, 2, 2, 256, 64, 0, 8), -1),       # B < 1
+    ((1, 3, 2, 256, 64, 0, 8), -1),       # H % Hkv
+    ((1, 2, 2, 0, 64, 0, 8), -1),         # N < 1
+    ((1, 2, 2, 256, 64, 2, 8), -1),       # causal not 0/1
+    ((1, 2, 2, 256, 96, 0, 8), -2),       # d
+    ((1, 2, 2, 256, 64, 0, 6), -2),       # qk_bits
+    ((1, 2, 2, (1 << 23) + 1, 64, 0, 8), -2),   # N beyond the exact-sum bound
+])
+def test_validation_errors(pkg, args, status):
+    lib = pkg._lib
+    n = ctypes.c_size_t(0)
+    assert lib.sage_attn_workspace_bytes(*args, ctypes.byref(n)) == status
+    fake = ctypes.c_void_p(0x1000)          # never dereferenced: validation fails first
+    assert lib.sage_attn_fwd(fake, fake, fake, fake, *args, ctypes.c_void_p(0x10000), 1 << 40, None) == status
+
+
+def test_null_and_workspace_errors(pkg):
+    lib = pkg._lib
+    fake = ctypes.c_void_p(0x1000)
+    dims = (1, 2, 2, 256, 64, 0, 8)
+    need = pkg.workspace_bytes(*dims)
+    ws = ctypes.c_void_p(0x100000)
+    assert lib.sage_attn_fwd(None, fake, fake, fake, *dims, ws, need, None) == -1
+    assert lib.sage_attn_fwd(fake, fake, fake, None, *dims, ws, need, None) == -1
+    assert lib.sage_attn_fwd(fake, fake, fake, fake, *dims, None, need, None) == -3
+    assert lib.sage_attn_fwd(fake, fake, fake, fake, *dims, ws, need - 1, None) == -3
+    assert lib.sage_attn_fwd(fake, fake, fake, fake, *dims, ctypes.c_void_p(0x100010), need, None) == -3
+    assert lib.sage_qk_tile_debug(fake, fake, fake, *dims, ws, need, None, 0, 0, 2, 0, fake) == -1   # qb
+    assert lib.sage_qk_tile_debug(fake, fake, fake, *dims, ws, need, None, 1, 0, 0, 0, fake) == -1   # b
+    assert lib.sage_qk_tile_debug(fake, fake, fake, *dims, ws, need, None, 0, 0, 0, 0, None) == -1
+    assert lib.sage_quant_debug(fake, None, fake, *dims, ws, need, None, *([None] * 9)) == -1
+    assert lib.sage_get_config(None) == -1
+
+
+def test_status_strings(pkg):
+    lib = pkg._lib
+    for s in (0, -1, -2, -3, -4, 7):
+        assert len(lib.sage_status_string(s)) > 0
+    assert lib.sage_last_error() == b""
+
+
+def test_python_wrapper_rejects_unsupported(pkg):
+    import torch
+    q = torch.zeros(1, 2, 16, 64, dtype=torch.float16)
+    with pytest.raises(NotImplementedError):
+        pkg.sageattn(q, q, q, attn_mask=torch.zeros(16, 16))
+    with pytest.raises(ValueError):
+        pkg.sageattn(q, q, q)                     # CPU tensors
+    with pytest.raises(ValueError):
+        pkg.sageattn(q.float(), q, q)

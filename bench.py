@@ -1,0 +1,226 @@
+#!/usr/bin/env python3
+"""Benchmark of the SageAttention2 quantized attention forward on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload bench|llm|dit|gqa|tiny]
+
+A step is one whole forward pass (quantize/smooth prologue + fused attention kernel) over the
+workload's seeded synthetic inputs, which are resident in HBM before the timed region.  The
+K timed steps are bracketed by torch.cuda.synchronize(); per-kernel times come from HIP
+events recorded on the stream the kernels are launched on (torch's current stream, which the
+binding passes to the library).
+
+Prints one JSON line: effective attention TOPS = 4*B*H*N^2*d / t (halved when causal), the
+roofline of the dominant kernel (the fused attention kernel, MFMA bound) and the CPU oracle's
+rate on a bounded sample of the same workload.
+
+Other modes:
+  --calibrate-copy   run a plain device copy of known size (for scaling rocprofv3's
+                     FETCH_SIZE / WRITE_SIZE counters to bytes)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "effective attention TOPS (4·B·H·N²·d/t, ½ if causal) at N=8K–32K, d=64/128"
+PEAK_TOPS = 5000.0          # MI355X dense INT8 (POP/s) and FP8 (PFLOP/s): 5.0 P each
+PEAK_HBM_GBPS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+ATTN_SRC = os.path.join(ROOT, "quantized_attention_smooth_amd", "csrc", "attention.hip")
+
+
+def _describe(w) -> str:
+    kind = "causal" if w.causal else "non-causal"
+    heads = f"H{w.H}" if w.H == w.Hkv else f"H{w.H}/Hkv{w.Hkv}"
+    return (f"{w.name}: B{w.B} {heads} N{w.N} d{w.d} {kind}, "
+            f"{'INT8' if w.qk_bits == 8 else 'INT4-range'} QK + FP8 PV")
+
+
+def _src_hash() -> str:
+    return hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
+
+
+def _traffic(workload: str):
+    """HBM bytes per attention-kernel launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source; else None."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    e = t.get("workloads", {}).get(workload)
+    if not e or t.get("attention_src_sha256") != _src_hash():
+        return None
+    return (e["fetch_kib"] * t["fetch_factor"] + e["write_kib"] * t["write_factor"]) * 1024.0
+
+
+def cpu_baseline(w, q, k, v, budget_s: float) -> dict:
+    """The oracle as it stands, on one (b, h) head: its full prologue plus as many query blocks
+    as fit the budget (spread over the sequence), extrapolated to the workload by block cost
+    (causal block qb costs qb + 1 key blocks)."""
+    import numpy as np
+    from oracle import sage as osage
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - reporting only
+        blas = 1
+    hk = 0
+    q1 = np.ascontiguousarray(q[:1, :1])
+    k1 = np.ascontiguousarray(k[:1, hk:hk + 1])
+    v1 = np.ascontiguousarray(v[:1, hk:hk + 1])
+    t0 = time.perf_counter()
+    pro = osage.prologue(q1, k1, v1, w.causal, w.qk_bits)
+    t_pro = time.perf_counter() - t0
+    nqb = pro.nqb
+    cost = [(qb + 1) if w.causal else pro.nkb for qb in range(nqb)]
+    order = []
+    step = max(1, nqb // 16)
+    for s in range(step):
+        order += list(range(nqb - 1 - s, -1, -step))
+    done_cost, t_att = 0, 0.0
+    nblk = 0
+    for qb in order:
+        t1 = time.perf_counter()
+        osage.attend_block(pro, 0, 0, qb)
+        t_att += time.perf_counter() - t1
+        done_cost += cost[qb]
+        nblk += 1
+        if t_pro + t_att >= budget_s:
+            break
+    per_unit = t_att / done_cost
+    t_head = t_pro + per_unit * sum(cost)
+    t_total = t_head * w.B * w.H
+    value = w.ops / t_total / 1e12
+    return {
+        "value": value, "unit": "TOPS", "cores": int(blas), "kind": "oracle",
+        "sample": (f"numpy oracle on head (b0,h0): full prologue ({t_pro:.1f} s) + {nblk} of {nqb} query "
+                   f"blocks ({t_att:.1f} s), extrapolated by block cost to {w.B * w.H} heads "
+                   f"(est. {t_total:.0f} s for the workload); BLAS threads {blas}, elementwise 1 thread"),
+    }
+
+
+def calibrate_copy(nbytes: int = 1 << 30, reps: int = 3) -> None:
+    import torch
+    x = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": nbytes, "reps": reps}), flush=True)
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="bench")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: the quantized attention forward is a single-GPU kernel "
+              f"here (heads shard across GPUs with no communication); --gpus {args.gpus} is not supported.",
+              file=sys.stderr)
+        return 2
+    if int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on one GPU only (WORLD_SIZE > 1 given)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    if args.calibrate_copy:
+        calibrate_copy()
+        return 0
+
+    import quantized_attention_smooth_amd as sa
+    from workloads import WORKLOADS, make_inputs
+
+    w = WORKLOADS[args.workload]
+    q, k, v = make_inputs(w, seed=0)
+    dev = torch.device("cuda:0")
+    qd = torch.from_numpy(q).to(dev)
+    kd = torch.from_numpy(k).to(dev)
+    vd = torch.from_numpy(v).to(dev)
+    o = torch.empty_like(qd)
+    nbytes = sa.workspace_bytes(w.B, w.H, w.Hkv, w.N, w.d, w.causal, w.qk_bits)
+    ws = sa.alloc_workspace(nbytes, dev)
+    shape = (w.B, w.H, w.N, w.d)
+
+    def step():
+        sa.prologue(qd, kd, vd, ws, w.causal, w.qk_bits)
+        sa.attend(o, ws, shape, w.Hkv, w.causal, w.qk_bits)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if not torch.isfinite(o).all():
+        print("non-finite output", file=sys.stderr)
+        return 1
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    e_start, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e_start.record()
+    for s in range(K):
+        ev[s][0].record()
+        sa.prologue(qd, kd, vd, ws, w.causal, w.qk_bits)
+        ev[s][1].record()
+        sa.attend(o, ws, shape, w.Hkv, w.causal, w.qk_bits)
+        ev[s][2].record()
+    e_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    ms_step = e_start.elapsed_time(e_end) / K
+    pro_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    att_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    ops = w.ops
+    value = ops / (ms_step * 1e-3) / 1e12
+    achieved = ops / (att_ms * 1e-3) / 1e12
+    nqb = -(-w.N // 128)
+    npad = nqb * 128
+    n_q, n_kv = w.B * w.H * w.N * w.d, w.B * w.Hkv * w.N * w.d
+    pro_bytes = 2 * (n_q + 2 * n_kv) + (n_q + 2 * n_kv) + 4 * w.B * w.H * nqb * npad
+    traffic = _traffic(args.workload)
+
+    line = {
+        "metric": METRIC, "value": value, "unit": "TOPS", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "i8+fp8e4m3", "data": "synthetic",
+        "config": {"workload": _describe(w), "B": w.B, "H": w.H, "Hkv": w.Hkv, "N": w.N, "d": w.d,
+                   "causal": w.causal, "qk_bits": w.qk_bits, "seed": 0},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_TOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_TOPS, "traffic": traffic,
+                     "kernel": "attn_fwd (fused QK^T int8 MFMA + softmax + P~V fp8 MFMA)",
+                     "per_unit": f"4*d = {4 * w.d} int8/fp8 ops per score element; "
+                                 f"{ops / (4 * w.d):.4g} score elements per launch"},
+        "breakdown": {"prologue_ms": pro_ms, "attention_ms": att_ms,
+                      "prologue_GBps_algorithmic": pro_bytes / (pro_ms * 1e-3) / 1e9,
+                      "prologue_frac_hbm": pro_bytes / (pro_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                      "wall_s_timed": wall},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_budget)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

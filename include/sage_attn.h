@@ -94,6 +94,20 @@ int sage_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, i
                   size_t workspace_bytes, void* stream);
 
 /*
+ * The two halves of sage_attn_fwd, for callers that time or schedule them separately.
+ * sage_attn_prologue smooths and quantizes q, k, v into `workspace` (K/Q/V codes, scales,
+ * means and the Delta_S bias).  sage_attn_attend runs the fused attention kernel on a
+ * workspace the prologue filled for the same (B, H, Hkv, N, d, causal, qk_bits) and writes
+ * o; a workspace filled for another problem gives meaningless output.  Stream ordered;
+ * same argument and error rules as sage_attn_fwd.
+ */
+int sage_attn_prologue(const void* q, const void* k, const void* v, int B, int H, int Hkv, int N,
+                       int d, int causal, int qk_bits, void* workspace, size_t workspace_bytes,
+                       void* stream);
+int sage_attn_attend(void* o, int B, int H, int Hkv, int N, int d, int causal, int qk_bits,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Test/debug: run the prologue only and copy its results, in plain layouts, to the
  * caller's device buffers (any pointer may be NULL to skip it):
  *   mu_k     fp32 [B, Hkv, d]            mean of K over all N keys

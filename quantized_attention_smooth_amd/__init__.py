@@ -1,7 +1,7 @@
 """MI355X (gfx950) SageAttention2 quantized attention forward.
 
 A thin Python binding over the C ABI in include/sage_attn.h (libsage_mi355x.so, built by
-quantized_attention_smooth_amd.build).  Every step of the computation runs in the library's
+quantized_attention_smooth_amd/build.py).  Every step of the computation runs in the library's
 HIP kernels; this module only checks arguments, allocates the output and the workspace with
 torch, and passes raw device pointers and the current stream.  There is no fallback: if the
 library is missing or fails to load, importing this package raises ImportError.
@@ -16,7 +16,7 @@ import os
 
 import torch
 
-__all__ = ["sageattn", "fwd", "workspace_bytes", "get_config", "quant_debug", "qk_tile_debug",
+__all__ = ["sageattn", "fwd", "prologue", "attend", "workspace_bytes", "get_config", "quant_debug", "qk_tile_debug",
            "LIB_PATH", "SageError"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsage_mi355x.so")
@@ -28,8 +28,9 @@ SAGE_ERR_WORKSPACE = -3
 SAGE_ERR_HIP = -4
 
 #: every symbol include/sage_attn.h declares
-EXPORTS = ("sage_get_config", "sage_attn_workspace_bytes", "sage_attn_fwd", "sage_quant_debug",
-           "sage_qk_tile_debug", "sage_status_string", "sage_last_error")
+EXPORTS = ("sage_get_config", "sage_attn_workspace_bytes", "sage_attn_fwd", "sage_attn_prologue",
+           "sage_attn_attend", "sage_quant_debug", "sage_qk_tile_debug", "sage_status_string",
+           "sage_last_error")
 
 
 class SageConfig(ctypes.Structure):
@@ -47,7 +48,7 @@ class SageError(RuntimeError):
 
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m quantized_attention_smooth_amd.build`")
+        raise ImportError(f"{LIB_PATH} is not built; run `python quantized_attention_smooth_amd/build.py`")
     try:
         lib = ctypes.CDLL(LIB_PATH)
     except OSError as e:
@@ -56,14 +57,16 @@ def _load() -> ctypes.CDLL:
     lib.sage_get_config.argtypes = [ctypes.POINTER(SageConfig)]
     lib.sage_attn_workspace_bytes.argtypes = [I, I, I, I, I, I, I, ctypes.POINTER(S)]
     lib.sage_attn_fwd.argtypes = [P, P, P, P, I, I, I, I, I, I, I, P, S, P]
+    lib.sage_attn_prologue.argtypes = [P, P, P, I, I, I, I, I, I, I, P, S, P]
+    lib.sage_attn_attend.argtypes = [P, I, I, I, I, I, I, I, P, S, P]
     lib.sage_quant_debug.argtypes = [P, P, P, I, I, I, I, I, I, I, P, S, P] + [P] * 9
     lib.sage_qk_tile_debug.argtypes = [P, P, P, I, I, I, I, I, I, I, P, S, P, I, I, I, I, P]
     lib.sage_status_string.argtypes = [I]
     lib.sage_status_string.restype = ctypes.c_char_p
     lib.sage_last_error.argtypes = []
     lib.sage_last_error.restype = ctypes.c_char_p
-    for name in ("sage_get_config", "sage_attn_workspace_bytes", "sage_attn_fwd", "sage_quant_debug",
-                 "sage_qk_tile_debug"):
+    for name in ("sage_get_config", "sage_attn_workspace_bytes", "sage_attn_fwd", "sage_attn_prologue",
+                 "sage_attn_attend", "sage_quant_debug", "sage_qk_tile_debug"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -131,6 +134,24 @@ def fwd(q, k, v, o, workspace, is_causal: bool = False, qk_bits: int = 8) -> Non
         raise ValueError("o must be a contiguous float16 tensor shaped like q on q's device")
     _check(_lib.sage_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, Hkv, N, d, int(is_causal), qk_bits,
                               _ptr(workspace), workspace.numel(), _stream(q.device)))
+
+
+def prologue(q, k, v, workspace, is_causal: bool = False, qk_bits: int = 8) -> None:
+    """sage_attn_prologue: fill `workspace` with the quantized/smoothed operands."""
+    B, H, Hkv, N, d = _shapes(q, k, v)
+    _check(_lib.sage_attn_prologue(_ptr(q), _ptr(k), _ptr(v), B, H, Hkv, N, d, int(is_causal), qk_bits,
+                                   _ptr(workspace), workspace.numel(), _stream(q.device)))
+
+
+def attend(o, workspace, shape, Hkv: int, is_causal: bool = False, qk_bits: int = 8) -> None:
+    """sage_attn_attend: the fused attention kernel on a workspace filled by prologue().
+
+    shape = (B, H, N, d) of q/o."""
+    B, H, N, d = shape
+    if tuple(o.shape) != (B, H, N, d) or o.dtype != torch.float16 or not o.is_contiguous() or not o.is_cuda:
+        raise ValueError("o must be a contiguous float16 CUDA tensor of shape (B, H, N, d)")
+    _check(_lib.sage_attn_attend(_ptr(o), B, H, Hkv, N, d, int(is_causal), qk_bits, _ptr(workspace),
+                                 workspace.numel(), _stream(o.device)))
 
 
 def sageattn(q, k, v, attn_mask=None, dropout_p: float = 0.0, is_causal: bool = False, scale=None,

@@ -1,6 +1,7 @@
 """Build the gfx950 HIP library in-tree: quantized_attention_smooth_amd/libsage_mi355x.so.
 
-Run `python -m quantized_attention_smooth_amd.build` (or call build()).  hipcc cross-compiles
+Run `python quantized_attention_smooth_amd/build.py` (or call build()); it imports nothing from
+the package, whose import loads the library this script builds.  hipcc cross-compiles
 for gfx950 without a GPU present.
 """
 from __future__ import annotations

@@ -97,6 +97,34 @@ int sage_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, i
   return SAGE_OK;
 }
 
+int sage_attn_prologue(const void* q, const void* k, const void* v, int B, int H, int Hkv, int N, int d,
+                       int causal, int qk_bits, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v) return SAGE_ERR_INVALID_ARG;
+  sage::Dims D;
+  int st = check_dims(B, H, Hkv, N, d, causal, qk_bits, &D);
+  if (st != SAGE_OK) return st;
+  const sage::Layout L = sage::make_layout(D);
+  st = check_ws(workspace, workspace_bytes, L);
+  if (st != SAGE_OK) return st;
+  const sage::Ptrs P = sage::carve(workspace, L, q, k, v, nullptr);
+  const hipError_t e = sage::launch_prologue(D, P, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SAGE_OK : hip_fail(e, "prologue launch");
+}
+
+int sage_attn_attend(void* o, int B, int H, int Hkv, int N, int d, int causal, int qk_bits, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  if (!o) return SAGE_ERR_INVALID_ARG;
+  sage::Dims D;
+  int st = check_dims(B, H, Hkv, N, d, causal, qk_bits, &D);
+  if (st != SAGE_OK) return st;
+  const sage::Layout L = sage::make_layout(D);
+  st = check_ws(workspace, workspace_bytes, L);
+  if (st != SAGE_OK) return st;
+  const sage::Ptrs P = sage::carve(workspace, L, nullptr, nullptr, nullptr, o);
+  const hipError_t e = sage::launch_attention(D, P, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SAGE_OK : hip_fail(e, "attention launch");
+}
+
 int sage_quant_debug(const void* q, const void* k, const void* v, int B, int H, int Hkv, int N, int d, int causal,
                      int qk_bits, void* workspace, size_t workspace_bytes, void* stream, void* mu_k, void* k_codes,
                      void* k_scales, void* v_codes, void* v_scales, void* mu_q, void* q_codes, void* q_scales,

@@ -26,6 +26,8 @@
 //     double buffered, 16-byte chunks XOR-swizzled against LDS bank conflicts.
 //   * Workgroup ids are remapped so each XCD (own L2) works through whole heads; causal
 //     grids start with the longest (diagonal-most) query blocks.
+#include <type_traits>
+
 #include "sage_internal.h"
 
 namespace sage {
@@ -56,10 +58,17 @@ struct AttnArgs {
 
 template <int D>
 struct Smem {
-  int8_t k[2][BK * D];       // K tile rows, 16-byte chunks swizzled
-  uint8_t v[2][BK * D];      // [64-key group][channel][64 slots], 16-byte chunks swizzled
-  float ds[2][BK];
+  __attribute__((aligned(16))) int8_t k[2][BK * D];    // K tile rows, 16-byte chunks swizzled
+  __attribute__((aligned(16))) uint8_t v[2][BK * D];   // [64-key group][channel][64 slots], swizzled
+  __attribute__((aligned(16))) float ds[2][BK];
 };
+
+// The int32 S^T accumulators start from the bit pattern of the float 1.5 * 2^23.  |S| <= 127^2 * 128
+// < 2^21, so after the integer MFMA adds S the bits read as the float 1.5 * 2^23 + S exactly (same
+// binade, unit spacing); one exact fp32 subtraction then yields S as a float.  This replaces the
+// int->float conversion, which issues at a quarter of the fp32 add rate on gfx950.
+constexpr int kAccBias = 0x4B400000;
+constexpr float kAccBiasF = 12582912.0f;   // 1.5 * 2^23
 
 // swizzle of the 16-byte chunk index inside a K row (row = key within the tile)
 template <int D>
@@ -110,7 +119,8 @@ __device__ inline void qk_tiles(const Smem<D>& sm, int st, const v4i (&qreg)[D /
                                 v16i (&sacc)[BK / 32]) {
 #pragma unroll
   for (int t = 0; t < BK / 32; ++t) {
-    v16i acc = {};
+    v16i acc = {kAccBias, kAccBias, kAccBias, kAccBias, kAccBias, kAccBias, kAccBias, kAccBias,
+                kAccBias, kAccBias, kAccBias, kAccBias, kAccBias, kAccBias, kAccBias, kAccBias};
     const int row = 32 * t + col;
 #pragma unroll
     for (int s = 0; s < D / 32; ++s) {
@@ -166,7 +176,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int jl = 32 * t + 8 * (e >> 2) + 4 * half + (e & 3);
-        a.dbg_out[il * BK + jl] = sacc[t][e];
+        a.dbg_out[il * BK + jl] = sacc[t][e] - kAccBias;
       }
     return;
   }
@@ -181,20 +191,21 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
   wait_loads();
   __syncthreads();
 
-  for (int kb = 0; kb < nblk; ++kb) {
+  // One KV block: S^T on the int8 MFMA, dequantize + bias (+ mask), online softmax, P~ V on the
+  // FP8 MFMA.  MASK is set only for the last block of a row range (causal diagonal or ragged tail).
+  auto block = [&](const int kb, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     const int st = kb & 1;
     if (kb + 1 < nblk) issue_tile<D>(a, sm, st ^ 1, bkv, bh, qb, kb + 1, w, lane);
 
     v16i sacc[BK / 32];
     qk_tiles<D>(sm, st, qreg, col, half, sacc);
 
-    // dequantize, add the Q-smoothing bias, mask; log2 domain
+    // dequantize and add the Q-smoothing bias, in the log2 domain
     const float kd = a.kscale[(bkv * a.nkb + kb) * 2 + half];
     const float cmul = qd * kd * a.k2;
     float z[BK / 32][16];
     float mloc = -INFINITY;
-    const bool diag = CAUSAL && kb == qb;
-    const bool tail = (kb + 1) * BK > a.N;
 #pragma unroll
     for (int t = 0; t < BK / 32; ++t) {
 #pragma unroll
@@ -204,12 +215,15 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
         const float dsa[4] = {dsv.x, dsv.y, dsv.z, dsv.w};
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          float x = (float)sacc[t][4 * qq + r] * cmul + dsa[r];
-          if (diag && j0 + r > il) x = -INFINITY;
-          if (tail && kb * BK + j0 + r >= a.N) x = -INFINITY;
+          const float sf = __int_as_float(sacc[t][4 * qq + r]) - kAccBiasF;   // exact S
+          float x = fmaf(sf, cmul, dsa[r]);
+          if (MASK) {
+            const int j = kb * BK + j0 + r;
+            if ((CAUSAL && j > i) || j >= a.N) x = -INFINITY;
+          }
           z[t][4 * qq + r] = x;
-          mloc = fmaxf(mloc, x);
         }
+        mloc = fmaxf(mloc, fmaxf(fmaxf(z[t][4 * qq], z[t][4 * qq + 1]), fmaxf(z[t][4 * qq + 2], z[t][4 * qq + 3])));
       }
     }
     // row max across the two lane halves holding the same query
@@ -228,17 +242,17 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
     for (int t = 0; t < BK / 32; ++t) {
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq) {
-        float p0 = __builtin_amdgcn_exp2f(z[t][4 * qq + 0] - mo);
-        float p1 = __builtin_amdgcn_exp2f(z[t][4 * qq + 1] - mo);
-        float p2 = __builtin_amdgcn_exp2f(z[t][4 * qq + 2] - mo);
-        float p3 = __builtin_amdgcn_exp2f(z[t][4 * qq + 3] - mo);
+        const float p0 = __builtin_amdgcn_exp2f(z[t][4 * qq + 0] - mo);
+        const float p1 = __builtin_amdgcn_exp2f(z[t][4 * qq + 1] - mo);
+        const float p2 = __builtin_amdgcn_exp2f(z[t][4 * qq + 2] - mo);
+        const float p3 = __builtin_amdgcn_exp2f(z[t][4 * qq + 3] - mo);
         lsum += (p0 + p1) + (p2 + p3);
         int word = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
         word = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, word, true);
         pb[t >> 1][(t & 1) * 4 + qq] = word;
       }
     }
-    l_part = l_part * alpha + lsum;
+    l_part = fmaf(l_part, alpha, lsum);
 
     // P~ V: block-local accumulation from zero, then the fp32 global accumulator
 #pragma unroll
@@ -260,7 +274,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
 
     wait_loads();
     __syncthreads();
-  }
+  };
+
+  // the last block needs masking when causal (diagonal block) or when N is not a multiple of BK
+  const bool mask_last = CAUSAL || (a.N % BK) != 0;
+  const int nfull = mask_last ? nblk - 1 : nblk;
+  for (int kb = 0; kb < nfull; ++kb) block(kb, std::false_type{});
+  if (mask_last) block(nblk - 1, std::true_type{});
 
   // epilogue: O = acc * delta_V / l   (l counts p * P_r, so it carries the 1/P_r)
   const float l = l_part + __shfl_xor(l_part, 32, 64);

@@ -13,9 +13,20 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "sage_attn.h")
 
 
+def _build_module():
+    """quantized_attention_smooth_amd/build.py, loaded by path so that building never needs the
+    package (whose import loads the library) to import first."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "_sage_build", os.path.join(ROOT, "quantized_attention_smooth_amd", "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
 @pytest.fixture(scope="module")
 def pkg():
-    from quantized_attention_smooth_amd import build as b
+    b = _build_module()
     if not os.path.exists(b.LIB):
         b.build()
     import quantized_attention_smooth_amd as p

@@ -33,7 +33,7 @@ sys.path.insert(0, ROOT)
 METRIC = "effective attention TOPS (4·B·H·N²·d/t, ½ if causal) at N=8K–32K, d=64/128"
 PEAK_TOPS = 5000.0          # MI355X dense INT8 (POP/s) and FP8 (PFLOP/s): 5.0 P each
 PEAK_HBM_GBPS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.txt")
 ATTN_SRC = os.path.join(ROOT, "quantized_attention_smooth_amd", "csrc", "attention.hip")
 
 

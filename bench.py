@@ -195,7 +195,8 @@ def main() -> int:
     nqb = -(-w.N // 128)
     npad = nqb * 128
     n_q, n_kv = w.B * w.H * w.N * w.d, w.B * w.Hkv * w.N * w.d
-    pro_bytes = 2 * (n_q + 2 * n_kv) + (n_q + 2 * n_kv) + 4 * w.B * w.H * nqb * npad
+    ds_elems = 128 * nqb * (nqb + 1) // 2 if w.causal else nqb * npad     # Delta_S rows per head
+    pro_bytes = 2 * (n_q + 2 * n_kv) + (n_q + 2 * n_kv) + 4 * w.B * w.H * ds_elems
     traffic = _traffic(args.workload)
 
     line = {

@@ -118,7 +118,9 @@ int sage_attn_attend(void* o, int B, int H, int Hkv, int N, int d, int causal, i
  *   mu_q     fp32 [B, H, ceil(N/bq), d]  per-block mean of Q
  *   q_codes  int8 [B, H, N, d]           quantized smoothed Q
  *   q_scales fp32 [B, H, N]              scale of each query's group
- *   delta_s  fp32 [B, H, ceil(N/bq), N] mu_Q . gamma_K^T (natural units, not log2)
+ *   delta_s  fp32 [B, H, ceil(N/bq), N] mu_Q . gamma_K^T (natural units, not log2); when
+ *            causal, row qb holds only keys j < (qb + 1) * bq (the keys that block can see)
+ *            and zeros beyond
  * Same tensor/workspace/stream rules as sage_attn_fwd.
  */
 int sage_quant_debug(const void* q, const void* k, const void* v, int B, int H, int Hkv, int N,

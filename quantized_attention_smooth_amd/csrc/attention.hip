@@ -51,6 +51,7 @@ struct AttnArgs {
   const float* ds;
   __half* o;
   int B, H, Hkv, N, Npad, nqb, nkb;
+  bool causal;          // Delta_S rows stored triangularly
   float k2;             // log2(e) / sqrt(d)
   int dbg_b, dbg_h, dbg_qb, dbg_kb;
   int32_t* dbg_out;
@@ -70,13 +71,27 @@ struct Smem {
 constexpr int kAccBias = 0x4B400000;
 constexpr float kAccBiasF = 12582912.0f;   // 1.5 * 2^23
 
-// swizzle of the 16-byte chunk index inside a K row (row = key within the tile)
+// XOR swizzles of the 16-byte chunk index inside an LDS row.  Each operand read has 32 lanes
+// fetch 16 bytes from 32 consecutive rows at one logical chunk; the swizzles spread those rows
+// over distinct bank groups whether the LDS serves 8 lanes per cycle over 32 banks or 16 lanes
+// per cycle over 64 banks (the former swizzle, row & 7, left 2-way conflicts on gfx950).
 template <int D>
-__device__ inline int kswz(int row) {
-  return D == 128 ? (row & 7) : ((row >> 1) & 3);
+__device__ inline int kswz(int row) {       // K rows: 128 bytes (d = 128) or 64 bytes (d = 64)
+  return D == 128 ? ((row ^ (row >> 3)) & 7) : (((row >> 1) ^ (row >> 3)) & 3);
 }
-// swizzle of the 16-byte chunk inside a 64-byte V^T row (c = channel)
-__device__ inline int vswz(int c) { return (c >> 1) & 3; }
+__device__ inline int vswz(int c) {         // V^T rows: 64 bytes per channel
+  return ((c >> 1) ^ (c >> 3)) & 3;
+}
+
+// combine a value with the one held by lane l ^ 32 (the other half holding the same query)
+__device__ inline float xhalf_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+  return fmaxf(__int_as_float(r[0]), __int_as_float(r[1]));
+}
+__device__ inline float xhalf_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+  return __int_as_float(r[0]) + __int_as_float(r[1]);
+}
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -106,7 +121,8 @@ __device__ inline void issue_tile(const AttnArgs& a, Smem<D>& sm, int st, size_t
     }
   }
   if (w == 0 && lane < BK / 4) {
-    const float* src = a.ds + (bh * a.nqb + qb) * (size_t)a.Npad + (size_t)kb * BK + lane * 4;
+    const float* src = a.ds + bh * ds_head_elems(a.causal, a.nqb, a.Npad) + ds_row_offset(a.causal, qb, a.Npad) +
+                       (size_t)kb * BK + lane * 4;
     __builtin_amdgcn_global_load_lds(src, (lds_void*)sm.ds[st], 16, 0, 0);
   }
 }
@@ -227,7 +243,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
       }
     }
     // row max across the two lane halves holding the same query
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+    mloc = xhalf_max(mloc);
     const float m_new = fmaxf(m_run, mloc);
     // a row has a finite max from its first block on (key 0 is never masked); the guards only
     // keep -inf - -inf out of the arithmetic
@@ -283,7 +299,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
   if (mask_last) block(nblk - 1, std::true_type{});
 
   // epilogue: O = acc * delta_V / l   (l counts p * P_r, so it carries the 1/P_r)
-  const float l = l_part + __shfl_xor(l_part, 32, 64);
+  const float l = xhalf_sum(l_part);
   const float inv_l = l > 0.f ? 1.f / l : 0.f;
   if (i < a.N) {
     __half* orow = a.o + (bh * a.N + i) * D;
@@ -316,6 +332,7 @@ AttnArgs make_args(const Dims& D, const Ptrs& P) {
   a.ds = P.ds;
   a.o = P.o;
   a.B = D.B; a.H = D.H; a.Hkv = D.Hkv; a.N = D.N; a.Npad = D.Npad; a.nqb = D.nqb; a.nkb = D.nkb;
+  a.causal = D.causal != 0;
   a.k2 = (float)(1.4426950408889634 / sqrt((double)D.d));
   return a;
 }

@@ -282,60 +282,106 @@ __global__ __launch_bounds__(256) void q_quant(const __half* __restrict__ q, int
 
 // ---------------------------------------------------------------------------------------
 // Delta_S[qb, j] = sum_c mu_Q[qb, c] * gamma_K[j, c], stored times log2(e)/sqrt(d).
-// Tiled fp32 GEMM: workgroup = 64 query blocks x 128 keys, channels in chunks of 32.
-// grid (Npad/128, ceil(nqb/64), B*H), 256 threads; thread = 4 query blocks x 8 keys.
+//
+// A GEMM (Q blocks x keys x channels) on the bf16 MFMA at fp32-class accuracy: every fp32
+// factor is split exactly into three bf16 parts, x = x1 + x2 + x3 (8 significant bits each,
+// 24 in all), and the six cross products whose weight is at least 2^-16 of the leading one
+// are accumulated, smallest first (x3y1 + x2y2 + x1y3 + x2y1 + x1y2 + x1y1); the dropped
+// terms are below 2^-24 of it.  The bf16 MFMA accumulates in fp32 (unlike the FP8 one).
+// gamma_K = RN32(K - mu_K) is recomputed from the fp16 keys; keys past N contribute zero.
+// grid (Npad/256 key tiles, ceil(nqb/32) Q-block tiles, B*H), 256 threads; each wave owns
+// 32 Q blocks x 64 keys (two 32x32 MFMA tiles).  Causal rows stop at key (qb + 1) * 128.
 // ---------------------------------------------------------------------------------------
-template <int D>
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+struct Split3 {
+  bf16x8 p[3];
+};
+
+__device__ inline Split3 split3(const float (&x)[8]) {
+  Split3 s;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const __bf16 b1 = (__bf16)x[e];
+    const float r1 = x[e] - (float)b1;       // exact: b1 is x rounded to 8 significant bits
+    const __bf16 b2 = (__bf16)r1;
+    const float r2 = r1 - (float)b2;         // exact
+    s.p[0][e] = b1;
+    s.p[1][e] = b2;
+    s.p[2][e] = (__bf16)r2;                  // r2 has at most 8 significant bits left: exact
+  }
+  return s;
+}
+
+template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) void delta_s(const __half* __restrict__ k, const float* __restrict__ muk,
                                                const float* __restrict__ muq, float* __restrict__ ds,
                                                int H, int Hkv, int N, int Npad, int nqb, float k2) {
-  constexpr int QT = 64, KT = 128, CC = 32;
-  __shared__ float sq[QT][CC + 1];
-  __shared__ float sk[KT][CC + 1];
-  const int tid = threadIdx.x;
-  const int kt = blockIdx.x, qt = blockIdx.y;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, r = lane & 31, hl = lane >> 5;
   const int bh = blockIdx.z, b = bh / H, h = bh % H, hk = h / (H / Hkv);
   const size_t bkv = (size_t)b * Hkv + hk;
-  const __half* kbase = k + bkv * (size_t)N * D;
-  const int tq = tid / 16, tk = tid % 16;
-  float acc[4][8];
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[a][e] = 0.f;
-  for (int c0 = 0; c0 < D; c0 += CC) {
-    for (int i = tid; i < QT * CC; i += 256) {
-      const int r = i / CC, c = i % CC, qb = qt * QT + r;
-      sq[r][c] = qb < nqb ? muq[((size_t)bh * nqb + qb) * D + c0 + c] : 0.f;
+  const int q0 = blockIdx.y * 32;                      // first Q block of this tile
+  const int j0 = blockIdx.x * 256 + w * 64;            // first key of this wave
+  const int qlast = min(q0 + 31, nqb - 1);
+  if (CAUSAL && j0 >= (qlast + 1) * BQ) return;        // every row of the tile stops earlier
+  const int qb = q0 + r;                               // A row (operand) of this lane
+  const bool qvalid = qb < nqb;
+  const __half* kb = k + bkv * (size_t)N * D;
+  f32x16 acc[2] = {};
+#pragma unroll 2
+  for (int ks = 0; ks < D / 16; ++ks) {
+    const int c0 = 16 * ks + 8 * hl;
+    float xa[8];
+    {
+      float4 m0 = make_float4(0.f, 0.f, 0.f, 0.f), m1 = m0;
+      if (qvalid) {
+        const float* src = muq + ((size_t)bh * nqb + qb) * D + c0;
+        m0 = *reinterpret_cast<const float4*>(src);
+        m1 = *reinterpret_cast<const float4*>(src + 4);
+      }
+      xa[0] = m0.x; xa[1] = m0.y; xa[2] = m0.z; xa[3] = m0.w;
+      xa[4] = m1.x; xa[5] = m1.y; xa[6] = m1.z; xa[7] = m1.w;
     }
-    for (int i = tid; i < KT * CC; i += 256) {
-      const int r = i / CC, c = i % CC, j = kt * KT + r;
-      sk[r][c] = j < N ? __half2float(kbase[(size_t)j * D + c0 + c]) - muk[bkv * D + c0 + c] : 0.f;
+    const Split3 A = split3(xa);
+    const float4 mk0 = *reinterpret_cast<const float4*>(muk + bkv * D + c0);
+    const float4 mk1 = *reinterpret_cast<const float4*>(muk + bkv * D + c0 + 4);
+    const float mkv[8] = {mk0.x, mk0.y, mk0.z, mk0.w, mk1.x, mk1.y, mk1.z, mk1.w};
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int j = j0 + 32 * t + r;                   // B column (key) of this lane
+      float xb[8];
+      if (j < N) {
+        const Half8 kk = load8(kb + (size_t)j * D + c0);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xb[e] = __half2float(kk.h[e]) - mkv[e];   // gamma_K, RN32
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xb[e] = 0.f;
+      }
+      const Split3 Bv = split3(xb);
+      f32x16 c = acc[t];
+      c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A.p[2], Bv.p[0], c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A.p[1], Bv.p[1], c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A.p[0], Bv.p[2], c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A.p[1], Bv.p[0], c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A.p[0], Bv.p[1], c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A.p[0], Bv.p[0], c, 0, 0, 0);
+      acc[t] = c;
     }
-    __syncthreads();
-#pragma unroll 4
-    for (int c = 0; c < CC; ++c) {
-      float qv[4], kv[8];
-#pragma unroll
-      for (int a = 0; a < 4; ++a) qv[a] = sq[4 * tq + a][c];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) kv[e] = sk[tk + 16 * e][c];
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[a][e] = fmaf(qv[a], kv[e], acc[a][e]);
-    }
-    __syncthreads();
   }
+  // lane holds rows q0 + 8a + 4hl + e (e < 4) of key column j0 + 32t + r
+  float* dsh = ds + (size_t)bh * ds_head_elems(CAUSAL, nqb, Npad);
 #pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    const int qb = qt * QT + 4 * tq + a;
-    if (qb >= nqb) continue;
+  for (int t = 0; t < 2; ++t) {
+    const int j = j0 + 32 * t + r;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int j = kt * KT + tk + 16 * e;
-      ds[((size_t)bh * nqb + qb) * Npad + j] = acc[a][e] * k2;
-    }
+    for (int a4 = 0; a4 < 4; ++a4)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int q = q0 + 8 * a4 + 4 * hl + e;
+        if (q < nqb && j < ds_row_len(CAUSAL, q, Npad)) dsh[ds_row_offset(CAUSAL, q, Npad) + j] = acc[t][4 * a4 + e] * k2;
+      }
   }
 }
 
@@ -356,6 +402,18 @@ __global__ void copy_rows_f32(const float* __restrict__ src, float* __restrict__
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
     const size_t r = i / n, c = i % n;
     dst[i] = src[r * npad + c] * mul;
+  }
+}
+// Delta_S rows -> [heads][nqb][N] in natural units; entries a causal row does not store are 0
+__global__ void copy_ds(const float* __restrict__ src, float* __restrict__ dst, int heads, int nqb, int N, int Npad,
+                        bool causal, float mul) {
+  const size_t total = (size_t)heads * nqb * N;
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
+    const size_t hd = i / ((size_t)nqb * N);
+    const int qb = (int)((i / N) % nqb), j = (int)(i % N);
+    dst[i] = j < ds_row_len(causal, qb, Npad)
+                 ? src[hd * ds_head_elems(causal, nqb, Npad) + ds_row_offset(causal, qb, Npad) + j] * mul
+                 : 0.f;
   }
 }
 __global__ void expand_kscale(const float* __restrict__ kscale, float* __restrict__ dst, int heads, int N, int nkb) {
@@ -388,8 +446,11 @@ hipError_t launch_prologue_d(const Dims& Dm, const Ptrs& P, hipStream_t s) {
                                                           P.kscale, P.muk, P.vscale, Dm.N, Dm.Npad, Dm.nkb, R);
   q_quant<D><<<dim3(Dm.nqb, Dm.B * Dm.H), 256, 0, s>>>(P.q, P.qcodes, P.qscale, P.muq, Dm.N, Dm.Npad, Dm.nqb, R);
   const float k2 = (float)(1.4426950408889634 / sqrt((double)D));
-  delta_s<D><<<dim3(Dm.Npad / 128, (Dm.nqb + 63) / 64, Dm.B * Dm.H), 256, 0, s>>>(
-      P.k, P.muk, P.muq, P.ds, Dm.H, Dm.Hkv, Dm.N, Dm.Npad, Dm.nqb, k2);
+  const dim3 gds((Dm.Npad + 255) / 256, (Dm.nqb + 31) / 32, Dm.B * Dm.H);
+  if (Dm.causal)
+    delta_s<D, true><<<gds, 256, 0, s>>>(P.k, P.muk, P.muq, P.ds, Dm.H, Dm.Hkv, Dm.N, Dm.Npad, Dm.nqb, k2);
+  else
+    delta_s<D, false><<<gds, 256, 0, s>>>(P.k, P.muk, P.muq, P.ds, Dm.H, Dm.Hkv, Dm.N, Dm.Npad, Dm.nqb, k2);
   return hipGetLastError();
 }
 
@@ -423,7 +484,7 @@ hipError_t launch_debug_copy(const Dims& D, const Ptrs& P, hipStream_t s, float*
   if (v_codes) unpermute_v<<<grid, blk, 0, s>>>(P.vcodes, v_codes, hkv, D.N, D.Npad, D.d);
   if (delta_s_out) {
     const float inv_k2 = (float)(sqrt((double)D.d) / 1.4426950408889634);
-    copy_rows_f32<<<grid, blk, 0, s>>>(P.ds, delta_s_out, (size_t)hq * D.nqb, D.N, D.Npad, inv_k2);
+    copy_ds<<<grid, blk, 0, s>>>(P.ds, delta_s_out, hq, D.nqb, D.N, D.Npad, D.causal != 0, inv_k2);
   }
   return hipGetLastError();
 }

@@ -40,7 +40,21 @@ struct Dims {
 //  vamax  : u32   [B][Hkv][d]                 bits of max|V| per channel (non-negative floats)
 //  vscale : fp32  [B][Hkv][d]                 delta_V
 //  muq    : fp32  [B][H][nqb][d]
-//  ds     : fp32  [B][H][nqb][Npad]           Delta_S * log2(e) / sqrt(d)
+//  ds     : fp32  per (b, h): the rows of Delta_S * log2(e) / sqrt(d), one per Q block.
+//           Non-causal: nqb rows of Npad keys.  Causal: row qb holds only the keys a causal
+//           Q block can see, j < (qb + 1) * 128, packed back to back (ds_row_offset).
+//           Entries past N are zero.
+// Delta_S storage: elements per (b, h) and the offset of Q block qb's row inside it.
+__host__ __device__ inline size_t ds_head_elems(bool causal, int nqb, int Npad) {
+  return causal ? (size_t)BQ * nqb * (nqb + 1) / 2 : (size_t)nqb * Npad;
+}
+__host__ __device__ inline size_t ds_row_offset(bool causal, int qb, int Npad) {
+  return causal ? (size_t)BQ * qb * (qb + 1) / 2 : (size_t)qb * Npad;
+}
+__host__ __device__ inline int ds_row_len(bool causal, int qb, int Npad) {
+  return causal ? (qb + 1) * BQ : Npad;
+}
+
 struct Layout {
   size_t kcodes, vcodes, qcodes, kscale, qscale, muk, ksum, vamax, vscale, muq, ds, total;
 };
@@ -62,7 +76,7 @@ inline Layout make_layout(const Dims& D) {
   L.vamax = take(B * Hkv * d * 4);
   L.vscale = take(B * Hkv * d * 4);
   L.muq = take(B * H * (size_t)D.nqb * d * 4);
-  L.ds = take(B * H * (size_t)D.nqb * Np * 4);
+  L.ds = take(B * H * ds_head_elems(D.causal != 0, D.nqb, D.Npad) * 4);
   L.total = off;
   return L;
 }

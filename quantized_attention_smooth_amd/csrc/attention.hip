@@ -100,6 +100,7 @@ __device__ inline void issue_tile(const AttnArgs& a, Smem<D>& sm, int st, size_t
                                   int w, int lane) {
   constexpr int CPR = D / 16;                 // 16-byte chunks per K row
   constexpr int NI = BK * D / 16 / 64 / WAVES; // direct-to-LDS instructions per wave per tile
+  // wave-uniform tile bases (scalar registers) plus 32-bit per-lane byte offsets
   const int8_t* kbase = a.kcodes + (bkv * a.Npad + (size_t)kb * BK) * D;
   const uint8_t* vbase = a.vcodes + (bkv * (size_t)(a.Npad / VGROUP) + (size_t)kb * 2) * D * VGROUP;
 #pragma unroll
@@ -108,22 +109,19 @@ __device__ inline void issue_tile(const AttnArgs& a, Smem<D>& sm, int st, size_t
     const int p = blk * 64 + lane;            // 16-byte chunk index in LDS
     {
       const int row = p / CPR, pc = p % CPR;
-      const int lc = pc ^ kswz<D>(row);
-      __builtin_amdgcn_global_load_lds(kbase + (size_t)row * D + lc * 16,
-                                       (lds_void*)(sm.k[st] + blk * 1024), 16, 0, 0);
+      const uint32_t off = (uint32_t)(row * D + ((pc ^ kswz<D>(row)) * 16));
+      __builtin_amdgcn_global_load_lds(kbase + off, (lds_void*)(sm.k[st] + blk * 1024), 16, 0, 0);
     }
     {
       const int row = p >> 2, pc = p & 3;     // row = group * D + channel
-      const int c = row % D;
-      const int lc = pc ^ vswz(c);
-      __builtin_amdgcn_global_load_lds(vbase + (size_t)row * VGROUP + lc * 16,
-                                       (lds_void*)(sm.v[st] + blk * 1024), 16, 0, 0);
+      const uint32_t off = (uint32_t)(row * VGROUP + ((pc ^ vswz(row % D)) * 16));
+      __builtin_amdgcn_global_load_lds(vbase + off, (lds_void*)(sm.v[st] + blk * 1024), 16, 0, 0);
     }
   }
   if (w == 0 && lane < BK / 4) {
     const float* src = a.ds + bh * ds_head_elems(a.causal, a.nqb, a.Npad) + ds_row_offset(a.causal, qb, a.Npad) +
-                       (size_t)kb * BK + lane * 4;
-    __builtin_amdgcn_global_load_lds(src, (lds_void*)sm.ds[st], 16, 0, 0);
+                       (size_t)kb * BK;
+    __builtin_amdgcn_global_load_lds(src + (uint32_t)(lane * 4), (lds_void*)sm.ds[st], 16, 0, 0);
   }
 }
 
@@ -218,7 +216,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
     qk_tiles<D>(sm, st, qreg, col, half, sacc);
 
     // dequantize and add the Q-smoothing bias, in the log2 domain
-    const float kd = a.kscale[(bkv * a.nkb + kb) * 2 + half];
+    // both lane halves' delta_K through one wave-uniform (scalar) load, so that waiting for it
+    // does not also wait for the tile prefetch just issued
+    typedef __attribute__((address_space(4))) const float cfloat;   // read-only here: scalar load
+    const cfloat* kdp = (const cfloat*)(a.kscale + (bkv * a.nkb + kb) * 2);
+    const float kd0 = kdp[0], kd1 = kdp[1];
+    const float kd = half ? kd1 : kd0;
     const float cmul = qd * kd * a.k2;
     float z[BK / 32][16];
     float mloc = -INFINITY;
@@ -227,8 +230,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq) {
         const int j0 = 32 * t + 8 * qq + 4 * half;
-        const float4 dsv = *reinterpret_cast<const float4*>(&sm.ds[st][j0]);
-        const float dsa[4] = {dsv.x, dsv.y, dsv.z, dsv.w};
+        // read as an int vector: this stage was filled and waited for in the previous block
+        const v4i dsv = *reinterpret_cast<const v4i*>(&sm.ds[st][j0]);
+        const float dsa[4] = {__int_as_float(dsv[0]), __int_as_float(dsv[1]), __int_as_float(dsv[2]), __int_as_float(dsv[3])};
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const float sf = __int_as_float(sacc[t][4 * qq + r]) - kAccBiasF;   // exact S

@@ -127,22 +127,41 @@ __device__ inline void issue_tile(const AttnArgs& a, Smem<D>& sm, int st, size_t
 
 __device__ inline void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// S^T tile t (32 keys) x the wave's 32 queries, exact int32
-template <int D>
+// S^T tiles (32 keys each) x the wave's 32 queries, exact.  INT8 codes: v_mfma_i32_32x32x32_i8
+// from the biased accumulator (see kAccBias), 16 code bytes per lane per k-step.  INT4-range codes
+// (stored as E4M3 bytes): v_mfma_f32_32x32x64_f8f6f4 from zero, 32 bytes per lane per k-step; the
+// products and sums of integers this small are exact in its accumulator, so S arrives as fp32.
+template <int D, bool QK4>
 __device__ inline void qk_tiles(const Smem<D>& sm, int st, const v4i (&qreg)[D / 32], int col, int half,
                                 v16i (&sacc)[BK / 32]) {
 #pragma unroll
   for (int t = 0; t < BK / 32; ++t) {
-    v16i acc = {kAccBias, kAccBias, kAccBias, kAccBias, kAccBias, kAccBias, kAccBias, kAccBias,
-                kAccBias, kAccBias, kAccBias, kAccBias, kAccBias, kAccBias, kAccBias, kAccBias};
     const int row = 32 * t + col;
+    if (QK4) {
+      v16f acc = {};
 #pragma unroll
-    for (int s = 0; s < D / 32; ++s) {
-      const int pc = (2 * s + half) ^ kswz<D>(row);
-      const v4i av = *reinterpret_cast<const v4i*>(sm.k[st] + row * D + pc * 16);
-      acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(av, qreg[s], acc, 0, 0, 0);
+      for (int s = 0; s < D / 64; ++s) {
+        const int c0 = 4 * s + 2 * half;       // this lane's two 16-byte chunks of the 64-channel step
+        const v4i lo = *reinterpret_cast<const v4i*>(sm.k[st] + row * D + (c0 ^ kswz<D>(row)) * 16);
+        const v4i hi = *reinterpret_cast<const v4i*>(sm.k[st] + row * D + ((c0 + 1) ^ kswz<D>(row)) * 16);
+        const v8i av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        const v8i bv = {qreg[2 * s][0], qreg[2 * s][1], qreg[2 * s][2], qreg[2 * s][3],
+                        qreg[2 * s + 1][0], qreg[2 * s + 1][1], qreg[2 * s + 1][2], qreg[2 * s + 1][3]};
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc, 0, 0, 0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sacc[t][e] = __float_as_int(acc[e]);
+    } else {
+      v16i acc = {kAccBias, kAccBias, kAccBias, kAccBias, kAccBias, kAccBias, kAccBias, kAccBias,
+                  kAccBias, kAccBias, kAccBias, kAccBias, kAccBias, kAccBias, kAccBias, kAccBias};
+#pragma unroll
+      for (int s = 0; s < D / 32; ++s) {
+        const int pc = (2 * s + half) ^ kswz<D>(row);
+        const v4i av = *reinterpret_cast<const v4i*>(sm.k[st] + row * D + pc * 16);
+        acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(av, qreg[s], acc, 0, 0, 0);
+      }
+      sacc[t] = acc;
     }
-    sacc[t] = acc;
   }
 }
 
@@ -152,7 +171,7 @@ __device__ inline int xcd_remap(int bid, int total) {
   return x * q + min(x, r) + k;
 }
 
-template <int D, bool CAUSAL, bool DUMP>
+template <int D, bool CAUSAL, bool DUMP, bool QK4>
 __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
   __shared__ Smem<D> sm;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, col = lane & 31, half = lane >> 5;
@@ -173,10 +192,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
   const int i = qb * BQ + il;
 
   // the wave's 32 query rows as the B operand of S^T = K Q^T (16 bytes per k-step)
+  // (INT4 range: 32 bytes per 64-channel step, held as two consecutive v4i)
   v4i qreg[D / 32];
 #pragma unroll
-  for (int s = 0; s < D / 32; ++s)
-    qreg[s] = *reinterpret_cast<const v4i*>(a.qcodes + (bh * a.Npad + i) * D + 32 * s + 16 * half);
+  for (int s = 0; s < D / 32; ++s) {
+    const int ch = QK4 ? 64 * (s >> 1) + 32 * half + 16 * (s & 1) : 32 * s + 16 * half;
+    qreg[s] = *reinterpret_cast<const v4i*>(a.qcodes + (bh * a.Npad + i) * D + ch);
+  }
   const float qd = a.qscale[bh * a.Npad + i];
 
   if (DUMP) {
@@ -184,13 +206,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
     wait_loads();
     __syncthreads();
     v16i sacc[BK / 32];
-    qk_tiles<D>(sm, 0, qreg, col, half, sacc);
+    qk_tiles<D, QK4>(sm, 0, qreg, col, half, sacc);
 #pragma unroll
     for (int t = 0; t < BK / 32; ++t)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int jl = 32 * t + 8 * (e >> 2) + 4 * half + (e & 3);
-        a.dbg_out[il * BK + jl] = sacc[t][e] - kAccBias;
+        a.dbg_out[il * BK + jl] = QK4 ? (int32_t)__int_as_float(sacc[t][e]) : sacc[t][e] - kAccBias;
       }
     return;
   }
@@ -213,7 +235,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
     if (kb + 1 < nblk) issue_tile<D>(a, sm, st ^ 1, bkv, bh, qb, kb + 1, w, lane);
 
     v16i sacc[BK / 32];
-    qk_tiles<D>(sm, st, qreg, col, half, sacc);
+    qk_tiles<D, QK4>(sm, st, qreg, col, half, sacc);
 
     // dequantize and add the Q-smoothing bias, in the log2 domain
     // both lane halves' delta_K through one wave-uniform (scalar) load, so that waiting for it
@@ -235,7 +257,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
         const float dsa[4] = {__int_as_float(dsv[0]), __int_as_float(dsv[1]), __int_as_float(dsv[2]), __int_as_float(dsv[3])};
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float sf = __int_as_float(sacc[t][4 * qq + r]) - kAccBiasF;   // exact S
+          const float sf = QK4 ? __int_as_float(sacc[t][4 * qq + r])                // exact S
+                               : __int_as_float(sacc[t][4 * qq + r]) - kAccBiasF;
           float x = fmaf(sf, cmul, dsa[r]);
           if (MASK) {
             const int j = kb * BK + j0 + r;
@@ -341,13 +364,13 @@ AttnArgs make_args(const Dims& D, const Ptrs& P) {
   return a;
 }
 
-template <int DD>
+template <int DD, bool QK4>
 hipError_t launch_d(const Dims& D, const AttnArgs& a, hipStream_t s) {
   const int grid = D.B * D.H * D.nqb;
   if (D.causal)
-    attn_fwd<DD, true, false><<<grid, 256, 0, s>>>(a);
+    attn_fwd<DD, true, false, QK4><<<grid, 256, 0, s>>>(a);
   else
-    attn_fwd<DD, false, false><<<grid, 256, 0, s>>>(a);
+    attn_fwd<DD, false, false, QK4><<<grid, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -355,16 +378,20 @@ hipError_t launch_d(const Dims& D, const AttnArgs& a, hipStream_t s) {
 
 hipError_t launch_attention(const Dims& D, const Ptrs& P, hipStream_t s) {
   const AttnArgs a = make_args(D, P);
-  return D.d == 128 ? launch_d<128>(D, a, s) : launch_d<64>(D, a, s);
+  if (D.qk_bits == 4) return D.d == 128 ? launch_d<128, true>(D, a, s) : launch_d<64, true>(D, a, s);
+  return D.d == 128 ? launch_d<128, false>(D, a, s) : launch_d<64, false>(D, a, s);
 }
 
 hipError_t launch_qk_tile(const Dims& D, const Ptrs& P, int b, int h, int qb, int kb, int32_t* out, hipStream_t s) {
   AttnArgs a = make_args(D, P);
   a.dbg_b = b; a.dbg_h = h; a.dbg_qb = qb; a.dbg_kb = kb; a.dbg_out = out;
-  if (D.d == 128)
-    attn_fwd<128, false, true><<<1, 256, 0, s>>>(a);
-  else
-    attn_fwd<64, false, true><<<1, 256, 0, s>>>(a);
+  if (D.qk_bits == 4) {
+    if (D.d == 128) attn_fwd<128, false, true, true><<<1, 256, 0, s>>>(a);
+    else attn_fwd<64, false, true, true><<<1, 256, 0, s>>>(a);
+  } else {
+    if (D.d == 128) attn_fwd<128, false, true, false><<<1, 256, 0, s>>>(a);
+    else attn_fwd<64, false, true, false><<<1, 256, 0, s>>>(a);
+  }
   return hipGetLastError();
 }
 

@@ -42,6 +42,12 @@ __device__ inline float wave_max(float x) {
 // ---------------------------------------------------------------------------------------
 // zero the atomically reduced statistics
 // ---------------------------------------------------------------------------------------
+// One code as stored for the attention kernel: a two's-complement int8, or for the INT4 range
+// (|code| <= 7) the OCP E4M3 byte of the same integer, which the FP8 MFMA multiplies exactly.
+__device__ inline uint8_t code_byte(float x, bool e4m3) {
+  return e4m3 ? (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(x, 0.f, 0, false) & 0xff) : (uint8_t)(int8_t)(int)x;
+}
+
 __global__ void init_stats(unsigned long long* ksum, unsigned int* vamax, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) {
@@ -174,7 +180,7 @@ __global__ __launch_bounds__(256) void kv_quant(const __half* __restrict__ k, co
     for (int e = 0; e < 8; ++e) {
       float x = rintf(g[p][e] * inv);
       x = fminf(fmaxf(x, -R), R);
-      out.c[e] = (int8_t)(int)x;
+      out.c[e] = (int8_t)code_byte(x, R < 8.f);
     }
     *reinterpret_cast<uint2*>(kcodes + (bh * Npad + row) * D + cq * 8) = out.u;
   }
@@ -273,7 +279,7 @@ __global__ __launch_bounds__(256) void q_quant(const __half* __restrict__ q, int
     for (int e = 0; e < 8; ++e) {
       float y = rintf(x[p][e] * inv);
       y = fminf(fmaxf(y, -R), R);
-      out.c[e] = (int8_t)(int)y;
+      out.c[e] = (int8_t)code_byte(y, R < 8.f);
     }
     *reinterpret_cast<uint2*>(qcodes + (bh * Npad + row) * D + cq * 8) = out.u;
     if (cq == 0) qscale[bh * Npad + row] = am / R;
@@ -389,11 +395,12 @@ __global__ __launch_bounds__(256) void delta_s(const __half* __restrict__ k, con
 // debug: internal layouts -> plain layouts
 // ---------------------------------------------------------------------------------------
 __global__ void copy_rows_i8(const int8_t* __restrict__ src, int8_t* __restrict__ dst, int heads, int N,
-                             int Npad, int d) {
+                             int Npad, int d, bool e4m3) {
   const size_t total = (size_t)heads * N * d;
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
     const size_t hd = i / ((size_t)N * d), rem = i % ((size_t)N * d);
-    dst[i] = src[hd * Npad * d + rem];
+    const int8_t c = src[hd * Npad * d + rem];
+    dst[i] = e4m3 ? (int8_t)(int)__builtin_amdgcn_cvt_f32_fp8((int)(uint8_t)c, 0) : c;
   }
 }
 __global__ void copy_rows_f32(const float* __restrict__ src, float* __restrict__ dst, size_t rows, int n,
@@ -477,8 +484,9 @@ hipError_t launch_debug_copy(const Dims& D, const Ptrs& P, hipStream_t s, float*
     hipError_t e = hipMemcpyAsync(mu_q, P.muq, (size_t)hq * D.nqb * D.d * 4, hipMemcpyDeviceToDevice, s);
     if (e != hipSuccess) return e;
   }
-  if (k_codes) copy_rows_i8<<<grid, blk, 0, s>>>(P.kcodes, k_codes, hkv, D.N, D.Npad, D.d);
-  if (q_codes) copy_rows_i8<<<grid, blk, 0, s>>>(P.qcodes, q_codes, hq, D.N, D.Npad, D.d);
+  const bool e4m3 = D.qk_bits == 4;   // INT4-range codes are stored as E4M3 bytes
+  if (k_codes) copy_rows_i8<<<grid, blk, 0, s>>>(P.kcodes, k_codes, hkv, D.N, D.Npad, D.d, e4m3);
+  if (q_codes) copy_rows_i8<<<grid, blk, 0, s>>>(P.qcodes, q_codes, hq, D.N, D.Npad, D.d, e4m3);
   if (k_scales) expand_kscale<<<grid, blk, 0, s>>>(P.kscale, k_scales, hkv, D.N, D.nkb);
   if (q_scales) copy_rows_f32<<<grid, blk, 0, s>>>(P.qscale, q_scales, (size_t)hq, D.N, D.Npad, 1.f);
   if (v_codes) unpermute_v<<<grid, blk, 0, s>>>(P.vcodes, v_codes, hkv, D.N, D.Npad, D.d);

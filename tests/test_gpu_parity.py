@@ -202,3 +202,31 @@ def test_full_size_sampled_parity(sa, name):
                                           err_msg=f"{name} tile b{b} h{h} {qb},{kb}")
     del dbg
     torch.cuda.empty_cache()
+
+
+def test_int4_extreme_codes_exact(sa):
+    """INT4-range QK^T runs on the FP8 MFMA with E4M3 codes.  Inputs of +-1 whose block and
+    sequence means are zero make every code +-7, so S reaches its largest magnitude 49 d; the
+    raw tiles must still match the exact integer products."""
+    n, d = 256, 128
+    hs = np.array([[1.0]])
+    while hs.shape[0] < 256:                                  # Sylvester Hadamard, +-1 entries
+        hs = np.block([[hs, hs], [hs, -hs]])
+    cols = list(range(1, 128)) + [129]                        # zero sum over every aligned 128 rows
+    q = np.ascontiguousarray(hs[:n, cols], dtype=np.float16).reshape(1, 1, n, d)
+    k = q.copy()                                              # key j = query j: S_jj = +49 d
+    v = np.random.default_rng(1).standard_normal((1, 1, n, d)).astype(np.float16)
+    pro = osage.prologue(q, k, v, False, 4)
+    assert np.all(np.abs(pro.q_codes) == 7) and np.all(np.abs(pro.k_codes) == 7)
+    dev = _to_dev(q, k, v)
+    dbg = {n_: t.cpu().numpy() for n_, t in sa.quant_debug(*dev, False, 4).items()}
+    np.testing.assert_array_equal(dbg["q_codes"][0, 0], pro.q_codes[0, 0])
+    np.testing.assert_array_equal(dbg["k_codes"][0, 0], pro.k_codes[0, 0])
+    top = 0
+    for qb in range(2):
+        for kb in range(2):
+            tile = sa.qk_tile_debug(*dev, 0, 0, qb, kb, False, 4).cpu().numpy()
+            ref = osage.scores_int(pro, 0, 0, slice(128 * qb, 128 * qb + 128), slice(128 * kb, 128 * kb + 128))
+            np.testing.assert_array_equal(tile, ref, err_msg=f"tile {qb},{kb}")
+            top = max(top, int(np.abs(ref).max()))
+    assert top == 49 * d

@@ -129,8 +129,9 @@ __device__ inline void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "mem
 
 // S^T tiles (32 keys each) x the wave's 32 queries, exact.  INT8 codes: v_mfma_i32_32x32x32_i8
 // from the biased accumulator (see kAccBias), 16 code bytes per lane per k-step.  INT4-range codes
-// (stored as E4M3 bytes): v_mfma_f32_32x32x64_f8f6f4 from zero, 32 bytes per lane per k-step; the
-// products and sums of integers this small are exact in its accumulator, so S arrives as fp32.
+// (stored as FP6 E2M3, 24 bytes of each 32-byte slot): v_mfma_f32_32x32x64_f8f6f4 in FP6 mode from
+// zero, one slot per lane per k-step, at twice the INT8 rate; the products and sums of integers
+// this small are exact in its accumulator, so S arrives as fp32.
 template <int D, bool QK4>
 __device__ inline void qk_tiles(const Smem<D>& sm, int st, const v4i (&qreg)[D / 32], int col, int half,
                                 v16i (&sacc)[BK / 32]) {
@@ -147,7 +148,7 @@ __device__ inline void qk_tiles(const Smem<D>& sm, int st, const v4i (&qreg)[D /
         const v8i av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         const v8i bv = {qreg[2 * s][0], qreg[2 * s][1], qreg[2 * s][2], qreg[2 * s][3],
                         qreg[2 * s + 1][0], qreg[2 * s + 1][1], qreg[2 * s + 1][2], qreg[2 * s + 1][3]};
-        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc, 0, 0, 0, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc, 2, 2, 0, 0, 0, 0);   // FP6 E2M3
       }
 #pragma unroll
       for (int e = 0; e < 16; ++e) sacc[t][e] = __float_as_int(acc[e]);

@@ -42,10 +42,39 @@ __device__ inline float wave_max(float x) {
 // ---------------------------------------------------------------------------------------
 // zero the atomically reduced statistics
 // ---------------------------------------------------------------------------------------
-// One code as stored for the attention kernel: a two's-complement int8, or for the INT4 range
-// (|code| <= 7) the OCP E4M3 byte of the same integer, which the FP8 MFMA multiplies exactly.
-__device__ inline uint8_t code_byte(float x, bool e4m3) {
-  return e4m3 ? (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(x, 0.f, 0, false) & 0xff) : (uint8_t)(int8_t)(int)x;
+// INT4-range codes (|code| <= 7) go to the attention kernel as OCP FP6 E2M3 numbers, which hold
+// the integers -7..7 exactly and feed the FP6 MFMA at twice the FP8/INT8 rate.  Each 32-channel
+// group of a row occupies a 32-byte slot: 24 bytes of packed 6-bit codes (channel i of the group
+// at bits 6i..6i+5) and 8 zero bytes, so rows keep d bytes and the FP8/INT8 tile geometry.
+__device__ inline uint32_t e2m3_bits(float x) {        // x integer in [-7, 7]
+  const int a = (int)fabsf(x);
+  const uint32_t mag = a == 0 ? 0u : a == 1 ? 8u : a < 4 ? 16u + 4u * (a - 2) : 24u + 2u * (a - 4);
+  return mag | (x < 0.f ? 0x20u : 0u);
+}
+
+// Store the 8 codes of channels 8 cq .. 8 cq + 7 of one row (row points at its d code bytes).
+// FP6: the four threads of a 32-channel slot are consecutive lanes (cq & 3 = 0..3); they swap
+// their 48-bit packs so that each writes one aligned 8-byte word of the slot.
+__device__ inline void store_codes(int8_t* row, int cq, const float (&x)[8], bool fp6) {
+  if (!fp6) {
+    union { int8_t c[8]; uint2 u; } out;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) out.c[e] = (int8_t)(int)x[e];
+    *reinterpret_cast<uint2*>(row + cq * 8) = out.u;
+    return;
+  }
+  unsigned long long mine = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) mine |= (unsigned long long)e2m3_bits(x[e]) << (6 * e);
+  const int j = cq & 3;
+  // slot bits [48 t, 48 t + 48) hold thread t's pack; word j covers bits [64 j, 64 j + 64)
+  const unsigned long long nxt = __shfl_down(mine, 1, 4);   // pack of thread j + 1 (same slot)
+  unsigned long long word;
+  if (j == 0) word = mine | (nxt << 48);
+  else if (j == 1) word = (mine >> 16) | (nxt << 32);
+  else if (j == 2) word = (mine >> 32) | (nxt << 16);
+  else word = 0;                                            // bytes 24..31: padding
+  *reinterpret_cast<uint2*>(row + 32 * (cq >> 2) + 8 * j) = make_uint2((uint32_t)word, (uint32_t)(word >> 32));
 }
 
 __global__ void init_stats(unsigned long long* ksum, unsigned int* vamax, int n) {
@@ -175,14 +204,10 @@ __global__ __launch_bounds__(256) void kv_quant(const __half* __restrict__ k, co
 #pragma unroll
   for (int p = 0; p < PASSES; ++p) {
     const int row = kb * BK + p * RPP + r0;   // < Npad: rows past N get zero codes
-    union { int8_t c[8]; uint2 u; } out;
+    float x[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float x = rintf(g[p][e] * inv);
-      x = fminf(fmaxf(x, -R), R);
-      out.c[e] = (int8_t)code_byte(x, R < 8.f);
-    }
-    *reinterpret_cast<uint2*>(kcodes + (bh * Npad + row) * D + cq * 8) = out.u;
+    for (int e = 0; e < 8; ++e) x[e] = fminf(fmaxf(rintf(g[p][e] * inv), -R), R);
+    store_codes(kcodes + (bh * Npad + row) * D, cq, x, R < 8.f);
   }
 
   // V: per-channel FP8, transposed into [group u][channel][slot] in LDS, then streamed out
@@ -274,14 +299,10 @@ __global__ __launch_bounds__(256) void q_quant(const __half* __restrict__ q, int
 #pragma unroll
     for (int m = TPR / 2; m >= 1; m >>= 1) am = fmaxf(am, __shfl_xor(am, m, 64));
     const float inv = am > 0.f ? R / am : 0.f;
-    union { int8_t c[8]; uint2 u; } out;
+    float y[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float y = rintf(x[p][e] * inv);
-      y = fminf(fmaxf(y, -R), R);
-      out.c[e] = (int8_t)code_byte(y, R < 8.f);
-    }
-    *reinterpret_cast<uint2*>(qcodes + (bh * Npad + row) * D + cq * 8) = out.u;
+    for (int e = 0; e < 8; ++e) y[e] = fminf(fmaxf(rintf(x[p][e] * inv), -R), R);
+    store_codes(qcodes + (bh * Npad + row) * D, cq, y, R < 8.f);
     if (cq == 0) qscale[bh * Npad + row] = am / R;
   }
 }
@@ -395,12 +416,23 @@ __global__ __launch_bounds__(256) void delta_s(const __half* __restrict__ k, con
 // debug: internal layouts -> plain layouts
 // ---------------------------------------------------------------------------------------
 __global__ void copy_rows_i8(const int8_t* __restrict__ src, int8_t* __restrict__ dst, int heads, int N,
-                             int Npad, int d, bool e4m3) {
+                             int Npad, int d, bool fp6) {
   const size_t total = (size_t)heads * N * d;
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
     const size_t hd = i / ((size_t)N * d), rem = i % ((size_t)N * d);
-    const int8_t c = src[hd * Npad * d + rem];
-    dst[i] = e4m3 ? (int8_t)(int)__builtin_amdgcn_cvt_f32_fp8((int)(uint8_t)c, 0) : c;
+    const size_t r = rem / d;
+    const int c = (int)(rem % d);
+    const uint8_t* row = reinterpret_cast<const uint8_t*>(src) + (hd * Npad + r) * d;
+    if (!fp6) {
+      dst[i] = (int8_t)row[c];
+    } else {                                   // unpack one E2M3 code and decode it
+      const int bit = 6 * (c & 31);
+      const uint8_t* slot = row + 32 * (c >> 5);
+      const uint32_t b = ((uint32_t)slot[bit >> 3] | ((uint32_t)slot[(bit >> 3) + 1] << 8)) >> (bit & 7) & 63u;
+      const int e = (b >> 3) & 3, m = b & 7;
+      const int mag = e == 0 ? 0 : ((8 + m) << (e - 1)) >> 3;   // (1 + m/8) 2^(e-1), an integer here
+      dst[i] = (int8_t)((b & 0x20) ? -mag : mag);
+    }
   }
 }
 __global__ void copy_rows_f32(const float* __restrict__ src, float* __restrict__ dst, size_t rows, int n,
@@ -484,9 +516,9 @@ hipError_t launch_debug_copy(const Dims& D, const Ptrs& P, hipStream_t s, float*
     hipError_t e = hipMemcpyAsync(mu_q, P.muq, (size_t)hq * D.nqb * D.d * 4, hipMemcpyDeviceToDevice, s);
     if (e != hipSuccess) return e;
   }
-  const bool e4m3 = D.qk_bits == 4;   // INT4-range codes are stored as E4M3 bytes
-  if (k_codes) copy_rows_i8<<<grid, blk, 0, s>>>(P.kcodes, k_codes, hkv, D.N, D.Npad, D.d, e4m3);
-  if (q_codes) copy_rows_i8<<<grid, blk, 0, s>>>(P.qcodes, q_codes, hq, D.N, D.Npad, D.d, e4m3);
+  const bool fp6 = D.qk_bits == 4;    // INT4-range codes are stored as packed FP6 E2M3
+  if (k_codes) copy_rows_i8<<<grid, blk, 0, s>>>(P.kcodes, k_codes, hkv, D.N, D.Npad, D.d, fp6);
+  if (q_codes) copy_rows_i8<<<grid, blk, 0, s>>>(P.qcodes, q_codes, hq, D.N, D.Npad, D.d, fp6);
   if (k_scales) expand_kscale<<<grid, blk, 0, s>>>(P.kscale, k_scales, hkv, D.N, D.nkb);
   if (q_scales) copy_rows_f32<<<grid, blk, 0, s>>>(P.qscale, q_scales, (size_t)hq, D.N, D.Npad, 1.f);
   if (v_codes) unpermute_v<<<grid, blk, 0, s>>>(P.vcodes, v_codes, hkv, D.N, D.Npad, D.d);

@@ -28,12 +28,12 @@ struct Dims {
 
 // ---- workspace carve-up (byte offsets, all WS_ALIGN aligned) ----
 //  kcodes : int8  [B][Hkv][Npad][d]           smoothed+quantized K, zero past N (INT4 range:
-//                                             the E4M3 bytes of the same integers)
+//                                             packed FP6 E2M3, 24 of every 32 bytes)
 //  vcodes : uint8 [B][Hkv][Npad/64][d][64]    FP8 V, transposed per 64-key group; inside a
 //           group the byte at position 32*h + b of channel row c holds key
 //           32*(b/16) + 8*((b%16)/4) + 4*h + (b%4): the k-slot order of the FP8 MFMA
 //           B operand built from the S^T accumulators (see attention kernel)
-//  qcodes : int8  [B][H][Npad][d]              (INT4 range: E4M3 bytes, as kcodes)
+//  qcodes : int8  [B][H][Npad][d]              (INT4 range: packed FP6 E2M3, as kcodes)
 //  kscale : fp32  [B][Hkv][nkb][2]            delta_K per (KV block, lane half)
 //  qscale : fp32  [B][H][Npad]                delta_Q per query row
 //  muk    : fp32  [B][Hkv][d]

@@ -243,7 +243,7 @@ __global__ __launch_bounds__(256) void kv_quant(const __half* __restrict__ k, co
 template <int D>
 __global__ __launch_bounds__(256) void q_quant(const __half* __restrict__ q, int8_t* __restrict__ qcodes,
                                                float* __restrict__ qscale, float* __restrict__ muq,
-                                               int N, int Npad, int nqb, float R) {
+                                               uint16_t* __restrict__ muqs, int N, int Npad, int nqb, float R) {
   constexpr int TPR = D / 8, RPP = 256 / TPR, PASSES = BQ / RPP;
   __shared__ long long ls[RPP][D];
   __shared__ float lmu[D];
@@ -281,6 +281,15 @@ __global__ __launch_bounds__(256) void q_quant(const __half* __restrict__ q, int
     const float m = (float)((double)t / ((double)nvalid * 16777216.0));
     lmu[c] = m;
     muq[(bh * nqb + qb) * D + c] = m;
+    // exact three-part bf16 split of the mean, the A operand of the Delta_S GEMM
+    const __bf16 b1 = (__bf16)m;
+    const float r1 = m - (float)b1;
+    const __bf16 b2 = (__bf16)r1;
+    const __bf16 b3 = (__bf16)(r1 - (float)b2);
+    uint16_t* dst = muqs + ((bh * nqb + qb) * 3) * D + c;
+    dst[0] = __builtin_bit_cast(uint16_t, b1);
+    dst[D] = __builtin_bit_cast(uint16_t, b2);
+    dst[2 * D] = __builtin_bit_cast(uint16_t, b3);
   }
   __syncthreads();
   float mu[8];
@@ -310,17 +319,31 @@ __global__ __launch_bounds__(256) void q_quant(const __half* __restrict__ q, int
 // ---------------------------------------------------------------------------------------
 // Delta_S[qb, j] = sum_c mu_Q[qb, c] * gamma_K[j, c], stored times log2(e)/sqrt(d).
 //
-// A GEMM (Q blocks x keys x channels) on the bf16 MFMA at fp32-class accuracy: every fp32
-// factor is split exactly into three bf16 parts, x = x1 + x2 + x3 (8 significant bits each,
+// A GEMM (Q blocks x keys x channels) on the bf16 MFMA at fp32-class accuracy: both fp32
+// factors are split exactly into three bf16 parts, x = x1 + x2 + x3 (8 significant bits each,
 // 24 in all), and the six cross products whose weight is at least 2^-16 of the leading one
 // are accumulated, smallest first (x3y1 + x2y2 + x1y3 + x2y1 + x1y2 + x1y1); the dropped
 // terms are below 2^-24 of it.  The bf16 MFMA accumulates in fp32 (unlike the FP8 one).
-// gamma_K = RN32(K - mu_K) is recomputed from the fp16 keys; keys past N contribute zero.
-// grid (Npad/256 key tiles, ceil(nqb/32) Q-block tiles, B*H), 256 threads; each wave owns
-// 32 Q blocks x 64 keys (two 32x32 MFMA tiles).  Causal rows stop at key (qb + 1) * 128.
+//
+// One workgroup per (KV head, 128-key block): it reads the block's fp16 keys once, forms
+// gamma_K = RN32(K - mu_K), splits it and keeps the three parts in LDS in the MFMA operand
+// layout, then sweeps the Q blocks of every query head that shares the KV head (the mu_Q parts
+// come split from the Q prologue).  Causal: only Q blocks qb >= kb see these keys.
+// 256 threads: wave w owns keys 64 (w & 1) .. +63 of the block (two 32x32 accumulators) and
+// every other 32-Q-block tile (parity w >> 1); the next tile's mu_Q parts are loaded while the
+// current tile is stored.
 // ---------------------------------------------------------------------------------------
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+
+template <int D>
+struct DsSmem {
+  __attribute__((aligned(16))) uint16_t g[3][D / 16][BK][16];   // [part][k-step][key][16 ch], swizzled halves
+};
+
+// 16-byte half (8 channels) of a key's k-step row, XOR-swizzled by key bit 3 against bank conflicts
+__device__ inline int ds_half(int key, int hl) { return hl ^ ((key >> 3) & 1); }
 
 struct Split3 {
   bf16x8 p[3];
@@ -341,9 +364,12 @@ __device__ inline Split3 split3(const float (&x)[8]) {
   return s;
 }
 
+// Q-tile form, for few Q blocks per key: grid (Npad/256 key tiles, ceil(nqb/32) Q-block tiles,
+// B*H), 256 threads; each wave owns 32 Q blocks x 64 keys (two 32x32 MFMA tiles) and splits
+// its keys' gamma_K itself.  Causal rows stop at key (qb + 1) * 128.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void delta_s(const __half* __restrict__ k, const float* __restrict__ muk,
-                                               const float* __restrict__ muq, float* __restrict__ ds,
+__global__ __launch_bounds__(256) void delta_s_qtile(const __half* __restrict__ k, const float* __restrict__ muk,
+                                               const uint16_t* __restrict__ muqs, float* __restrict__ ds,
                                                int H, int Hkv, int N, int Npad, int nqb, float k2) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, r = lane & 31, hl = lane >> 5;
   const int bh = blockIdx.z, b = bh / H, h = bh % H, hk = h / (H / Hkv);
@@ -359,18 +385,15 @@ __global__ __launch_bounds__(256) void delta_s(const __half* __restrict__ k, con
 #pragma unroll 2
   for (int ks = 0; ks < D / 16; ++ks) {
     const int c0 = 16 * ks + 8 * hl;
-    float xa[8];
+    Split3 A;                                          // mu_Q parts, split by the Q prologue
     {
-      float4 m0 = make_float4(0.f, 0.f, 0.f, 0.f), m1 = m0;
-      if (qvalid) {
-        const float* src = muq + ((size_t)bh * nqb + qb) * D + c0;
-        m0 = *reinterpret_cast<const float4*>(src);
-        m1 = *reinterpret_cast<const float4*>(src + 4);
+      const uint16_t* ap = muqs + ((size_t)bh * nqb + min(qb, nqb - 1)) * 3 * D + c0;
+#pragma unroll
+      for (int p = 0; p < 3; ++p) {
+        const s16x8 av = qvalid ? *reinterpret_cast<const s16x8*>(ap + p * D) : (s16x8){};
+        A.p[p] = __builtin_bit_cast(bf16x8, av);
       }
-      xa[0] = m0.x; xa[1] = m0.y; xa[2] = m0.z; xa[3] = m0.w;
-      xa[4] = m1.x; xa[5] = m1.y; xa[6] = m1.z; xa[7] = m1.w;
     }
-    const Split3 A = split3(xa);
     const float4 mk0 = *reinterpret_cast<const float4*>(muk + bkv * D + c0);
     const float4 mk1 = *reinterpret_cast<const float4*>(muk + bkv * D + c0 + 4);
     const float mkv[8] = {mk0.x, mk0.y, mk0.z, mk0.w, mk1.x, mk1.y, mk1.z, mk1.w};
@@ -409,6 +432,133 @@ __global__ __launch_bounds__(256) void delta_s(const __half* __restrict__ k, con
         const int q = q0 + 8 * a4 + 4 * hl + e;
         if (q < nqb && j < ds_row_len(CAUSAL, q, Npad)) dsh[ds_row_offset(CAUSAL, q, Npad) + j] = acc[t][4 * a4 + e] * k2;
       }
+  }
+}
+
+// K-block form, for many Q blocks per key (grouped query heads, long sequences): see above.
+template <int D>
+struct AParts {                                  // one lane's mu_Q parts for a 32-Q-block tile
+  bf16x8 a[D / 16][3];
+};
+
+template <int D>
+__device__ inline void load_aparts(AParts<D>& A, const uint16_t* __restrict__ muqs, size_t bh, int nqb, int qa,
+                                   int hl) {
+  const uint16_t* ap = muqs + ((bh * nqb + min(qa, nqb - 1)) * 3) * D;
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+    for (int p = 0; p < 3; ++p) {
+      const s16x8 av = qa < nqb ? *reinterpret_cast<const s16x8*>(ap + p * D + 16 * ks + 8 * hl) : (s16x8){};
+      A.a[ks][p] = __builtin_bit_cast(bf16x8, av);
+    }
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void delta_s_kblock(const __half* __restrict__ k, const float* __restrict__ muk,
+                                               const uint16_t* __restrict__ muqs, float* __restrict__ ds,
+                                               int H, int Hkv, int N, int Npad, int nqb, float k2) {
+  __shared__ DsSmem<D> sm;
+  constexpr int KS = D / 16;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 31, hl = lane >> 5;
+  const int kb = blockIdx.x;
+  const int bkv = blockIdx.y, b = bkv / Hkv, hk = bkv % Hkv, G = H / Hkv;
+  const __half* kbase = k + (size_t)bkv * N * D;
+
+  // gamma_K parts of the block's 128 keys -> LDS
+  constexpr int CH = D / 8;                                   // 8-channel chunks per key
+#pragma unroll
+  for (int it = 0; it < BK * CH / 256; ++it) {
+    const int idx = it * 256 + tid, key = idx / CH, c8 = idx % CH;
+    const int j = kb * BK + key;
+    float x[8];
+    if (j < N) {
+      const Half8 kk = load8(kbase + (size_t)j * D + c8 * 8);
+      const float4 m0 = *reinterpret_cast<const float4*>(muk + (size_t)bkv * D + c8 * 8);
+      const float4 m1 = *reinterpret_cast<const float4*>(muk + (size_t)bkv * D + c8 * 8 + 4);
+      const float mm[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = __half2float(kk.h[e]) - mm[e];   // gamma_K, RN32
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = 0.f;
+    }
+    union { __bf16 b[8]; uint4 u; } p0, p1, p2;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const __bf16 b1 = (__bf16)x[e];
+      const float r1 = x[e] - (float)b1;       // exact: b1 is x rounded to 8 significant bits
+      const __bf16 b2 = (__bf16)r1;
+      p0.b[e] = b1;
+      p1.b[e] = b2;
+      p2.b[e] = (__bf16)(r1 - (float)b2);      // at most 8 significant bits remain: exact
+    }
+    const int ks = c8 >> 1, h = ds_half(key, c8 & 1);
+    *reinterpret_cast<uint4*>(&sm.g[0][ks][key][8 * h]) = p0.u;
+    *reinterpret_cast<uint4*>(&sm.g[1][ks][key][8 * h]) = p1.u;
+    *reinterpret_cast<uint4*>(&sm.g[2][ks][key][8 * h]) = p2.u;
+  }
+  __syncthreads();
+
+  // wave w: keys 64 (w & 1) .. +63 (two 32-key accumulators), Q tiles of parity w >> 1
+  const int qlo = CAUSAL ? kb & ~31 : 0;                     // first 32-aligned Q tile that sees the keys
+  const int ntile = (nqb - qlo + 31) / 32;
+  const int my0 = w >> 1;                                    // this wave's tiles: my0, my0 + 2, ...
+  const int total = G * ((ntile - my0 + 1) / 2);             // (q head, tile) pairs of this wave
+  auto pair = [&](int n, int& hq, int& q0) {
+    const int per = (ntile - my0 + 1) / 2;
+    hq = n / per;
+    q0 = qlo + 32 * (my0 + 2 * (n % per));
+  };
+  AParts<D> A;
+  if (total > 0) {
+    int hq, q0;
+    pair(0, hq, q0);
+    load_aparts<D>(A, muqs, (size_t)b * H + hk * G + hq, nqb, q0 + r, hl);
+  }
+  for (int n = 0; n < total; ++n) {
+    int hq, q0;
+    pair(n, hq, q0);
+    const size_t bh = (size_t)b * H + hk * G + hq;
+    f32x16 acc[2] = {};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int key = 64 * (w & 1) + 32 * t + r;
+        bf16x8 Bv[3];
+#pragma unroll
+        for (int p = 0; p < 3; ++p)
+          Bv[p] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const s16x8*>(&sm.g[p][ks][key][8 * ds_half(key, hl)]));
+        f32x16 c = acc[t];
+        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A.a[ks][2], Bv[0], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A.a[ks][1], Bv[1], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A.a[ks][0], Bv[2], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A.a[ks][1], Bv[0], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A.a[ks][0], Bv[1], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A.a[ks][0], Bv[0], c, 0, 0, 0);
+        acc[t] = c;
+      }
+    }
+    // next pair's mu_Q parts load while this pair's results are stored
+    if (n + 1 < total) {
+      int hq2, q02;
+      pair(n + 1, hq2, q02);
+      load_aparts<D>(A, muqs, (size_t)b * H + hk * G + hq2, nqb, q02 + r, hl);
+    }
+    float* dsh = ds + bh * ds_head_elems(CAUSAL, nqb, Npad);
+    // lane holds Q blocks q0 + 8a + 4hl + e (e < 4) of key column j
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int j = kb * BK + 64 * (w & 1) + 32 * t + r;
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int qb = q0 + 8 * a4 + 4 * hl + e;
+          if (qb < nqb && (!CAUSAL || qb >= kb)) dsh[ds_row_offset(CAUSAL, qb, Npad) + j] = acc[t][4 * a4 + e] * k2;
+        }
+    }
   }
 }
 
@@ -483,13 +633,23 @@ hipError_t launch_prologue_d(const Dims& Dm, const Ptrs& P, hipStream_t s) {
   kv_stats<D><<<dim3((Dm.N + 255) / 256, Dm.B * Dm.Hkv), 256, 0, s>>>(P.k, P.v, P.ksum, P.vamax, Dm.N);
   kv_quant<D><<<dim3(Dm.nkb, Dm.B * Dm.Hkv), 256, 0, s>>>(P.k, P.v, P.ksum, P.vamax, P.kcodes, P.vcodes,
                                                           P.kscale, P.muk, P.vscale, Dm.N, Dm.Npad, Dm.nkb, R);
-  q_quant<D><<<dim3(Dm.nqb, Dm.B * Dm.H), 256, 0, s>>>(P.q, P.qcodes, P.qscale, P.muq, Dm.N, Dm.Npad, Dm.nqb, R);
+  q_quant<D><<<dim3(Dm.nqb, Dm.B * Dm.H), 256, 0, s>>>(P.q, P.qcodes, P.qscale, P.muq, P.muqs, Dm.N, Dm.Npad,
+                                                         Dm.nqb, R);
   const float k2 = (float)(1.4426950408889634 / sqrt((double)D));
-  const dim3 gds((Dm.Npad + 255) / 256, (Dm.nqb + 31) / 32, Dm.B * Dm.H);
-  if (Dm.causal)
-    delta_s<D, true><<<gds, 256, 0, s>>>(P.k, P.muk, P.muq, P.ds, Dm.H, Dm.Hkv, Dm.N, Dm.Npad, Dm.nqb, k2);
-  else
-    delta_s<D, false><<<gds, 256, 0, s>>>(P.k, P.muk, P.muq, P.ds, Dm.H, Dm.Hkv, Dm.N, Dm.Npad, Dm.nqb, k2);
+  // the K-block form pays off when each key block serves many Q blocks
+  if ((size_t)(Dm.H / Dm.Hkv) * Dm.nqb >= 1024) {
+    const dim3 g(Dm.nkb, Dm.B * Dm.Hkv);
+    if (Dm.causal)
+      delta_s_kblock<D, true><<<g, 256, 0, s>>>(P.k, P.muk, P.muqs, P.ds, Dm.H, Dm.Hkv, Dm.N, Dm.Npad, Dm.nqb, k2);
+    else
+      delta_s_kblock<D, false><<<g, 256, 0, s>>>(P.k, P.muk, P.muqs, P.ds, Dm.H, Dm.Hkv, Dm.N, Dm.Npad, Dm.nqb, k2);
+  } else {
+    const dim3 g((Dm.Npad + 255) / 256, (Dm.nqb + 31) / 32, Dm.B * Dm.H);
+    if (Dm.causal)
+      delta_s_qtile<D, true><<<g, 256, 0, s>>>(P.k, P.muk, P.muqs, P.ds, Dm.H, Dm.Hkv, Dm.N, Dm.Npad, Dm.nqb, k2);
+    else
+      delta_s_qtile<D, false><<<g, 256, 0, s>>>(P.k, P.muk, P.muqs, P.ds, Dm.H, Dm.Hkv, Dm.N, Dm.Npad, Dm.nqb, k2);
+  }
   return hipGetLastError();
 }
 

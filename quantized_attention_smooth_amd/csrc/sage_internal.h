@@ -41,6 +41,8 @@ struct Dims {
 //  vamax  : u32   [B][Hkv][d]                 bits of max|V| per channel (non-negative floats)
 //  vscale : fp32  [B][Hkv][d]                 delta_V
 //  muq    : fp32  [B][H][nqb][d]
+//  muqs   : bf16  [B][H][nqb][3][d]           mu_Q split exactly into three bf16 parts
+//                                             (x = x1 + x2 + x3), the Delta_S MFMA operand
 //  ds     : fp32  per (b, h): the rows of Delta_S * log2(e) / sqrt(d), one per Q block.
 //           Non-causal: nqb rows of Npad keys.  Causal: row qb holds only the keys a causal
 //           Q block can see, j < (qb + 1) * 128, packed back to back (ds_row_offset).
@@ -57,7 +59,7 @@ __host__ __device__ inline int ds_row_len(bool causal, int qb, int Npad) {
 }
 
 struct Layout {
-  size_t kcodes, vcodes, qcodes, kscale, qscale, muk, ksum, vamax, vscale, muq, ds, total;
+  size_t kcodes, vcodes, qcodes, kscale, qscale, muk, ksum, vamax, vscale, muq, muqs, ds, total;
 };
 
 inline size_t align_up(size_t x) { return (x + WS_ALIGN - 1) / WS_ALIGN * WS_ALIGN; }
@@ -77,6 +79,7 @@ inline Layout make_layout(const Dims& D) {
   L.vamax = take(B * Hkv * d * 4);
   L.vscale = take(B * Hkv * d * 4);
   L.muq = take(B * H * (size_t)D.nqb * d * 4);
+  L.muqs = take(B * H * (size_t)D.nqb * 3 * d * 2);
   L.ds = take(B * H * ds_head_elems(D.causal != 0, D.nqb, D.Npad) * 4);
   L.total = off;
   return L;
@@ -97,6 +100,7 @@ struct Ptrs {
   unsigned int* vamax;
   float* vscale;
   float* muq;
+  uint16_t* muqs;
   float* ds;
 };
 
@@ -117,6 +121,7 @@ inline Ptrs carve(void* ws, const Layout& L, const void* q, const void* k, const
   p.vamax = reinterpret_cast<unsigned int*>(w + L.vamax);
   p.vscale = reinterpret_cast<float*>(w + L.vscale);
   p.muq = reinterpret_cast<float*>(w + L.muq);
+  p.muqs = reinterpret_cast<uint16_t*>(w + L.muqs);
   p.ds = reinterpret_cast<float*>(w + L.ds);
   return p;
 }

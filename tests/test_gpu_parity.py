@@ -230,3 +230,20 @@ def test_int4_extreme_codes_exact(sa):
             np.testing.assert_array_equal(tile, ref, err_msg=f"tile {qb},{kb}")
             top = max(top, int(np.abs(ref).max()))
     assert top == 49 * d
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_many_q_blocks_per_key_block(sa, causal):
+    """64 query heads on one KV head: each key block serves 64 x 16 Q blocks, so Delta_S takes the
+    key-block form of its GEMM.  Sampled heads: full prologue tensors and every output block."""
+    w = custom(1, 64, 1, 2048, 64, causal, 8, q_bias_std=1.0)
+    _say(f"[case many-q-blocks causal={causal}] B{w.B} H{w.H} Hkv{w.Hkv} N{w.N} d{w.d}")
+    q, k, v = make_inputs(w, seed=11)
+    qd, kd, vd = _to_dev(q, k, v)
+    o = sa.sageattn(qd, kd, vd, is_causal=causal, qk_bits=8).cpu().numpy()
+    dbg = {n: t.cpu().numpy() for n, t in sa.quant_debug(qd, kd, vd, causal, 8).items()}
+    for h in (0, 17, 63):
+        ph = osage.prologue(*_head_slice(q, k, v, 0, h, w.H, w.Hkv), causal, 8)
+        _check_prologue(dbg, ph, 0, h, 0, f"many-q-blocks h{h}")
+        ref = np.concatenate([osage.attend_block(ph, 0, 0, qb) for qb in range(ph.nqb)])
+        _check_o(o[0, h], ref, f"many-q-blocks h{h}")

@@ -9,9 +9,10 @@
 // All kernels are HBM-streaming codec work: each reads its fp16 input once (K and V twice:
 // statistics, then quantization) and writes 1-byte codes plus a few scales.
 //
-// Bit-exactness: the channel means are exact fixed-point sums (every fp16 value is an integer
-// multiple of 2^-24, |x * 2^24| < 2^40), reduced with 64-bit integer adds in any order, then
-// one fp64 division and one rounding to fp32.  Smoothing is one fp32 subtraction; codes are
+// Bit-exactness: the channel means are exact sums.  Every fp16 value is an integer multiple of
+// 2^-24 below 2^16, so a sum of up to 256 of them is exact in fp64 (below 2^24, 48 bits of
+// 2^-24 units); whole-sequence K sums cross workgroups as int64 counts of 2^-24 units.  Each
+// mean is one fp64 division rounded to fp32.  Smoothing is one fp32 subtraction; codes are
 // round-half-even of one fp32 product with the correctly rounded fp32 reciprocal R / amax;
 // scales are the correctly rounded fp32 quotient amax / R.  None of these depend on the
 // order of the parallel reduction, so codes and scales are reproducible bit for bit.
@@ -20,8 +21,6 @@
 namespace sage {
 
 namespace {
-
-constexpr float kFix = 16777216.0f;   // 2^24
 
 struct Half8 {
   __half h[8];
@@ -39,9 +38,6 @@ __device__ inline float wave_max(float x) {
   return x;
 }
 
-// ---------------------------------------------------------------------------------------
-// zero the atomically reduced statistics
-// ---------------------------------------------------------------------------------------
 // INT4-range codes (|code| <= 7) go to the attention kernel as OCP FP6 E2M3 numbers, which hold
 // the integers -7..7 exactly and feed the FP6 MFMA at twice the FP8/INT8 rate.  Each 32-channel
 // group of a row occupies a 32-byte slot: 24 bytes of packed 6-bit codes (channel i of the group
@@ -77,6 +73,9 @@ __device__ inline void store_codes(int8_t* row, int cq, const float (&x)[8], boo
   *reinterpret_cast<uint2*>(row + 32 * (cq >> 2) + 8 * j) = make_uint2((uint32_t)word, (uint32_t)(word >> 32));
 }
 
+// ---------------------------------------------------------------------------------------
+// zero the atomically reduced statistics
+// ---------------------------------------------------------------------------------------
 __global__ void init_stats(unsigned long long* ksum, unsigned int* vamax, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) {
@@ -86,7 +85,8 @@ __global__ void init_stats(unsigned long long* ksum, unsigned int* vamax, int n)
 }
 
 // ---------------------------------------------------------------------------------------
-// K channel sums (exact, int64 fixed point) and V channel abs-max, per (b, kv head).
+// K channel sums (exact: fp64 within a workgroup, int64 fixed point across) and V channel
+// abs-max, per (b, kv head).
 // grid (ceil(N / 256), B*Hkv), 256 threads; thread = (row slot, 8-channel chunk).
 // ---------------------------------------------------------------------------------------
 template <int D>
@@ -96,17 +96,21 @@ __global__ __launch_bounds__(256) void kv_stats(const __half* __restrict__ k, co
   constexpr int TPR = D / 8;      // threads per row
   constexpr int RPP = 256 / TPR;  // rows per pass
   constexpr int TOK = 256;        // tokens per workgroup
-  __shared__ long long ls[RPP][D];
+  __shared__ double ls[RPP][D];
   __shared__ float lm[RPP][D];
   const int tid = threadIdx.x, cq = tid % TPR, r0 = tid / TPR;
   const size_t bh = blockIdx.y;
   const __half* kb = k + bh * (size_t)N * D;
   const __half* vb = v + bh * (size_t)N * D;
-  long long s[8];
+  // Sums of at most TOK fp16 values are exact in fp64: every term is a multiple of 2^-24 and the
+  // total stays below 2^24 < 2^(53 - 24).  The workgroup's exact total is then handed to the
+  // cross-workgroup reduction as an int64 count of 2^-24 units.
+  double s[8];
   float mx[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) { s[e] = 0; mx[e] = 0.f; }
+  for (int e = 0; e < 8; ++e) { s[e] = 0.0; mx[e] = 0.f; }
   const int tok0 = blockIdx.x * TOK;
+#pragma unroll 4
   for (int p = 0; p < TOK / RPP; ++p) {
     const int row = tok0 + p * RPP + r0;
     if (row < N) {
@@ -114,7 +118,7 @@ __global__ __launch_bounds__(256) void kv_stats(const __half* __restrict__ k, co
       const Half8 vv = load8(vb + (size_t)row * D + cq * 8);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        s[e] += (long long)(__half2float(kk.h[e]) * kFix);   // exact: 11 significant bits
+        s[e] += (double)__half2float(kk.h[e]);
         mx[e] = fmaxf(mx[e], fabsf(__half2float(vv.h[e])));
       }
     }
@@ -123,10 +127,10 @@ __global__ __launch_bounds__(256) void kv_stats(const __half* __restrict__ k, co
   for (int e = 0; e < 8; ++e) { ls[r0][cq * 8 + e] = s[e]; lm[r0][cq * 8 + e] = mx[e]; }
   __syncthreads();
   for (int c = tid; c < D; c += 256) {
-    long long t = 0;
+    double t = 0.0;
     float m = 0.f;
     for (int r = 0; r < RPP; ++r) { t += ls[r][c]; m = fmaxf(m, lm[r][c]); }
-    atomicAdd(&ksum[bh * D + c], (unsigned long long)t);          // two's complement: exact
+    atomicAdd(&ksum[bh * D + c], (unsigned long long)(long long)(t * 16777216.0));   // exact integer
     atomicMax(&vamax[bh * D + c], __float_as_uint(m));            // order of non-negative floats
   }
 }
@@ -210,30 +214,46 @@ __global__ __launch_bounds__(256) void kv_quant(const __half* __restrict__ k, co
     store_codes(kcodes + (bh * Npad + row) * D, cq, x, R < 8.f);
   }
 
-  // V: per-channel FP8, transposed into [group u][channel][slot] in LDS, then streamed out
+  // V: per-channel FP8, transposed into [group u][channel][slot] in LDS, then streamed out.
+  // A thread takes 4 consecutive keys: their codes fill 4 consecutive slots, one 32-bit LDS
+  // write per channel.  The 16-byte chunk of a channel row is XOR-swizzled by channel bits 3-4
+  // against bank conflicts (lanes of a wave differ in channel by multiples of 8) and unswizzled
+  // on the way out.
+  constexpr int G4 = BK / 4 / RPP;             // passes of 4-key groups
 #pragma unroll
-  for (int p = 0; p < PASSES; ++p) {
-    const int jl = p * RPP + r0;               // key within the block
-    const int row = kb * BK + jl;
-    const int u = jl >> 6, jj = jl & 63;
-    const int pos = 32 * ((jj >> 2) & 1) + 16 * (jj >> 5) + 4 * ((jj >> 3) & 3) + (jj & 3);
-    if (row < N) {
-      const Half8 vv = load8(vbase + (size_t)row * D + cq * 8);
+  for (int p = 0; p < G4; ++p) {
+    const int jl0 = 4 * (p * RPP + r0);        // first of the thread's 4 keys within the block
+    const int u = jl0 >> 6, jj = jl0 & 63;
+    const int base = 32 * ((jj >> 2) & 1) + 16 * (jj >> 5) + 4 * ((jj >> 3) & 3);   // slot of key jj
+    float x[4][8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float x = __half2float(vv.h[e]) * vinv[e];
-        x = fminf(fmaxf(x, -V_RANGE), V_RANGE);
-        vt[(u * D + cq * 8 + e) * VGROUP + pos] = (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(x, 0.f, 0, false) & 0xff);
+    for (int i = 0; i < 4; ++i) {
+      const int row = kb * BK + jl0 + i;
+      if (row < N) {
+        const Half8 vv = load8(vbase + (size_t)row * D + cq * 8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[i][e] = fminf(fmaxf(__half2float(vv.h[e]) * vinv[e], -V_RANGE), V_RANGE);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[i][e] = 0.f;
       }
-    } else {
+    }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) vt[(u * D + cq * 8 + e) * VGROUP + pos] = 0;
+    for (int e = 0; e < 8; ++e) {
+      const int c = cq * 8 + e;
+      int word = __builtin_amdgcn_cvt_pk_fp8_f32(x[0][e], x[1][e], 0, false);
+      word = __builtin_amdgcn_cvt_pk_fp8_f32(x[2][e], x[3][e], word, true);
+      const int phys = (((base >> 4) ^ ((c >> 3) & 3)) << 4) | (base & 15);
+      *reinterpret_cast<int*>(&vt[(u * D + c) * VGROUP + phys]) = word;
     }
   }
   __syncthreads();
   uint8_t* dst = vcodes + (bh * (size_t)(Npad / VGROUP) + (size_t)kb * 2) * D * VGROUP;
-  for (int ch = tid; ch < 2 * D * VGROUP / 16; ch += 256)
-    *reinterpret_cast<uint4*>(dst + ch * 16) = *reinterpret_cast<const uint4*>(vt + ch * 16);
+  for (int ch = tid; ch < 2 * D * VGROUP / 16; ch += 256) {
+    const int rowc = ch >> 2, c = rowc % D;    // row = group * D + channel
+    const int src = rowc * VGROUP + (((ch & 3) ^ ((c >> 3) & 3)) << 4);
+    *reinterpret_cast<uint4*>(dst + ch * 16) = *reinterpret_cast<const uint4*>(vt + src);
+  }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -245,7 +265,7 @@ __global__ __launch_bounds__(256) void q_quant(const __half* __restrict__ q, int
                                                float* __restrict__ qscale, float* __restrict__ muq,
                                                uint16_t* __restrict__ muqs, int N, int Npad, int nqb, float R) {
   constexpr int TPR = D / 8, RPP = 256 / TPR, PASSES = BQ / RPP;
-  __shared__ long long ls[RPP][D];
+  __shared__ double ls[RPP][D];
   __shared__ float lmu[D];
   const int tid = threadIdx.x, cq = tid % TPR, r0 = tid / TPR;
   const int qb = blockIdx.x;
@@ -253,10 +273,11 @@ __global__ __launch_bounds__(256) void q_quant(const __half* __restrict__ q, int
   const __half* qbase = q + bh * (size_t)N * D;
   const int nvalid = min(BQ, N - qb * BQ);
 
+  // block sums in fp64 are exact (at most 128 fp16 terms, multiples of 2^-24, below 2^24)
   float x[PASSES][8];
-  long long s[8];
+  double s[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) s[e] = 0;
+  for (int e = 0; e < 8; ++e) s[e] = 0.0;
 #pragma unroll
   for (int p = 0; p < PASSES; ++p) {
     const int row = qb * BQ + p * RPP + r0;
@@ -265,7 +286,7 @@ __global__ __launch_bounds__(256) void q_quant(const __half* __restrict__ q, int
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         x[p][e] = __half2float(qq.h[e]);
-        s[e] += (long long)(x[p][e] * kFix);
+        s[e] += (double)x[p][e];
       }
     } else {
 #pragma unroll
@@ -276,9 +297,9 @@ __global__ __launch_bounds__(256) void q_quant(const __half* __restrict__ q, int
   for (int e = 0; e < 8; ++e) ls[r0][cq * 8 + e] = s[e];
   __syncthreads();
   for (int c = tid; c < D; c += 256) {
-    long long t = 0;
+    double t = 0.0;
     for (int r = 0; r < RPP; ++r) t += ls[r][c];
-    const float m = (float)((double)t / ((double)nvalid * 16777216.0));
+    const float m = (float)(t / (double)nvalid);
     lmu[c] = m;
     muq[(bh * nqb + qb) * D + c] = m;
     // exact three-part bf16 split of the mean, the A operand of the Delta_S GEMM

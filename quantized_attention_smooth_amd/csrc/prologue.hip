@@ -387,10 +387,10 @@ __device__ inline Split3 split3(const float (&x)[8]) {
 
 // Q-tile form, for few Q blocks per key: grid (Npad/256 key tiles, ceil(nqb/32) Q-block tiles,
 // B*H), 256 threads; each wave owns 32 Q blocks x 64 keys (two 32x32 MFMA tiles) and splits
-// its keys' gamma_K itself.  Causal rows stop at key (qb + 1) * 128.
+// both operands itself.  Causal rows stop at key (qb + 1) * 128.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) void delta_s_qtile(const __half* __restrict__ k, const float* __restrict__ muk,
-                                               const uint16_t* __restrict__ muqs, float* __restrict__ ds,
+                                               const float* __restrict__ muq, float* __restrict__ ds,
                                                int H, int Hkv, int N, int Npad, int nqb, float k2) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, r = lane & 31, hl = lane >> 5;
   const int bh = blockIdx.z, b = bh / H, h = bh % H, hk = h / (H / Hkv);
@@ -406,15 +406,18 @@ __global__ __launch_bounds__(256) void delta_s_qtile(const __half* __restrict__ 
 #pragma unroll 2
   for (int ks = 0; ks < D / 16; ++ks) {
     const int c0 = 16 * ks + 8 * hl;
-    Split3 A;                                          // mu_Q parts, split by the Q prologue
+    float xa[8];
     {
-      const uint16_t* ap = muqs + ((size_t)bh * nqb + min(qb, nqb - 1)) * 3 * D + c0;
-#pragma unroll
-      for (int p = 0; p < 3; ++p) {
-        const s16x8 av = qvalid ? *reinterpret_cast<const s16x8*>(ap + p * D) : (s16x8){};
-        A.p[p] = __builtin_bit_cast(bf16x8, av);
+      float4 m0 = make_float4(0.f, 0.f, 0.f, 0.f), m1 = m0;
+      if (qvalid) {
+        const float* src = muq + ((size_t)bh * nqb + qb) * D + c0;
+        m0 = *reinterpret_cast<const float4*>(src);
+        m1 = *reinterpret_cast<const float4*>(src + 4);
       }
+      xa[0] = m0.x; xa[1] = m0.y; xa[2] = m0.z; xa[3] = m0.w;
+      xa[4] = m1.x; xa[5] = m1.y; xa[6] = m1.z; xa[7] = m1.w;
     }
+    const Split3 A = split3(xa);
     const float4 mk0 = *reinterpret_cast<const float4*>(muk + bkv * D + c0);
     const float4 mk1 = *reinterpret_cast<const float4*>(muk + bkv * D + c0 + 4);
     const float mkv[8] = {mk0.x, mk0.y, mk0.z, mk0.w, mk1.x, mk1.y, mk1.z, mk1.w};
@@ -667,9 +670,9 @@ hipError_t launch_prologue_d(const Dims& Dm, const Ptrs& P, hipStream_t s) {
   } else {
     const dim3 g((Dm.Npad + 255) / 256, (Dm.nqb + 31) / 32, Dm.B * Dm.H);
     if (Dm.causal)
-      delta_s_qtile<D, true><<<g, 256, 0, s>>>(P.k, P.muk, P.muqs, P.ds, Dm.H, Dm.Hkv, Dm.N, Dm.Npad, Dm.nqb, k2);
+      delta_s_qtile<D, true><<<g, 256, 0, s>>>(P.k, P.muk, P.muq, P.ds, Dm.H, Dm.Hkv, Dm.N, Dm.Npad, Dm.nqb, k2);
     else
-      delta_s_qtile<D, false><<<g, 256, 0, s>>>(P.k, P.muk, P.muqs, P.ds, Dm.H, Dm.Hkv, Dm.N, Dm.Npad, Dm.nqb, k2);
+      delta_s_qtile<D, false><<<g, 256, 0, s>>>(P.k, P.muk, P.muq, P.ds, Dm.H, Dm.Hkv, Dm.N, Dm.Npad, Dm.nqb, k2);
   }
   return hipGetLastError();
 }

@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the SageAttention2 quantized attention forward on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload bench|llm|dit|gqa|tiny]
+    python bench.py [--steps K] [--warmup W] [--workload bench|llm|dit|gqa|tiny] [--pv-bits 8|16]
 
 A step is one whole forward pass (quantize/smooth prologue + fused attention kernel) over the
 workload's seeded synthetic inputs, which are resident in HBM before the timed region.  The
@@ -11,7 +11,10 @@ binding passes to the library).
 
 Prints one JSON line: effective attention TOPS = 4*B*H*N^2*d / t (halved when causal), the
 roofline of the dominant kernel (the fused attention kernel, MFMA bound) and the CPU oracle's
-rate on a bounded sample of the same workload.
+rate on a bounded sample of the same workload.  QK^T and PV each carry half of the kernel's
+ops, on different matrix instructions, so its peak is the harmonic mix of the two dense peaks:
+INT8 5.0 P (QK^T, 8-bit codes), FP6 10.1 P (QK^T, INT4-range codes), FP8 5.0 P (P~V) and
+fp16 2.5 P (PV in the fp16 mode).
 
 Other modes:
   --calibrate-copy   run a plain device copy of known size (for scaling rocprofv3's
@@ -31,37 +34,46 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "effective attention TOPS (4·B·H·N²·d/t, ½ if causal) at N=8K–32K, d=64/128"
-PEAK_TOPS = 5000.0          # MI355X dense INT8 (POP/s) and FP8 (PFLOP/s): 5.0 P each
+# MI355X dense matrix peaks, TOPS / TFLOP/s
+PEAK_QK = {8: 5000.0, 4: 10100.0}      # INT8 codes on the int8 MFMA; INT4-range codes on FP6
+PEAK_PV = {8: 5000.0, 16: 2500.0}      # FP8 P~ V; fp16 P V
 PEAK_HBM_GBPS = 8000.0
+
+
+def attn_peak(qk_bits: int, pv_bits: int) -> float:
+    """Peak of a kernel that spends half its ops on QK^T and half on PV."""
+    return 1.0 / (0.5 / PEAK_QK[qk_bits] + 0.5 / PEAK_PV[pv_bits])
+
+
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.txt")
 ATTN_SRC = os.path.join(ROOT, "quantized_attention_smooth_amd", "csrc", "attention.hip")
 
 
-def _describe(w) -> str:
+def _describe(w, pv_bits: int) -> str:
     kind = "causal" if w.causal else "non-causal"
     heads = f"H{w.H}" if w.H == w.Hkv else f"H{w.H}/Hkv{w.Hkv}"
     return (f"{w.name}: B{w.B} {heads} N{w.N} d{w.d} {kind}, "
-            f"{'INT8' if w.qk_bits == 8 else 'INT4-range'} QK + FP8 PV")
+            f"{'INT8' if w.qk_bits == 8 else 'INT4-range'} QK + {'FP8' if pv_bits == 8 else 'fp16'} PV")
 
 
 def _src_hash() -> str:
     return hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
 
 
-def _traffic(workload: str):
+def _traffic(workload: str, pv_bits: int):
     """HBM bytes per attention-kernel launch from committed rocprofv3 counter runs, if they were
     taken on the current kernel source; else None."""
     try:
         t = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
-    e = t.get("workloads", {}).get(workload)
+    e = t.get("workloads", {}).get(workload if pv_bits == 8 else f"{workload}-pv16")
     if not e or t.get("attention_src_sha256") != _src_hash():
         return None
     return (e["fetch_kib"] * t["fetch_factor"] + e["write_kib"] * t["write_factor"]) * 1024.0
 
 
-def cpu_baseline(w, q, k, v, budget_s: float) -> dict:
+def cpu_baseline(w, q, k, v, budget_s: float, pv_bits: int = 8) -> dict:
     """The oracle as it stands, on one (b, h) head: its full prologue plus as many query blocks
     as fit the budget (spread over the sequence), extrapolated to the workload by block cost
     (causal block qb costs qb + 1 key blocks)."""
@@ -77,7 +89,7 @@ def cpu_baseline(w, q, k, v, budget_s: float) -> dict:
     k1 = np.ascontiguousarray(k[:1, hk:hk + 1])
     v1 = np.ascontiguousarray(v[:1, hk:hk + 1])
     t0 = time.perf_counter()
-    pro = osage.prologue(q1, k1, v1, w.causal, w.qk_bits)
+    pro = osage.prologue(q1, k1, v1, w.causal, w.qk_bits, quant_pv=pv_bits == 8)
     t_pro = time.perf_counter() - t0
     nqb = pro.nqb
     cost = [(qb + 1) if w.causal else pro.nkb for qb in range(nqb)]
@@ -124,6 +136,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="bench")
+    ap.add_argument("--pv-bits", type=int, default=8, choices=(8, 16),
+                    help="8: FP8 P~ and V (fast mode); 16: fp16 P and V (high-fidelity mode)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
@@ -155,13 +169,14 @@ def main() -> int:
     kd = torch.from_numpy(k).to(dev)
     vd = torch.from_numpy(v).to(dev)
     o = torch.empty_like(qd)
-    nbytes = sa.workspace_bytes(w.B, w.H, w.Hkv, w.N, w.d, w.causal, w.qk_bits)
+    pv = args.pv_bits
+    nbytes = sa.workspace_bytes(w.B, w.H, w.Hkv, w.N, w.d, w.causal, w.qk_bits, pv)
     ws = sa.alloc_workspace(nbytes, dev)
     shape = (w.B, w.H, w.N, w.d)
 
     def step():
-        sa.prologue(qd, kd, vd, ws, w.causal, w.qk_bits)
-        sa.attend(o, ws, shape, w.Hkv, w.causal, w.qk_bits)
+        sa.prologue(qd, kd, vd, ws, w.causal, w.qk_bits, pv)
+        sa.attend(o, ws, shape, w.Hkv, w.causal, w.qk_bits, pv)
 
     for _ in range(args.warmup):
         step()
@@ -178,9 +193,9 @@ def main() -> int:
     e_start.record()
     for s in range(K):
         ev[s][0].record()
-        sa.prologue(qd, kd, vd, ws, w.causal, w.qk_bits)
+        sa.prologue(qd, kd, vd, ws, w.causal, w.qk_bits, pv)
         ev[s][1].record()
-        sa.attend(o, ws, shape, w.Hkv, w.causal, w.qk_bits)
+        sa.attend(o, ws, shape, w.Hkv, w.causal, w.qk_bits, pv)
         ev[s][2].record()
     e_end.record()
     torch.cuda.synchronize()
@@ -196,18 +211,23 @@ def main() -> int:
     npad = nqb * 128
     n_q, n_kv = w.B * w.H * w.N * w.d, w.B * w.Hkv * w.N * w.d
     ds_elems = 128 * nqb * (nqb + 1) // 2 if w.causal else nqb * npad     # Delta_S rows per head
-    pro_bytes = 2 * (n_q + 2 * n_kv) + (n_q + 2 * n_kv) + 4 * w.B * w.H * ds_elems
-    traffic = _traffic(args.workload)
+    # read q, k, v once (fp16); write Q/K codes (1 byte), V as FP8 codes or fp16, Delta_S rows
+    pro_bytes = 2 * (n_q + 2 * n_kv) + (n_q + n_kv) + n_kv * (pv // 8) + 4 * w.B * w.H * ds_elems
+    traffic = _traffic(args.workload, pv)
+    peak = attn_peak(w.qk_bits, pv)
+    qk_t = "int8" if w.qk_bits == 8 else "fp6 (INT4-range codes)"
+    pv_t = "P~V fp8" if pv == 8 else "PV fp16"
 
     line = {
         "metric": METRIC, "value": value, "unit": "TOPS", "n_gpus": 1, "steps": K, "warmup": args.warmup,
         "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "i8+fp8e4m3", "data": "synthetic",
-        "config": {"workload": _describe(w), "B": w.B, "H": w.H, "Hkv": w.Hkv, "N": w.N, "d": w.d,
-                   "causal": w.causal, "qk_bits": w.qk_bits, "seed": 0},
-        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_TOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_TOPS, "traffic": traffic,
-                     "kernel": "attn_fwd (fused QK^T int8 MFMA + softmax + P~V fp8 MFMA)",
+        "dtype": ("i8" if w.qk_bits == 8 else "fp6e2m3") + ("+fp8e4m3" if pv == 8 else "+fp16"),
+        "data": "synthetic",
+        "config": {"workload": _describe(w, pv), "B": w.B, "H": w.H, "Hkv": w.Hkv, "N": w.N, "d": w.d,
+                   "causal": w.causal, "qk_bits": w.qk_bits, "pv_bits": pv, "seed": 0},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                     "frac": achieved / peak, "traffic": traffic,
+                     "kernel": f"attn_fwd (fused QK^T {qk_t} MFMA + softmax + {pv_t} MFMA)",
                      "per_unit": f"4*d = {4 * w.d} int8/fp8 ops per score element; "
                                  f"{ops / (4 * w.d):.4g} score elements per launch"},
         "breakdown": {"prologue_ms": pro_ms, "attention_ms": att_ms,
@@ -216,7 +236,7 @@ def main() -> int:
                       "wall_s_timed": wall},
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_budget)
+        line["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_budget, pv)
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)

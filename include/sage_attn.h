@@ -11,7 +11,9 @@
  *           "key_machinery" and "supporting_citations".
  *   [BLOG]  "SageAttention：大模型量化注意力加速实践指南" (blog.gitcode.com), sections on the
  *           core API call and precision control: the method is a drop-in for PyTorch's
- *           scaled_dot_product_attention selected by a head_dim / is_causal / quant mode.
+ *           scaled_dot_product_attention selected by a head_dim / is_causal / quant mode;
+ *           the quant modes "qk_int8_pv_fp8" (fast) and "qk_int8_pv_fp16" (high fidelity:
+ *           V kept in fp16) select the P~V precision.
  *
  * What the library computes: O = softmax(Q K^T / sqrt(d)) V, approximated as in [SA2]:
  * K is smoothed by its per-channel mean over tokens, Q by its per-block mean with the
@@ -22,13 +24,16 @@
  * quantized to FP8 E4M3 with the static range P_r = 448; V is quantized per channel to
  * FP8 E4M3 with V_r = 448 [SA2pp key_machinery]; P~V runs on the FP8 MFMA, each KV block
  * into a zeroed block-local accumulator that is then folded into a global fp32
- * accumulator [SA2], [SA2c].
+ * accumulator [SA2], [SA2c].  With pv_bits = 16 (the [BLOG] high-fidelity mode) V is not
+ * quantized: P and V enter the fp16 MFMA (fp32 accumulation) and only QK^T is quantized.
  *
  * Tensors (all device pointers, caller-owned, never freed or retained by the library):
  *   q, o : fp16, contiguous [B, H, N, d]           (o is overwritten)
  *   k, v : fp16, contiguous [B, Hkv, N, d]; query head h reads kv head h / (H / Hkv)
  *   causal: 0 or 1; 1 masks key j > query i (top-left aligned, N_q == N_k)
  *   d    : 64 or 128; softmax scale 1/sqrt(d)
+ *   qk_bits: 8 (INT8 codes) or 4 (INT4-range codes)
+ *   pv_bits: 8 (FP8 P~ and V, two-level accumulation) or 16 (fp16 P and V)
  *   workspace: device memory of at least sage_attn_workspace_bytes(...) bytes, 256-byte
  *          aligned; its contents on entry are ignored.
  *   stream: a hipStream_t (NULL = the legacy default stream).  Every call is stream
@@ -52,7 +57,8 @@ extern "C" {
 
 #define SAGE_OK 0
 #define SAGE_ERR_INVALID_ARG (-1) /* null pointer, size < 1, H % Hkv != 0, size overflow  */
-#define SAGE_ERR_UNSUPPORTED (-2) /* d not in {64, 128}, qk_bits not in {4, 8}, N > 2^23  */
+#define SAGE_ERR_UNSUPPORTED (-2) /* d not in {64, 128}, qk_bits not in {4, 8},
+                                     pv_bits not in {8, 16}, N > 2^23                       */
 #define SAGE_ERR_WORKSPACE (-3)   /* workspace missing, too small or not 256-byte aligned */
 #define SAGE_ERR_HIP (-4)         /* a HIP runtime call or kernel launch failed          */
 
@@ -82,7 +88,7 @@ int sage_get_config(sage_config_t* out);
 
 /* Bytes of workspace sage_attn_fwd needs for this problem (written to *bytes). */
 int sage_attn_workspace_bytes(int B, int H, int Hkv, int N, int d, int causal, int qk_bits,
-                              size_t* bytes);
+                              int pv_bits, size_t* bytes);
 
 /*
  * The whole forward pass: quantize/smooth prologue kernels, then the fused attention
@@ -90,22 +96,22 @@ int sage_attn_workspace_bytes(int B, int H, int Hkv, int N, int d, int causal, i
  * is_causal=causal) for fp16 inputs [BLOG core API; SA2].
  */
 int sage_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, int Hkv,
-                  int N, int d, int causal, int qk_bits, void* workspace,
+                  int N, int d, int causal, int qk_bits, int pv_bits, void* workspace,
                   size_t workspace_bytes, void* stream);
 
 /*
  * The two halves of sage_attn_fwd, for callers that time or schedule them separately.
  * sage_attn_prologue smooths and quantizes q, k, v into `workspace` (K/Q/V codes, scales,
  * means and the Delta_S bias).  sage_attn_attend runs the fused attention kernel on a
- * workspace the prologue filled for the same (B, H, Hkv, N, d, causal, qk_bits) and writes
+ * workspace the prologue filled for the same (B, H, Hkv, N, d, causal, qk_bits, pv_bits) and writes
  * o; a workspace filled for another problem gives meaningless output.  Stream ordered;
  * same argument and error rules as sage_attn_fwd.
  */
 int sage_attn_prologue(const void* q, const void* k, const void* v, int B, int H, int Hkv, int N,
-                       int d, int causal, int qk_bits, void* workspace, size_t workspace_bytes,
-                       void* stream);
+                       int d, int causal, int qk_bits, int pv_bits, void* workspace,
+                       size_t workspace_bytes, void* stream);
 int sage_attn_attend(void* o, int B, int H, int Hkv, int N, int d, int causal, int qk_bits,
-                     void* workspace, size_t workspace_bytes, void* stream);
+                     int pv_bits, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Test/debug: run the prologue only and copy its results, in plain layouts, to the
@@ -113,8 +119,8 @@ int sage_attn_attend(void* o, int B, int H, int Hkv, int N, int d, int causal, i
  *   mu_k     fp32 [B, Hkv, d]            mean of K over all N keys
  *   k_codes  int8 [B, Hkv, N, d]         quantized smoothed K
  *   k_scales fp32 [B, Hkv, N]            scale of each key's group
- *   v_codes  uint8 [B, Hkv, N, d]        FP8 E4M3 codes of V
- *   v_scales fp32 [B, Hkv, d]            delta_V = max|V[:, c]| / V_r
+ *   v_codes  uint8 [B, Hkv, N, d]        FP8 E4M3 codes of V (must be NULL when pv_bits = 16)
+ *   v_scales fp32 [B, Hkv, d]            delta_V = max|V[:, c]| / V_r (NULL when pv_bits = 16)
  *   mu_q     fp32 [B, H, ceil(N/bq), d]  per-block mean of Q
  *   q_codes  int8 [B, H, N, d]           quantized smoothed Q
  *   q_scales fp32 [B, H, N]              scale of each query's group
@@ -124,9 +130,10 @@ int sage_attn_attend(void* o, int B, int H, int Hkv, int N, int d, int causal, i
  * Same tensor/workspace/stream rules as sage_attn_fwd.
  */
 int sage_quant_debug(const void* q, const void* k, const void* v, int B, int H, int Hkv, int N,
-                     int d, int causal, int qk_bits, void* workspace, size_t workspace_bytes,
-                     void* stream, void* mu_k, void* k_codes, void* k_scales, void* v_codes,
-                     void* v_scales, void* mu_q, void* q_codes, void* q_scales, void* delta_s);
+                     int d, int causal, int qk_bits, int pv_bits, void* workspace,
+                     size_t workspace_bytes, void* stream, void* mu_k, void* k_codes,
+                     void* k_scales, void* v_codes, void* v_scales, void* mu_q, void* q_codes,
+                     void* q_scales, void* delta_s);
 
 /*
  * Test/debug: run the prologue, then the attention kernel's own integer-MFMA QK^T code
@@ -135,8 +142,9 @@ int sage_quant_debug(const void* q, const void* k, const void* v, int B, int H, 
  * past N and keys past N hold the products of the zero padding codes).
  */
 int sage_qk_tile_debug(const void* q, const void* k, const void* v, int B, int H, int Hkv, int N,
-                       int d, int causal, int qk_bits, void* workspace, size_t workspace_bytes,
-                       void* stream, int b, int h, int qb, int kb, int32_t* tile_out);
+                       int d, int causal, int qk_bits, int pv_bits, void* workspace,
+                       size_t workspace_bytes, void* stream, int b, int h, int qb, int kb,
+                       int32_t* tile_out);
 
 /* Static text for a status code. */
 const char* sage_status_string(int status);

@@ -7,7 +7,7 @@ torch, and passes raw device pointers and the current stream.  There is no fallb
 library is missing or fails to load, importing this package raises ImportError.
 
     from quantized_attention_smooth_amd import sageattn
-    o = sageattn(q, k, v, is_causal=True, qk_bits=8)   # like F.scaled_dot_product_attention
+    o = sageattn(q, k, v, is_causal=True, qk_bits=8, pv_bits=8)   # like F.scaled_dot_product_attention
 """
 from __future__ import annotations
 
@@ -55,12 +55,12 @@ def _load() -> ctypes.CDLL:
         raise ImportError(f"cannot load {LIB_PATH}: {e}") from e
     P, I, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
     lib.sage_get_config.argtypes = [ctypes.POINTER(SageConfig)]
-    lib.sage_attn_workspace_bytes.argtypes = [I, I, I, I, I, I, I, ctypes.POINTER(S)]
-    lib.sage_attn_fwd.argtypes = [P, P, P, P, I, I, I, I, I, I, I, P, S, P]
-    lib.sage_attn_prologue.argtypes = [P, P, P, I, I, I, I, I, I, I, P, S, P]
-    lib.sage_attn_attend.argtypes = [P, I, I, I, I, I, I, I, P, S, P]
-    lib.sage_quant_debug.argtypes = [P, P, P, I, I, I, I, I, I, I, P, S, P] + [P] * 9
-    lib.sage_qk_tile_debug.argtypes = [P, P, P, I, I, I, I, I, I, I, P, S, P, I, I, I, I, P]
+    lib.sage_attn_workspace_bytes.argtypes = [I, I, I, I, I, I, I, I, ctypes.POINTER(S)]
+    lib.sage_attn_fwd.argtypes = [P, P, P, P, I, I, I, I, I, I, I, I, P, S, P]
+    lib.sage_attn_prologue.argtypes = [P, P, P, I, I, I, I, I, I, I, I, P, S, P]
+    lib.sage_attn_attend.argtypes = [P, I, I, I, I, I, I, I, I, P, S, P]
+    lib.sage_quant_debug.argtypes = [P, P, P, I, I, I, I, I, I, I, I, P, S, P] + [P] * 9
+    lib.sage_qk_tile_debug.argtypes = [P, P, P, I, I, I, I, I, I, I, I, P, S, P, I, I, I, I, P]
     lib.sage_status_string.argtypes = [I]
     lib.sage_status_string.restype = ctypes.c_char_p
     lib.sage_last_error.argtypes = []
@@ -91,9 +91,10 @@ def get_config() -> dict:
     return {name: getattr(cfg, name) for name, _ in SageConfig._fields_}
 
 
-def workspace_bytes(B: int, H: int, Hkv: int, N: int, d: int, causal: bool, qk_bits: int) -> int:
+def workspace_bytes(B: int, H: int, Hkv: int, N: int, d: int, causal: bool, qk_bits: int,
+                    pv_bits: int = 8) -> int:
     n = ctypes.c_size_t(0)
-    _check(_lib.sage_attn_workspace_bytes(B, H, Hkv, N, d, int(causal), qk_bits, ctypes.byref(n)))
+    _check(_lib.sage_attn_workspace_bytes(B, H, Hkv, N, d, int(causal), qk_bits, pv_bits, ctypes.byref(n)))
     return n.value
 
 
@@ -127,54 +128,56 @@ def alloc_workspace(nbytes: int, device) -> torch.Tensor:
     return buf[off:off + nbytes]
 
 
-def fwd(q, k, v, o, workspace, is_causal: bool = False, qk_bits: int = 8) -> None:
+def fwd(q, k, v, o, workspace, is_causal: bool = False, qk_bits: int = 8, pv_bits: int = 8) -> None:
     """sage_attn_fwd on caller-provided tensors (o and workspace are written)."""
     B, H, Hkv, N, d = _shapes(q, k, v)
     if o.shape != q.shape or o.dtype != torch.float16 or not o.is_contiguous() or o.device != q.device:
         raise ValueError("o must be a contiguous float16 tensor shaped like q on q's device")
     _check(_lib.sage_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, Hkv, N, d, int(is_causal), qk_bits,
-                              _ptr(workspace), workspace.numel(), _stream(q.device)))
+                              pv_bits, _ptr(workspace), workspace.numel(), _stream(q.device)))
 
 
-def prologue(q, k, v, workspace, is_causal: bool = False, qk_bits: int = 8) -> None:
+def prologue(q, k, v, workspace, is_causal: bool = False, qk_bits: int = 8, pv_bits: int = 8) -> None:
     """sage_attn_prologue: fill `workspace` with the quantized/smoothed operands."""
     B, H, Hkv, N, d = _shapes(q, k, v)
     _check(_lib.sage_attn_prologue(_ptr(q), _ptr(k), _ptr(v), B, H, Hkv, N, d, int(is_causal), qk_bits,
-                                   _ptr(workspace), workspace.numel(), _stream(q.device)))
+                                   pv_bits, _ptr(workspace), workspace.numel(), _stream(q.device)))
 
 
-def attend(o, workspace, shape, Hkv: int, is_causal: bool = False, qk_bits: int = 8) -> None:
+def attend(o, workspace, shape, Hkv: int, is_causal: bool = False, qk_bits: int = 8, pv_bits: int = 8) -> None:
     """sage_attn_attend: the fused attention kernel on a workspace filled by prologue().
 
     shape = (B, H, N, d) of q/o."""
     B, H, N, d = shape
     if tuple(o.shape) != (B, H, N, d) or o.dtype != torch.float16 or not o.is_contiguous() or not o.is_cuda:
         raise ValueError("o must be a contiguous float16 CUDA tensor of shape (B, H, N, d)")
-    _check(_lib.sage_attn_attend(_ptr(o), B, H, Hkv, N, d, int(is_causal), qk_bits, _ptr(workspace),
+    _check(_lib.sage_attn_attend(_ptr(o), B, H, Hkv, N, d, int(is_causal), qk_bits, pv_bits, _ptr(workspace),
                                  workspace.numel(), _stream(o.device)))
 
 
 def sageattn(q, k, v, attn_mask=None, dropout_p: float = 0.0, is_causal: bool = False, scale=None,
-             qk_bits: int = 8, workspace=None):
+             qk_bits: int = 8, pv_bits: int = 8, workspace=None):
     """Quantized drop-in for F.scaled_dot_product_attention(q, k, v, is_causal=...).
 
     q [B, H, N, d], k/v [B, Hkv, N, d], fp16, contiguous; d in {64, 128}; qk_bits 8 (INT8
-    codes) or 4 (INT4-range codes).  Grouped-query attention maps head h to kv head
+    codes) or 4 (INT4-range codes); pv_bits 8 (FP8 P~ and V, the fast mode) or 16 (fp16 P
+    and V, the high-fidelity mode).  Grouped-query attention maps head h to kv head
     h // (H // Hkv).  Returns fp16 [B, H, N, d].
     """
     if attn_mask is not None or dropout_p != 0.0 or scale is not None:
         raise NotImplementedError("attn_mask, dropout and custom scale are not supported")
     B, H, Hkv, N, d = _shapes(q, k, v)
-    nbytes = workspace_bytes(B, H, Hkv, N, d, is_causal, qk_bits)
+    nbytes = workspace_bytes(B, H, Hkv, N, d, is_causal, qk_bits, pv_bits)
     if workspace is None or workspace.numel() < nbytes:
         workspace = alloc_workspace(nbytes, q.device)
     o = torch.empty_like(q)
-    fwd(q, k, v, o, workspace, is_causal, qk_bits)
+    fwd(q, k, v, o, workspace, is_causal, qk_bits, pv_bits)
     return o
 
 
-def quant_debug(q, k, v, is_causal: bool = False, qk_bits: int = 8) -> dict:
-    """Prologue outputs in plain layouts (see sage_quant_debug in include/sage_attn.h)."""
+def quant_debug(q, k, v, is_causal: bool = False, qk_bits: int = 8, pv_bits: int = 8) -> dict:
+    """Prologue outputs in plain layouts (see sage_quant_debug in include/sage_attn.h); with
+    pv_bits = 16 there are no V codes or scales and those entries are None."""
     B, H, Hkv, N, d = _shapes(q, k, v)
     nqb = -(-N // get_config()["bq"])
     dev = q.device
@@ -189,19 +192,22 @@ def quant_debug(q, k, v, is_causal: bool = False, qk_bits: int = 8) -> dict:
         "q_scales": torch.empty(B, H, N, dtype=torch.float32, device=dev),
         "delta_s": torch.empty(B, H, nqb, N, dtype=torch.float32, device=dev),
     }
-    ws = alloc_workspace(workspace_bytes(B, H, Hkv, N, d, is_causal, qk_bits), dev)
+    if pv_bits == 16:
+        out["v_codes"] = out["v_scales"] = None
+    ws = alloc_workspace(workspace_bytes(B, H, Hkv, N, d, is_causal, qk_bits, pv_bits), dev)
     names = ("mu_k", "k_codes", "k_scales", "v_codes", "v_scales", "mu_q", "q_codes", "q_scales", "delta_s")
-    _check(_lib.sage_quant_debug(_ptr(q), _ptr(k), _ptr(v), B, H, Hkv, N, d, int(is_causal), qk_bits, _ptr(ws),
-                                 ws.numel(), _stream(dev), *[_ptr(out[n]) for n in names]))
+    _check(_lib.sage_quant_debug(_ptr(q), _ptr(k), _ptr(v), B, H, Hkv, N, d, int(is_causal), qk_bits, pv_bits,
+                                 _ptr(ws), ws.numel(), _stream(dev), *[_ptr(out[n]) for n in names]))
     return out
 
 
-def qk_tile_debug(q, k, v, b: int, h: int, qb: int, kb: int, is_causal: bool = False, qk_bits: int = 8):
+def qk_tile_debug(q, k, v, b: int, h: int, qb: int, kb: int, is_causal: bool = False, qk_bits: int = 8,
+                  pv_bits: int = 8):
     """Raw int32 S tile [bq, bk] of the attention kernel's integer MFMA path."""
     B, H, Hkv, N, d = _shapes(q, k, v)
     cfg = get_config()
     tile = torch.empty(cfg["bq"], cfg["bk"], dtype=torch.int32, device=q.device)
-    ws = alloc_workspace(workspace_bytes(B, H, Hkv, N, d, is_causal, qk_bits), q.device)
-    _check(_lib.sage_qk_tile_debug(_ptr(q), _ptr(k), _ptr(v), B, H, Hkv, N, d, int(is_causal), qk_bits, _ptr(ws),
-                                   ws.numel(), _stream(q.device), b, h, qb, kb, _ptr(tile)))
+    ws = alloc_workspace(workspace_bytes(B, H, Hkv, N, d, is_causal, qk_bits, pv_bits), q.device)
+    _check(_lib.sage_qk_tile_debug(_ptr(q), _ptr(k), _ptr(v), B, H, Hkv, N, d, int(is_causal), qk_bits, pv_bits,
+                                   _ptr(ws), ws.numel(), _stream(q.device), b, h, qb, kb, _ptr(tile)))
     return tile

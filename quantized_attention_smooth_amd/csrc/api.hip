@@ -20,12 +20,13 @@ int hip_fail(hipError_t e, const char* what) {
 }
 
 // Shape checks shared by every entry point; fills D on success.
-int check_dims(int B, int H, int Hkv, int N, int d, int causal, int qk_bits, sage::Dims* D) {
+int check_dims(int B, int H, int Hkv, int N, int d, int causal, int qk_bits, int pv_bits, sage::Dims* D) {
   if (B < 1 || H < 1 || Hkv < 1 || N < 1) return SAGE_ERR_INVALID_ARG;
   if (H % Hkv != 0) return SAGE_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return SAGE_ERR_INVALID_ARG;
   if (d != 64 && d != 128) return SAGE_ERR_UNSUPPORTED;
   if (qk_bits != 4 && qk_bits != 8) return SAGE_ERR_UNSUPPORTED;
+  if (pv_bits != 8 && pv_bits != 16) return SAGE_ERR_UNSUPPORTED;
   if (N > (1 << 23)) return SAGE_ERR_UNSUPPORTED;   // exact fixed-point K sums need N <= 2^23
   const long long npad = ((long long)N + 127) / 128 * 128;
   // every element count the kernels index must fit comfortably in 64 bits, and the number of
@@ -35,7 +36,7 @@ int check_dims(int B, int H, int Hkv, int N, int d, int causal, int qk_bits, sag
   if (heads * (double)(npad / 128) * (double)npad * 4.0 > 9.0e18) return SAGE_ERR_INVALID_ARG;
   if (heads * (double)(npad / 128) > 2147483647.0) return SAGE_ERR_INVALID_ARG;
   if ((double)B * Hkv > 65535.0 || heads > 65535.0) return SAGE_ERR_INVALID_ARG;   // grid.y/z limits
-  D->B = B; D->H = H; D->Hkv = Hkv; D->N = N; D->d = d; D->causal = causal; D->qk_bits = qk_bits;
+  D->B = B; D->H = H; D->Hkv = Hkv; D->N = N; D->d = d; D->causal = causal; D->qk_bits = qk_bits; D->pv_bits = pv_bits;
   D->Npad = (int)npad;
   D->nqb = D->Npad / 128;
   D->nkb = D->Npad / 128;
@@ -70,20 +71,21 @@ int sage_get_config(sage_config_t* out) {
   return SAGE_OK;
 }
 
-int sage_attn_workspace_bytes(int B, int H, int Hkv, int N, int d, int causal, int qk_bits, size_t* bytes) {
+int sage_attn_workspace_bytes(int B, int H, int Hkv, int N, int d, int causal, int qk_bits, int pv_bits,
+                              size_t* bytes) {
   if (bytes == nullptr) return SAGE_ERR_INVALID_ARG;
   sage::Dims D;
-  const int st = check_dims(B, H, Hkv, N, d, causal, qk_bits, &D);
+  const int st = check_dims(B, H, Hkv, N, d, causal, qk_bits, pv_bits, &D);
   if (st != SAGE_OK) return st;
   *bytes = sage::make_layout(D).total;
   return SAGE_OK;
 }
 
 int sage_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, int Hkv, int N, int d,
-                  int causal, int qk_bits, void* workspace, size_t workspace_bytes, void* stream) {
+                  int causal, int qk_bits, int pv_bits, void* workspace, size_t workspace_bytes, void* stream) {
   if (!q || !k || !v || !o) return SAGE_ERR_INVALID_ARG;
   sage::Dims D;
-  int st = check_dims(B, H, Hkv, N, d, causal, qk_bits, &D);
+  int st = check_dims(B, H, Hkv, N, d, causal, qk_bits, pv_bits, &D);
   if (st != SAGE_OK) return st;
   const sage::Layout L = sage::make_layout(D);
   st = check_ws(workspace, workspace_bytes, L);
@@ -98,10 +100,11 @@ int sage_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, i
 }
 
 int sage_attn_prologue(const void* q, const void* k, const void* v, int B, int H, int Hkv, int N, int d,
-                       int causal, int qk_bits, void* workspace, size_t workspace_bytes, void* stream) {
+                       int causal, int qk_bits, int pv_bits, void* workspace, size_t workspace_bytes,
+                       void* stream) {
   if (!q || !k || !v) return SAGE_ERR_INVALID_ARG;
   sage::Dims D;
-  int st = check_dims(B, H, Hkv, N, d, causal, qk_bits, &D);
+  int st = check_dims(B, H, Hkv, N, d, causal, qk_bits, pv_bits, &D);
   if (st != SAGE_OK) return st;
   const sage::Layout L = sage::make_layout(D);
   st = check_ws(workspace, workspace_bytes, L);
@@ -111,11 +114,11 @@ int sage_attn_prologue(const void* q, const void* k, const void* v, int B, int H
   return e == hipSuccess ? SAGE_OK : hip_fail(e, "prologue launch");
 }
 
-int sage_attn_attend(void* o, int B, int H, int Hkv, int N, int d, int causal, int qk_bits, void* workspace,
-                     size_t workspace_bytes, void* stream) {
+int sage_attn_attend(void* o, int B, int H, int Hkv, int N, int d, int causal, int qk_bits, int pv_bits,
+                     void* workspace, size_t workspace_bytes, void* stream) {
   if (!o) return SAGE_ERR_INVALID_ARG;
   sage::Dims D;
-  int st = check_dims(B, H, Hkv, N, d, causal, qk_bits, &D);
+  int st = check_dims(B, H, Hkv, N, d, causal, qk_bits, pv_bits, &D);
   if (st != SAGE_OK) return st;
   const sage::Layout L = sage::make_layout(D);
   st = check_ws(workspace, workspace_bytes, L);
@@ -126,12 +129,13 @@ int sage_attn_attend(void* o, int B, int H, int Hkv, int N, int d, int causal, i
 }
 
 int sage_quant_debug(const void* q, const void* k, const void* v, int B, int H, int Hkv, int N, int d, int causal,
-                     int qk_bits, void* workspace, size_t workspace_bytes, void* stream, void* mu_k, void* k_codes,
-                     void* k_scales, void* v_codes, void* v_scales, void* mu_q, void* q_codes, void* q_scales,
-                     void* delta_s) {
+                     int qk_bits, int pv_bits, void* workspace, size_t workspace_bytes, void* stream, void* mu_k,
+                     void* k_codes, void* k_scales, void* v_codes, void* v_scales, void* mu_q, void* q_codes,
+                     void* q_scales, void* delta_s) {
   if (!q || !k || !v) return SAGE_ERR_INVALID_ARG;
+  if (pv_bits == 16 && (v_codes || v_scales)) return SAGE_ERR_INVALID_ARG;   // V is not quantized
   sage::Dims D;
-  int st = check_dims(B, H, Hkv, N, d, causal, qk_bits, &D);
+  int st = check_dims(B, H, Hkv, N, d, causal, qk_bits, pv_bits, &D);
   if (st != SAGE_OK) return st;
   const sage::Layout L = sage::make_layout(D);
   st = check_ws(workspace, workspace_bytes, L);
@@ -150,11 +154,11 @@ int sage_quant_debug(const void* q, const void* k, const void* v, int B, int H, 
 }
 
 int sage_qk_tile_debug(const void* q, const void* k, const void* v, int B, int H, int Hkv, int N, int d, int causal,
-                       int qk_bits, void* workspace, size_t workspace_bytes, void* stream, int b, int h, int qb,
-                       int kb, int32_t* tile_out) {
+                       int qk_bits, int pv_bits, void* workspace, size_t workspace_bytes, void* stream, int b, int h,
+                       int qb, int kb, int32_t* tile_out) {
   if (!q || !k || !v || !tile_out) return SAGE_ERR_INVALID_ARG;
   sage::Dims D;
-  int st = check_dims(B, H, Hkv, N, d, causal, qk_bits, &D);
+  int st = check_dims(B, H, Hkv, N, d, causal, qk_bits, pv_bits, &D);
   if (st != SAGE_OK) return st;
   if (b < 0 || b >= B || h < 0 || h >= H || qb < 0 || qb >= D.nqb || kb < 0 || kb >= D.nkb)
     return SAGE_ERR_INVALID_ARG;
@@ -174,7 +178,7 @@ const char* sage_status_string(int status) {
   switch (status) {
     case SAGE_OK: return "ok";
     case SAGE_ERR_INVALID_ARG: return "invalid argument (null pointer, size < 1, H % Hkv != 0 or size overflow)";
-    case SAGE_ERR_UNSUPPORTED: return "unsupported configuration (d must be 64 or 128, qk_bits 4 or 8, N <= 2^23)";
+    case SAGE_ERR_UNSUPPORTED: return "unsupported configuration (d must be 64 or 128, qk_bits 4 or 8, pv_bits 8 or 16, N <= 2^23)";
     case SAGE_ERR_WORKSPACE: return "workspace missing, too small or not 256-byte aligned";
     case SAGE_ERR_HIP: return "HIP runtime error (see sage_last_error)";
     default: return "unknown status";

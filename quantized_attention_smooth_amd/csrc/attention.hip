@@ -26,6 +26,13 @@
 //     double buffered, 16-byte chunks XOR-swizzled against LDS bank conflicts.
 //   * Workgroup ids are remapped so each XCD (own L2) works through whole heads; causal
 //     grids start with the longest (diagonal-most) query blocks.
+//   * fp16 P V (PV16; the high-fidelity "qk_int8_pv_fp16" mode of the blog page "SageAttention：
+//     大模型量化注意力加速实践指南", section on precision control): V stays fp16 and P = e^(z - m)
+//     is rounded to fp16 into the B operand of v_mfma_f32_32x32x16_f16 (8 k-slots per lane: a
+//     lane's keys 8a + 4(l / 32) + r of two adjacent a), accumulating straight into the fp32
+//     output accumulator.  The fp16 V tile is twice the FP8 one, so it has one LDS stage: the
+//     next block's V is issued once every wave is done with the current one and lands while
+//     the next QK^T and softmax run.
 #include <type_traits>
 
 #include "sage_internal.h"
@@ -38,6 +45,9 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2Pr = 8.807354922057604f;   // log2(448)
 
@@ -57,10 +67,13 @@ struct AttnArgs {
   int32_t* dbg_out;
 };
 
-template <int D>
+// V stages: FP8 codes [64-key group][channel][64 slots], double buffered; or fp16 V
+// [16-key group][channel][16 slots], one stage.  16-byte chunks swizzled in both.
+template <int D, bool PV16>
 struct Smem {
+  static constexpr int VST = PV16 ? 1 : 2;
   __attribute__((aligned(16))) int8_t k[2][BK * D];    // K tile rows, 16-byte chunks swizzled
-  __attribute__((aligned(16))) uint8_t v[2][BK * D];   // [64-key group][channel][64 slots], swizzled
+  __attribute__((aligned(16))) uint8_t v[VST][BK * D * (PV16 ? 2 : 1)];
   __attribute__((aligned(16))) float ds[2][BK];
 };
 
@@ -82,6 +95,9 @@ __device__ inline int kswz(int row) {       // K rows: 128 bytes (d = 128) or 64
 __device__ inline int vswz(int c) {         // V^T rows: 64 bytes per channel
   return ((c >> 1) ^ (c >> 3)) & 3;
 }
+__device__ inline int v16swz(int c) {       // fp16 V^T rows: 32 bytes per channel and group
+  return ((c >> 2) ^ (c >> 3)) & 1;
+}
 
 // combine a value with the one held by lane l ^ 32 (the other half holding the same query)
 __device__ inline float xhalf_max(float x) {
@@ -95,45 +111,69 @@ __device__ inline float xhalf_sum(float x) {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
+// direct-to-LDS instructions per wave per tile: K codes (and FP8 V codes), fp16 V
 template <int D>
-__device__ inline void issue_tile(const AttnArgs& a, Smem<D>& sm, int st, size_t bkv, size_t bh, int qb, int kb,
-                                  int w, int lane) {
+constexpr int kTileInstrs = BK * D / 16 / 64 / WAVES;
+
+// K codes of block kb (and its Delta_S row slice, wave 0) into stage st.  The Delta_S load
+// goes first, so a wait for "all but the last kTileInstrs" loads of wave 0 leaves only K
+// chunks outstanding.
+template <int D, bool PV16>
+__device__ inline void issue_k(const AttnArgs& a, Smem<D, PV16>& sm, int st, size_t bkv, size_t bh, int qb, int kb,
+                               int w, int lane) {
   constexpr int CPR = D / 16;                 // 16-byte chunks per K row
-  constexpr int NI = BK * D / 16 / 64 / WAVES; // direct-to-LDS instructions per wave per tile
-  // wave-uniform tile bases (scalar registers) plus 32-bit per-lane byte offsets
-  const int8_t* kbase = a.kcodes + (bkv * a.Npad + (size_t)kb * BK) * D;
-  const uint8_t* vbase = a.vcodes + (bkv * (size_t)(a.Npad / VGROUP) + (size_t)kb * 2) * D * VGROUP;
-#pragma unroll
-  for (int m = 0; m < NI; ++m) {
-    const int blk = m * WAVES + w;            // which 1 KB of the tile this wave writes
-    const int p = blk * 64 + lane;            // 16-byte chunk index in LDS
-    {
-      const int row = p / CPR, pc = p % CPR;
-      const uint32_t off = (uint32_t)(row * D + ((pc ^ kswz<D>(row)) * 16));
-      __builtin_amdgcn_global_load_lds(kbase + off, (lds_void*)(sm.k[st] + blk * 1024), 16, 0, 0);
-    }
-    {
-      const int row = p >> 2, pc = p & 3;     // row = group * D + channel
-      const uint32_t off = (uint32_t)(row * VGROUP + ((pc ^ vswz(row % D)) * 16));
-      __builtin_amdgcn_global_load_lds(vbase + off, (lds_void*)(sm.v[st] + blk * 1024), 16, 0, 0);
-    }
-  }
   if (w == 0 && lane < BK / 4) {
     const float* src = a.ds + bh * ds_head_elems(a.causal, a.nqb, a.Npad) + ds_row_offset(a.causal, qb, a.Npad) +
                        (size_t)kb * BK;
     __builtin_amdgcn_global_load_lds(src + (uint32_t)(lane * 4), (lds_void*)sm.ds[st], 16, 0, 0);
   }
+  // wave-uniform tile base (scalar registers) plus 32-bit per-lane byte offsets
+  const int8_t* kbase = a.kcodes + (bkv * a.Npad + (size_t)kb * BK) * D;
+#pragma unroll
+  for (int m = 0; m < kTileInstrs<D>; ++m) {
+    const int blk = m * WAVES + w;            // which 1 KB of the tile this wave writes
+    const int p = blk * 64 + lane;            // 16-byte chunk index in LDS
+    const int row = p / CPR, pc = p % CPR;
+    const uint32_t off = (uint32_t)(row * D + ((pc ^ kswz<D>(row)) * 16));
+    __builtin_amdgcn_global_load_lds(kbase + off, (lds_void*)(sm.k[st] + blk * 1024), 16, 0, 0);
+  }
+}
+
+// V of block kb into stage st: FP8 codes (64-byte rows) or fp16 V (32-byte rows, twice the
+// instructions).
+template <int D, bool PV16>
+__device__ inline void issue_v(const AttnArgs& a, Smem<D, PV16>& sm, int st, size_t bkv, int kb, int w, int lane) {
+  constexpr int RB = PV16 ? 32 : VGROUP;      // bytes per LDS row (group, channel)
+  constexpr int CR = RB / 16;                 // 16-byte chunks per row
+  const uint8_t* vbase = a.vcodes + (bkv * (size_t)a.Npad + (size_t)kb * BK) * D * (PV16 ? 2 : 1);
+#pragma unroll
+  for (int m = 0; m < kTileInstrs<D> * (PV16 ? 2 : 1); ++m) {
+    const int blk = m * WAVES + w;
+    const int p = blk * 64 + lane;
+    const int row = p / CR, pc = p % CR;      // row = group * D + channel
+    const int sw = PV16 ? v16swz(row % D) : vswz(row % D);
+    const uint32_t off = (uint32_t)(row * RB + ((pc ^ sw) * 16));
+    __builtin_amdgcn_global_load_lds(vbase + off, (lds_void*)(sm.v[st] + blk * 1024), 16, 0, 0);
+  }
 }
 
 __device__ inline void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// wait until at most the last kTileInstrs<D> vector loads of this wave are outstanding
+template <int D>
+__device__ inline void wait_all_but_k_tile() {
+  static_assert(kTileInstrs<D> == 4 || kTileInstrs<D> == 2, "vmcnt immediate");
+  if (kTileInstrs<D> == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+}
 
 // S^T tiles (32 keys each) x the wave's 32 queries, exact.  INT8 codes: v_mfma_i32_32x32x32_i8
 // from the biased accumulator (see kAccBias), 16 code bytes per lane per k-step.  INT4-range codes
 // (stored as FP6 E2M3, 24 bytes of each 32-byte slot): v_mfma_f32_32x32x64_f8f6f4 in FP6 mode from
 // zero, one slot per lane per k-step, at twice the INT8 rate; the products and sums of integers
 // this small are exact in its accumulator, so S arrives as fp32.
-template <int D, bool QK4>
-__device__ inline void qk_tiles(const Smem<D>& sm, int st, const v4i (&qreg)[D / 32], int col, int half,
+template <int D, bool QK4, bool PV16>
+__device__ inline void qk_tiles(const Smem<D, PV16>& sm, int st, const v4i (&qreg)[D / 32], int col, int half,
                                 v16i (&sacc)[BK / 32]) {
 #pragma unroll
   for (int t = 0; t < BK / 32; ++t) {
@@ -172,9 +212,9 @@ __device__ inline int xcd_remap(int bid, int total) {
   return x * q + min(x, r) + k;
 }
 
-template <int D, bool CAUSAL, bool DUMP, bool QK4>
+template <int D, bool CAUSAL, bool DUMP, bool QK4, bool PV16>
 __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
-  __shared__ Smem<D> sm;
+  __shared__ Smem<D, PV16> sm;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, col = lane & 31, half = lane >> 5;
 
   int b, h, qb;
@@ -203,11 +243,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
   const float qd = a.qscale[bh * a.Npad + i];
 
   if (DUMP) {
-    issue_tile<D>(a, sm, 0, bkv, bh, qb, a.dbg_kb, w, lane);
+    issue_k<D, PV16>(a, sm, 0, bkv, bh, qb, a.dbg_kb, w, lane);
     wait_loads();
     __syncthreads();
     v16i sacc[BK / 32];
-    qk_tiles<D, QK4>(sm, 0, qreg, col, half, sacc);
+    qk_tiles<D, QK4, PV16>(sm, 0, qreg, col, half, sacc);
 #pragma unroll
     for (int t = 0; t < BK / 32; ++t)
 #pragma unroll
@@ -224,19 +264,25 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
 #pragma unroll
   for (int ct = 0; ct < D / 32; ++ct) og[ct] = (v16f){};
 
-  issue_tile<D>(a, sm, 0, bkv, bh, qb, 0, w, lane);
+  issue_v<D, PV16>(a, sm, 0, bkv, 0, w, lane);
+  issue_k<D, PV16>(a, sm, 0, bkv, bh, qb, 0, w, lane);
   wait_loads();
   __syncthreads();
 
   // One KV block: S^T on the int8 MFMA, dequantize + bias (+ mask), online softmax, P~ V on the
-  // FP8 MFMA.  MASK is set only for the last block of a row range (causal diagonal or ragged tail).
+  // FP8 MFMA (or P V on the fp16 MFMA).  MASK is set only for the last block of a row range
+  // (causal diagonal or ragged tail).
   auto block = [&](const int kb, auto mask_tag) {
     constexpr bool MASK = decltype(mask_tag)::value;
     const int st = kb & 1;
-    if (kb + 1 < nblk) issue_tile<D>(a, sm, st ^ 1, bkv, bh, qb, kb + 1, w, lane);
+    const bool more = kb + 1 < nblk;
+    if (more) {
+      if (!PV16) issue_v<D, PV16>(a, sm, st ^ 1, bkv, kb + 1, w, lane);
+      issue_k<D, PV16>(a, sm, st ^ 1, bkv, bh, qb, kb + 1, w, lane);
+    }
 
     v16i sacc[BK / 32];
-    qk_tiles<D, QK4>(sm, st, qreg, col, half, sacc);
+    qk_tiles<D, QK4, PV16>(sm, st, qreg, col, half, sacc);
 
     // dequantize and add the Q-smoothing bias, in the log2 domain
     // both lane halves' delta_K through one wave-uniform (scalar) load, so that waiting for it
@@ -276,8 +322,63 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
     // a row has a finite max from its first block on (key 0 is never masked); the guards only
     // keep -inf - -inf out of the arithmetic
     const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-    const float mo = (m_new == -INFINITY ? 0.f : m_new) - kLog2Pr;   // p * P_r = 2^(z - mo)
+    // p * P_r = 2^(z - mo) (FP8 P~); p = 2^(z - mo) (fp16 P)
+    const float mo = (m_new == -INFINITY ? 0.f : m_new) - (PV16 ? 0.f : kLog2Pr);
     m_run = m_new;
+
+    if (PV16) {
+      // this block's fp16 V (issued at the end of the previous block) must have landed; later
+      // loads (the next K tile) may still be in flight
+      if (more) wait_all_but_k_tile<D>();
+      else wait_loads();
+      __syncthreads();
+#pragma unroll
+      for (int ct = 0; ct < D / 32; ++ct)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) og[ct][e] *= alpha;
+
+      // per 32-key tile: P = RN16(p) packed straight into two fp16 MFMA B operands (operand m
+      // takes the lane's keys of accumulator quads 2m and 2m + 1), then P V into the fp32
+      // output accumulator
+      float lsum = 0.f;
+#pragma unroll
+      for (int t = 0; t < BK / 32; ++t) {
+        h8 pb[2];
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+          const float p0 = __builtin_amdgcn_exp2f(z[t][4 * qq + 0] - mo);
+          const float p1 = __builtin_amdgcn_exp2f(z[t][4 * qq + 1] - mo);
+          const float p2 = __builtin_amdgcn_exp2f(z[t][4 * qq + 2] - mo);
+          const float p3 = __builtin_amdgcn_exp2f(z[t][4 * qq + 3] - mo);
+          lsum += (p0 + p1) + (p2 + p3);
+          const h2 lo = __builtin_convertvector((f2){p0, p1}, h2);
+          const h2 hi = __builtin_convertvector((f2){p2, p3}, h2);
+          const int o = 4 * (qq & 1);
+          pb[qq >> 1][o + 0] = lo[0];
+          pb[qq >> 1][o + 1] = lo[1];
+          pb[qq >> 1][o + 2] = hi[0];
+          pb[qq >> 1][o + 3] = hi[1];
+        }
+#pragma unroll
+        for (int ct = 0; ct < D / 32; ++ct) {
+          const int c = 32 * ct + col;
+          const int hc = (half ^ v16swz(c)) * 16;
+#pragma unroll
+          for (int m = 0; m < 2; ++m) {
+            const h8 va = *reinterpret_cast<const h8*>(sm.v[0] + ((2 * t + m) * D + c) * 32 + hc);
+            og[ct] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pb[m], og[ct], 0, 0, 0);
+          }
+        }
+        // keep the scheduler from hoisting later tiles' V reads (registers) above this one
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      l_part = fmaf(l_part, alpha, lsum);
+
+      wait_loads();
+      __syncthreads();
+      if (more) issue_v<D, PV16>(a, sm, 0, bkv, kb + 1, w, lane);
+      return;
+    }
 
     // P~ = E4M3(p * P_r), packed straight into the FP8 MFMA B operand
     v8i pb[BK / 64];
@@ -326,7 +427,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
   for (int kb = 0; kb < nfull; ++kb) block(kb, std::false_type{});
   if (mask_last) block(nblk - 1, std::true_type{});
 
-  // epilogue: O = acc * delta_V / l   (l counts p * P_r, so it carries the 1/P_r)
+  // epilogue: O = acc * delta_V / l   (FP8: l counts p * P_r, so it carries the 1/P_r;
+  // fp16: no V scale)
   const float l = xhalf_sum(l_part);
   const float inv_l = l > 0.f ? 1.f / l : 0.f;
   if (i < a.N) {
@@ -337,7 +439,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq) {
         const int c0 = 32 * ct + 8 * qq + 4 * half;
-        const float4 sc = *reinterpret_cast<const float4*>(vs + c0);
+        const float4 sc = PV16 ? make_float4(1.f, 1.f, 1.f, 1.f) : *reinterpret_cast<const float4*>(vs + c0);
         union { __half hh[4]; uint2 u; } pk;
         pk.hh[0] = __float2half_rn(og[ct][4 * qq + 0] * sc.x * inv_l);
         pk.hh[1] = __float2half_rn(og[ct][4 * qq + 1] * sc.y * inv_l);
@@ -365,33 +467,38 @@ AttnArgs make_args(const Dims& D, const Ptrs& P) {
   return a;
 }
 
-template <int DD, bool QK4>
+template <int DD, bool QK4, bool PV16>
 hipError_t launch_d(const Dims& D, const AttnArgs& a, hipStream_t s) {
   const int grid = D.B * D.H * D.nqb;
   if (D.causal)
-    attn_fwd<DD, true, false, QK4><<<grid, 256, 0, s>>>(a);
+    attn_fwd<DD, true, false, QK4, PV16><<<grid, 256, 0, s>>>(a);
   else
-    attn_fwd<DD, false, false, QK4><<<grid, 256, 0, s>>>(a);
+    attn_fwd<DD, false, false, QK4, PV16><<<grid, 256, 0, s>>>(a);
   return hipGetLastError();
+}
+
+template <bool QK4, bool PV16>
+hipError_t launch_qp(const Dims& D, const AttnArgs& a, hipStream_t s) {
+  return D.d == 128 ? launch_d<128, QK4, PV16>(D, a, s) : launch_d<64, QK4, PV16>(D, a, s);
 }
 
 }  // namespace
 
 hipError_t launch_attention(const Dims& D, const Ptrs& P, hipStream_t s) {
   const AttnArgs a = make_args(D, P);
-  if (D.qk_bits == 4) return D.d == 128 ? launch_d<128, true>(D, a, s) : launch_d<64, true>(D, a, s);
-  return D.d == 128 ? launch_d<128, false>(D, a, s) : launch_d<64, false>(D, a, s);
+  if (D.pv_bits == 16) return D.qk_bits == 4 ? launch_qp<true, true>(D, a, s) : launch_qp<false, true>(D, a, s);
+  return D.qk_bits == 4 ? launch_qp<true, false>(D, a, s) : launch_qp<false, false>(D, a, s);
 }
 
 hipError_t launch_qk_tile(const Dims& D, const Ptrs& P, int b, int h, int qb, int kb, int32_t* out, hipStream_t s) {
   AttnArgs a = make_args(D, P);
   a.dbg_b = b; a.dbg_h = h; a.dbg_qb = qb; a.dbg_kb = kb; a.dbg_out = out;
   if (D.qk_bits == 4) {
-    if (D.d == 128) attn_fwd<128, false, true, true><<<1, 256, 0, s>>>(a);
-    else attn_fwd<64, false, true, true><<<1, 256, 0, s>>>(a);
+    if (D.d == 128) attn_fwd<128, false, true, true, false><<<1, 256, 0, s>>>(a);
+    else attn_fwd<64, false, true, true, false><<<1, 256, 0, s>>>(a);
   } else {
-    if (D.d == 128) attn_fwd<128, false, true, false><<<1, 256, 0, s>>>(a);
-    else attn_fwd<64, false, true, false><<<1, 256, 0, s>>>(a);
+    if (D.d == 128) attn_fwd<128, false, true, false, false><<<1, 256, 0, s>>>(a);
+    else attn_fwd<64, false, true, false, false><<<1, 256, 0, s>>>(a);
   }
   return hipGetLastError();
 }

@@ -86,10 +86,10 @@ __global__ void init_stats(unsigned long long* ksum, unsigned int* vamax, int n)
 
 // ---------------------------------------------------------------------------------------
 // K channel sums (exact: fp64 within a workgroup, int64 fixed point across) and V channel
-// abs-max, per (b, kv head).
+// abs-max, per (b, kv head).  VSTATS = false (V kept in fp16) skips V entirely.
 // grid (ceil(N / 256), B*Hkv), 256 threads; thread = (row slot, 8-channel chunk).
 // ---------------------------------------------------------------------------------------
-template <int D>
+template <int D, bool VSTATS>
 __global__ __launch_bounds__(256) void kv_stats(const __half* __restrict__ k, const __half* __restrict__ v,
                                                 unsigned long long* __restrict__ ksum,
                                                 unsigned int* __restrict__ vamax, int N) {
@@ -115,11 +115,12 @@ __global__ __launch_bounds__(256) void kv_stats(const __half* __restrict__ k, co
     const int row = tok0 + p * RPP + r0;
     if (row < N) {
       const Half8 kk = load8(kb + (size_t)row * D + cq * 8);
-      const Half8 vv = load8(vb + (size_t)row * D + cq * 8);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        s[e] += (double)__half2float(kk.h[e]);
-        mx[e] = fmaxf(mx[e], fabsf(__half2float(vv.h[e])));
+      for (int e = 0; e < 8; ++e) s[e] += (double)__half2float(kk.h[e]);
+      if (VSTATS) {
+        const Half8 vv = load8(vb + (size_t)row * D + cq * 8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) mx[e] = fmaxf(mx[e], fabsf(__half2float(vv.h[e])));
       }
     }
   }
@@ -131,7 +132,57 @@ __global__ __launch_bounds__(256) void kv_stats(const __half* __restrict__ k, co
     float m = 0.f;
     for (int r = 0; r < RPP; ++r) { t += ls[r][c]; m = fmaxf(m, lm[r][c]); }
     atomicAdd(&ksum[bh * D + c], (unsigned long long)(long long)(t * 16777216.0));   // exact integer
-    atomicMax(&vamax[bh * D + c], __float_as_uint(m));            // order of non-negative floats
+    if (VSTATS) atomicMax(&vamax[bh * D + c], __float_as_uint(m));   // order of non-negative floats
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// fp16 V for the fp16 P V MFMA: the 128 keys of KV block kb, transposed into 8 groups of 16
+// keys, [group][channel][16 slots]; key kk of a group sits in slot 8 ((kk / 4) % 2) +
+// 4 (kk / 8) + kk % 4, the k-slot order of the fp16 MFMA B operand the attention kernel
+// builds from its S^T accumulators.  A thread takes 4 consecutive keys (4 consecutive slots:
+// one 8-byte LDS write per channel).  LDS rows (32 bytes) are XOR-permuted within each run of
+// 8 (row ^ (row / 8) % 8) so that the 8 channels 8 apart a wave writes at once fall on
+// distinct banks; the copy-out undoes it.
+// ---------------------------------------------------------------------------------------
+__device__ inline int v16_lds_row(int row) { return row ^ ((row >> 3) & 7); }
+
+template <int D>
+__device__ inline void store_v16(const __half* __restrict__ vbase, uint8_t* vt, uint8_t* __restrict__ vout,
+                                 size_t bh, int kb, int N, int Npad, int tid, int cq, int r0) {
+  constexpr int TPR = D / 8, RPP = 256 / TPR, G4 = BK / 4 / RPP;
+#pragma unroll
+  for (int p = 0; p < G4; ++p) {
+    const int jl0 = 4 * (p * RPP + r0);        // first of the thread's 4 keys within the block
+    const int g = jl0 >> 4, kk = jl0 & 15;
+    const int quad = 2 * ((kk >> 2) & 1) + (kk >> 3);   // slots 4 quad .. 4 quad + 3
+    uint16_t x[4][8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = kb * BK + jl0 + i;
+      if (row < N) {
+        const Half8 vv = load8(vbase + (size_t)row * D + cq * 8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[i][e] = __half_as_ushort(vv.h[e]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[i][e] = 0;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int row = g * D + cq * 8 + e;
+      const uint2 w2 = make_uint2((uint32_t)x[0][e] | ((uint32_t)x[1][e] << 16),
+                                  (uint32_t)x[2][e] | ((uint32_t)x[3][e] << 16));
+      *reinterpret_cast<uint2*>(vt + v16_lds_row(row) * 32 + quad * 8) = w2;
+    }
+  }
+  __syncthreads();
+  uint8_t* dst = vout + (bh * (size_t)(Npad / 16) + (size_t)kb * (BK / 16)) * D * 32;
+  for (int ch = tid; ch < BK * D * 2 / 16; ch += 256) {
+    const int row = ch >> 1;
+    *reinterpret_cast<uint4*>(dst + ch * 16) =
+        *reinterpret_cast<const uint4*>(vt + v16_lds_row(row) * 32 + (ch & 1) * 16);
   }
 }
 
@@ -140,9 +191,10 @@ __global__ __launch_bounds__(256) void kv_stats(const __half* __restrict__ k, co
 // grid (nkb, B*Hkv), 256 threads.
 // K group: keys 8a + 4h + r of the block share the scale of lane half h (one scale per
 // lane of the 32x32 integer MFMA accumulator that holds those keys).
-// V codes are written transposed per 64-key group in the FP8 MFMA k-slot order.
+// V codes are written transposed per 64-key group in the FP8 MFMA k-slot order; with PV16
+// V itself (fp16) is written transposed per 16-key group in the fp16 MFMA k-slot order.
 // ---------------------------------------------------------------------------------------
-template <int D>
+template <int D, bool PV16>
 __global__ __launch_bounds__(256) void kv_quant(const __half* __restrict__ k, const __half* __restrict__ v,
                                                 const unsigned long long* __restrict__ ksum,
                                                 const unsigned int* __restrict__ vamax,
@@ -152,7 +204,7 @@ __global__ __launch_bounds__(256) void kv_quant(const __half* __restrict__ k, co
   constexpr int TPR = D / 8, RPP = 256 / TPR, PASSES = BK / RPP;
   static_assert(RPP % 8 == 0, "a thread's rows must share (row % 8)");
   __shared__ float red[WAVES][2];
-  __shared__ __attribute__((aligned(16))) uint8_t vt[2 * D * VGROUP];
+  __shared__ __attribute__((aligned(16))) uint8_t vt[BK * D * (PV16 ? 2 : 1)];
   const int tid = threadIdx.x, cq = tid % TPR, r0 = tid / TPR, lane = tid % 64, w = tid / 64;
   const int kb = blockIdx.x;
   const size_t bh = blockIdx.y;
@@ -165,11 +217,11 @@ __global__ __launch_bounds__(256) void kv_quant(const __half* __restrict__ k, co
     const int c = cq * 8 + e;
     const long long S = (long long)ksum[bh * D + c];
     mu[e] = (float)((double)S / ((double)N * 16777216.0));
-    const float va = __uint_as_float(vamax[bh * D + c]);
+    const float va = PV16 ? 0.f : __uint_as_float(vamax[bh * D + c]);
     vinv[e] = va > 0.f ? V_RANGE / va : 0.f;
     if (kb == 0 && r0 == 0) {
       muk_out[bh * D + c] = mu[e];
-      vscale[bh * D + c] = va / V_RANGE;
+      if (!PV16) vscale[bh * D + c] = va / V_RANGE;
     }
   }
 
@@ -212,6 +264,11 @@ __global__ __launch_bounds__(256) void kv_quant(const __half* __restrict__ k, co
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] = fminf(fmaxf(rintf(g[p][e] * inv), -R), R);
     store_codes(kcodes + (bh * Npad + row) * D, cq, x, R < 8.f);
+  }
+
+  if (PV16) {
+    store_v16<D>(vbase, vt, vcodes, bh, kb, N, Npad, tid, cq, r0);
+    return;
   }
 
   // V: per-channel FP8, transposed into [group u][channel][slot] in LDS, then streamed out.
@@ -654,9 +711,16 @@ hipError_t launch_prologue_d(const Dims& Dm, const Ptrs& P, hipStream_t s) {
   const float R = Dm.qk_bits == 4 ? 7.f : 127.f;
   const int nkv = Dm.B * Dm.Hkv * D;
   init_stats<<<(nkv + 255) / 256, 256, 0, s>>>(P.ksum, P.vamax, nkv);
-  kv_stats<D><<<dim3((Dm.N + 255) / 256, Dm.B * Dm.Hkv), 256, 0, s>>>(P.k, P.v, P.ksum, P.vamax, Dm.N);
-  kv_quant<D><<<dim3(Dm.nkb, Dm.B * Dm.Hkv), 256, 0, s>>>(P.k, P.v, P.ksum, P.vamax, P.kcodes, P.vcodes,
-                                                          P.kscale, P.muk, P.vscale, Dm.N, Dm.Npad, Dm.nkb, R);
+  const dim3 gs((Dm.N + 255) / 256, Dm.B * Dm.Hkv), gq(Dm.nkb, Dm.B * Dm.Hkv);
+  if (Dm.pv_bits == 16) {
+    kv_stats<D, false><<<gs, 256, 0, s>>>(P.k, P.v, P.ksum, P.vamax, Dm.N);
+    kv_quant<D, true><<<gq, 256, 0, s>>>(P.k, P.v, P.ksum, P.vamax, P.kcodes, P.vcodes, P.kscale, P.muk,
+                                         P.vscale, Dm.N, Dm.Npad, Dm.nkb, R);
+  } else {
+    kv_stats<D, true><<<gs, 256, 0, s>>>(P.k, P.v, P.ksum, P.vamax, Dm.N);
+    kv_quant<D, false><<<gq, 256, 0, s>>>(P.k, P.v, P.ksum, P.vamax, P.kcodes, P.vcodes, P.kscale, P.muk,
+                                          P.vscale, Dm.N, Dm.Npad, Dm.nkb, R);
+  }
   q_quant<D><<<dim3(Dm.nqb, Dm.B * Dm.H), 256, 0, s>>>(P.q, P.qcodes, P.qscale, P.muq, P.muqs, Dm.N, Dm.Npad,
                                                          Dm.nqb, R);
   const float k2 = (float)(1.4426950408889634 / sqrt((double)D));
@@ -692,7 +756,8 @@ hipError_t launch_debug_copy(const Dims& D, const Ptrs& P, hipStream_t s, float*
     hipError_t e = hipMemcpyAsync(mu_k, P.muk, (size_t)hkv * D.d * 4, hipMemcpyDeviceToDevice, s);
     if (e != hipSuccess) return e;
   }
-  if (v_scales) {
+  const bool pv8 = D.pv_bits == 8;     // fp16 V has no codes or scales to copy
+  if (v_scales && pv8) {
     hipError_t e = hipMemcpyAsync(v_scales, P.vscale, (size_t)hkv * D.d * 4, hipMemcpyDeviceToDevice, s);
     if (e != hipSuccess) return e;
   }
@@ -705,7 +770,7 @@ hipError_t launch_debug_copy(const Dims& D, const Ptrs& P, hipStream_t s, float*
   if (q_codes) copy_rows_i8<<<grid, blk, 0, s>>>(P.qcodes, q_codes, hq, D.N, D.Npad, D.d, fp6);
   if (k_scales) expand_kscale<<<grid, blk, 0, s>>>(P.kscale, k_scales, hkv, D.N, D.nkb);
   if (q_scales) copy_rows_f32<<<grid, blk, 0, s>>>(P.qscale, q_scales, (size_t)hq, D.N, D.Npad, 1.f);
-  if (v_codes) unpermute_v<<<grid, blk, 0, s>>>(P.vcodes, v_codes, hkv, D.N, D.Npad, D.d);
+  if (v_codes && pv8) unpermute_v<<<grid, blk, 0, s>>>(P.vcodes, v_codes, hkv, D.N, D.Npad, D.d);
   if (delta_s_out) {
     const float inv_k2 = (float)(sqrt((double)D.d) / 1.4426950408889634);
     copy_ds<<<grid, blk, 0, s>>>(P.ds, delta_s_out, hq, D.nqb, D.N, D.Npad, D.causal != 0, inv_k2);

@@ -20,7 +20,7 @@ constexpr size_t WS_ALIGN = 256;
 
 // ---- problem description ----
 struct Dims {
-  int B, H, Hkv, N, d, causal, qk_bits;
+  int B, H, Hkv, N, d, causal, qk_bits, pv_bits;
   int Npad;   // N rounded up to a multiple of 128 (= BQ = BK)
   int nqb;    // query blocks
   int nkb;    // KV blocks
@@ -29,10 +29,13 @@ struct Dims {
 // ---- workspace carve-up (byte offsets, all WS_ALIGN aligned) ----
 //  kcodes : int8  [B][Hkv][Npad][d]           smoothed+quantized K, zero past N (INT4 range:
 //                                             packed FP6 E2M3, 24 of every 32 bytes)
-//  vcodes : uint8 [B][Hkv][Npad/64][d][64]    FP8 V, transposed per 64-key group; inside a
-//           group the byte at position 32*h + b of channel row c holds key
+//  vcodes : pv_bits 8:  uint8 [B][Hkv][Npad/64][d][64]  FP8 V, transposed per 64-key group;
+//           inside a group the byte at position 32*h + b of channel row c holds key
 //           32*(b/16) + 8*((b%16)/4) + 4*h + (b%4): the k-slot order of the FP8 MFMA
 //           B operand built from the S^T accumulators (see attention kernel)
+//           pv_bits 16: fp16 [B][Hkv][Npad/16][d][16]  V itself, transposed per 16-key group;
+//           slot 8*((kk/4)%2) + 4*(kk/8) + kk%4 holds key kk of the group: the k-slot order of
+//           the fp16 MFMA B operand built from the S^T accumulators
 //  qcodes : int8  [B][H][Npad][d]              (INT4 range: packed FP6 E2M3, as kcodes)
 //  kscale : fp32  [B][Hkv][nkb][2]            delta_K per (KV block, lane half)
 //  qscale : fp32  [B][H][Npad]                delta_Q per query row
@@ -70,7 +73,7 @@ inline Layout make_layout(const Dims& D) {
   auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
   const size_t B = D.B, H = D.H, Hkv = D.Hkv, Np = D.Npad, d = D.d;
   L.kcodes = take(B * Hkv * Np * d);
-  L.vcodes = take(B * Hkv * Np * d);
+  L.vcodes = take(B * Hkv * Np * d * (D.pv_bits / 8));
   L.qcodes = take(B * H * Np * d);
   L.kscale = take(B * Hkv * (size_t)D.nkb * 2 * 4);
   L.qscale = take(B * H * Np * 4);

@@ -58,6 +58,8 @@ def test_config_matches_oracle_geometry(pkg):
 def test_workspace_bytes(pkg):
     n1 = pkg.workspace_bytes(1, 2, 2, 256, 64, False, 8)
     assert n1 > 0 and n1 % 256 == 0
+    # fp16 V (pv_bits = 16) takes one more byte per V element than its FP8 codes
+    assert pkg.workspace_bytes(1, 2, 2, 256, 64, False, 8, 16) >= n1 + 2 * 256 * 64
     # codes (K, V, Q) + Delta_S dominate: 3 * 256*64*2 + 2*2*256*4 bytes at least
     assert n1 >= 3 * 256 * 64 * 2 + 2 * 2 * 256 * 4
     assert pkg.workspace_bytes(1, 2, 2, 257, 64, False, 8) > n1           # one more 128-row block
@@ -67,13 +69,15 @@ def test_workspace_bytes(pkg):
 
 
 @pytest.mark.parametrize("args,status", [
-    ((0, 2, 2, 256, 64, 0, 8), -1),       # B < 1
-    ((1, 3, 2, 256, 64, 0, 8), -1),       # H % Hkv
-    ((1, 2, 2, 0, 64, 0, 8), -1),         # N < 1
-    ((1, 2, 2, 256, 64, 2, 8), -1),       # causal not 0/1
-    ((1, 2, 2, 256, 96, 0, 8), -2),       # d
-    ((1, 2, 2, 256, 64, 0, 6), -2),       # qk_bits
-    ((1, 2, 2, (1 << 23) + 1, 64, 0, 8), -2),   # N beyond the exact-sum bound
+    ((0, 2, 2, 256, 64, 0, 8, 8), -1),    # B < 1
+    ((1, 3, 2, 256, 64, 0, 8, 8), -1),    # H % Hkv
+    ((1, 2, 2, 0, 64, 0, 8, 8), -1),      # N < 1
+    ((1, 2, 2, 256, 64, 2, 8, 8), -1),    # causal not 0/1
+    ((1, 2, 2, 256, 96, 0, 8, 8), -2),    # d
+    ((1, 2, 2, 256, 64, 0, 6, 8), -2),    # qk_bits
+    ((1, 2, 2, 256, 64, 0, 8, 4), -2),    # pv_bits
+    ((1, 2, 2, 256, 64, 0, 8, 32), -2),   # pv_bits
+    ((1, 2, 2, (1 << 23) + 1, 64, 0, 8, 8), -2),   # N beyond the exact-sum bound
 ])
 def test_validation_errors(pkg, args, status):
     lib = pkg._lib
@@ -86,7 +90,7 @@ def test_validation_errors(pkg, args, status):
 def test_null_and_workspace_errors(pkg):
     lib = pkg._lib
     fake = ctypes.c_void_p(0x1000)
-    dims = (1, 2, 2, 256, 64, 0, 8)
+    dims = (1, 2, 2, 256, 64, 0, 8, 8)
     need = pkg.workspace_bytes(*dims)
     ws = ctypes.c_void_p(0x100000)
     assert lib.sage_attn_fwd(None, fake, fake, fake, *dims, ws, need, None) == -1
@@ -98,6 +102,13 @@ def test_null_and_workspace_errors(pkg):
     assert lib.sage_qk_tile_debug(fake, fake, fake, *dims, ws, need, None, 1, 0, 0, 0, fake) == -1   # b
     assert lib.sage_qk_tile_debug(fake, fake, fake, *dims, ws, need, None, 0, 0, 0, 0, None) == -1
     assert lib.sage_quant_debug(fake, None, fake, *dims, ws, need, None, *([None] * 9)) == -1
+    # no V codes or scales exist when V stays fp16
+    dims16 = dims[:-1] + (16,)
+    need16 = pkg.workspace_bytes(*dims16)
+    for i in (3, 4):
+        outs = [None] * 9
+        outs[i] = fake
+        assert lib.sage_quant_debug(fake, fake, fake, *dims16, ws, need16, None, *outs) == -1
     assert lib.sage_get_config(None) == -1
 
 

@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the SageAttention2 quantized attention forward on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload bench|llm|dit|gqa|tiny] [--pv-bits 8|16]
+    python bench.py [--steps K] [--warmup W] [--workload bench|llm|dit|gqa|tiny|varlen] [--pv-bits 8|16]
 
 A step is one whole forward pass (quantize/smooth prologue + fused attention kernel) over the
 workload's seeded synthetic inputs, which are resident in HBM before the timed region.  The
@@ -52,7 +52,8 @@ ATTN_SRC = os.path.join(ROOT, "quantized_attention_smooth_amd", "csrc", "attenti
 def _describe(w, pv_bits: int) -> str:
     kind = "causal" if w.causal else "non-causal"
     heads = f"H{w.H}" if w.H == w.Hkv else f"H{w.H}/Hkv{w.Hkv}"
-    return (f"{w.name}: B{w.B} {heads} N{w.N} d{w.d} {kind}, "
+    size = f"{w.B} sequences of {min(w.lens)}-{w.N} tokens (T={w.T})" if hasattr(w, "lens") else f"B{w.B} N{w.N}"
+    return (f"{w.name}: {size} {heads} d{w.d} {kind}, "
             f"{'INT8' if w.qk_bits == 8 else 'INT4-range'} QK + {'FP8' if pv_bits == 8 else 'fp16'} PV")
 
 
@@ -73,10 +74,11 @@ def _traffic(workload: str, pv_bits: int):
     return (e["fetch_kib"] * t["fetch_factor"] + e["write_kib"] * t["write_factor"]) * 1024.0
 
 
-def cpu_baseline(w, q, k, v, budget_s: float, pv_bits: int = 8) -> dict:
-    """The oracle as it stands, on one (b, h) head: its full prologue plus as many query blocks
-    as fit the budget (spread over the sequence), extrapolated to the workload by block cost
-    (causal block qb costs qb + 1 key blocks)."""
+def cpu_baseline(w, q1, k1, v1, budget_s: float, pv_bits: int = 8, head_ops: float | None = None) -> dict:
+    """The oracle as it stands, on one head of one sequence (q1, k1, v1: [1, 1, n, d]): its full
+    prologue plus as many query blocks as fit the budget (spread over the sequence),
+    extrapolated by block cost (causal block qb costs qb + 1 key blocks) to that head, then to
+    the workload by the ratio of their ops (head_ops: the sampled head's share)."""
     import numpy as np
     from oracle import sage as osage
     try:
@@ -84,10 +86,6 @@ def cpu_baseline(w, q, k, v, budget_s: float, pv_bits: int = 8) -> dict:
         blas = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:  # pragma: no cover - reporting only
         blas = 1
-    hk = 0
-    q1 = np.ascontiguousarray(q[:1, :1])
-    k1 = np.ascontiguousarray(k[:1, hk:hk + 1])
-    v1 = np.ascontiguousarray(v[:1, hk:hk + 1])
     t0 = time.perf_counter()
     pro = osage.prologue(q1, k1, v1, w.causal, w.qk_bits, quant_pv=pv_bits == 8)
     t_pro = time.perf_counter() - t0
@@ -109,12 +107,13 @@ def cpu_baseline(w, q, k, v, budget_s: float, pv_bits: int = 8) -> dict:
             break
     per_unit = t_att / done_cost
     t_head = t_pro + per_unit * sum(cost)
-    t_total = t_head * w.B * w.H
+    t_total = t_head * w.ops / head_ops
     value = w.ops / t_total / 1e12
     return {
         "value": value, "unit": "TOPS", "cores": int(blas), "kind": "oracle",
-        "sample": (f"numpy oracle on head (b0,h0): full prologue ({t_pro:.1f} s) + {nblk} of {nqb} query "
-                   f"blocks ({t_att:.1f} s), extrapolated by block cost to {w.B * w.H} heads "
+        "sample": (f"numpy oracle on one head ({pro.N} tokens): full prologue ({t_pro:.1f} s) + {nblk} of {nqb} "
+                   f"query blocks ({t_att:.1f} s), extrapolated by block cost to the head and by ops to the "
+                   f"workload "
                    f"(est. {t_total:.0f} s for the workload); BLAS threads {blas}, elementwise 1 thread"),
     }
 
@@ -160,23 +159,28 @@ def main() -> int:
         return 0
 
     import quantized_attention_smooth_amd as sa
-    from workloads import WORKLOADS, make_inputs
+    from workloads import VARLEN_WORKLOADS, WORKLOADS, make_inputs, make_varlen_inputs
 
-    w = WORKLOADS[args.workload]
-    q, k, v = make_inputs(w, seed=0)
+    pv = args.pv_bits
+    varlen = args.workload in VARLEN_WORKLOADS
+    if varlen:
+        w = VARLEN_WORKLOADS[args.workload]
+        q, k, v = make_varlen_inputs(w, seed=0)
+        pb = sa.Problem(w.B, w.H, w.Hkv, 0, w.d, w.causal, w.qk_bits, pv, "HND", cu_seqlens=w.cu_seqlens)
+    else:
+        w = WORKLOADS[args.workload]
+        q, k, v = make_inputs(w, seed=0)
+        pb = sa.Problem(w.B, w.H, w.Hkv, w.N, w.d, w.causal, w.qk_bits, pv, "HND")
     dev = torch.device("cuda:0")
     qd = torch.from_numpy(q).to(dev)
     kd = torch.from_numpy(k).to(dev)
     vd = torch.from_numpy(v).to(dev)
     o = torch.empty_like(qd)
-    pv = args.pv_bits
-    nbytes = sa.workspace_bytes(w.B, w.H, w.Hkv, w.N, w.d, w.causal, w.qk_bits, pv)
-    ws = sa.alloc_workspace(nbytes, dev)
-    shape = (w.B, w.H, w.N, w.d)
+    ws = sa.alloc_workspace(sa.problem_ws_bytes(pb), dev)
 
     def step():
-        sa.prologue(qd, kd, vd, ws, w.causal, w.qk_bits, pv)
-        sa.attend(o, ws, shape, w.Hkv, w.causal, w.qk_bits, pv)
+        sa.prologue_ex(pb, qd, kd, vd, ws)
+        sa.attend_ex(pb, o, ws)
 
     for _ in range(args.warmup):
         step()
@@ -193,9 +197,9 @@ def main() -> int:
     e_start.record()
     for s in range(K):
         ev[s][0].record()
-        sa.prologue(qd, kd, vd, ws, w.causal, w.qk_bits, pv)
+        sa.prologue_ex(pb, qd, kd, vd, ws)
         ev[s][1].record()
-        sa.attend(o, ws, shape, w.Hkv, w.causal, w.qk_bits, pv)
+        sa.attend_ex(pb, o, ws)
         ev[s][2].record()
     e_end.record()
     torch.cuda.synchronize()
@@ -207,12 +211,15 @@ def main() -> int:
     ops = w.ops
     value = ops / (ms_step * 1e-3) / 1e12
     achieved = ops / (att_ms * 1e-3) / 1e12
-    nqb = -(-w.N // 128)
-    npad = nqb * 128
-    n_q, n_kv = w.B * w.H * w.N * w.d, w.B * w.Hkv * w.N * w.d
-    ds_elems = 128 * nqb * (nqb + 1) // 2 if w.causal else nqb * npad     # Delta_S rows per head
+    lens = w.lens if varlen else [w.N] * w.B
+    tokens = sum(lens)
+    n_q, n_kv = tokens * w.H * w.d, tokens * w.Hkv * w.d
+    ds_elems = 0                                                          # Delta_S rows, all heads
+    for n in lens:
+        nqb = -(-n // 128)
+        ds_elems += w.H * (128 * nqb * (nqb + 1) // 2 if w.causal else nqb * nqb * 128)
     # read q, k, v once (fp16); write Q/K codes (1 byte), V as FP8 codes or fp16, Delta_S rows
-    pro_bytes = 2 * (n_q + 2 * n_kv) + (n_q + n_kv) + n_kv * (pv // 8) + 4 * w.B * w.H * ds_elems
+    pro_bytes = 2 * (n_q + 2 * n_kv) + (n_q + n_kv) + n_kv * (pv // 8) + 4 * ds_elems
     traffic = _traffic(args.workload, pv)
     peak = attn_peak(w.qk_bits, pv)
     qk_t = "int8" if w.qk_bits == 8 else "fp6 (INT4-range codes)"
@@ -224,7 +231,8 @@ def main() -> int:
         "dtype": ("i8" if w.qk_bits == 8 else "fp6e2m3") + ("+fp8e4m3" if pv == 8 else "+fp16"),
         "data": "synthetic",
         "config": {"workload": _describe(w, pv), "B": w.B, "H": w.H, "Hkv": w.Hkv, "N": w.N, "d": w.d,
-                   "causal": w.causal, "qk_bits": w.qk_bits, "pv_bits": pv, "seed": 0},
+                   "causal": w.causal, "qk_bits": w.qk_bits, "pv_bits": pv, "seed": 0,
+                   **({"cu_seqlens": w.cu_seqlens} if varlen else {})},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                      "frac": achieved / peak, "traffic": traffic,
                      "kernel": f"attn_fwd (fused QK^T {qk_t} MFMA + softmax + {pv_t} MFMA)",
@@ -236,7 +244,16 @@ def main() -> int:
                       "wall_s_timed": wall},
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_budget, pv)
+        if varlen:                      # one head of the longest sequence
+            s = int(np.argmax(w.lens))
+            a, b = w.cu_seqlens[s], w.cu_seqlens[s + 1]
+            q1, k1, v1 = (np.ascontiguousarray(x[a:b, :1].transpose(1, 0, 2))[None] for x in (q, k, v))
+            n = b - a
+        else:                           # head (0, 0)
+            q1, k1, v1 = (np.ascontiguousarray(x[:1, :1]) for x in (q, k, v))
+            n = w.N
+        head_ops = 4.0 * n * n * w.d / (2 if w.causal else 1)
+        line["cpu_baseline"] = cpu_baseline(w, q1, k1, v1, args.cpu_budget, pv, head_ops)
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)

@@ -13,7 +13,10 @@
  *           core API call and precision control: the method is a drop-in for PyTorch's
  *           scaled_dot_product_attention selected by a head_dim / is_causal / quant mode;
  *           the quant modes "qk_int8_pv_fp8" (fast) and "qk_int8_pv_fp16" (high fidelity:
- *           V kept in fp16) select the P~V precision.
+ *           V kept in fp16) select the P~V precision.  Its feature section on adapting
+ *           generation models names automatic tensor-layout conversion for the models'
+ *           attention interfaces, and its precision-control section a causal variable-length
+ *           (varlen) kernel for batches whose sequence lengths differ.
  *
  * What the library computes: O = softmax(Q K^T / sqrt(d)) V, approximated as in [SA2]:
  * K is smoothed by its per-channel mean over tokens, Q by its per-block mean with the
@@ -56,7 +59,8 @@ extern "C" {
 #endif
 
 #define SAGE_OK 0
-#define SAGE_ERR_INVALID_ARG (-1) /* null pointer, size < 1, H % Hkv != 0, size overflow  */
+#define SAGE_ERR_INVALID_ARG (-1) /* null pointer, size < 1, H % Hkv != 0, size overflow,
+                                     bad layout/dtype code, cu_seqlens not from 0 upwards  */
 #define SAGE_ERR_UNSUPPORTED (-2) /* d not in {64, 128}, qk_bits not in {4, 8},
                                      pv_bits not in {8, 16}, N > 2^23                       */
 #define SAGE_ERR_WORKSPACE (-3)   /* workspace missing, too small or not 256-byte aligned */
@@ -85,6 +89,50 @@ typedef struct sage_config {
 } sage_config_t;
 
 int sage_get_config(sage_config_t* out);
+
+/*
+ * Extended problem description ([BLOG] layout conversion and varlen batches).
+ *
+ *   layout  SAGE_LAYOUT_HND: q, o [B, H, N, d]; k, v [B, Hkv, N, d]  (as sage_attn_fwd)
+ *           SAGE_LAYOUT_NHD: q, o [B, N, H, d]; k, v [B, N, Hkv, d]  (token-major)
+ *   cu_seqlens  NULL: B sequences of N tokens each, in `layout`.
+ *           Otherwise a varlen batch: a HOST int32 array of B + 1 entries with
+ *           cu_seqlens[0] = 0 and cu_seqlens[s] < cu_seqlens[s + 1]; sequence s holds tokens
+ *           cu_seqlens[s] .. cu_seqlens[s + 1] - 1 of packed tensors q, o [T, H, d] and
+ *           k, v [T, Hkv, d], T = cu_seqlens[B] (N and layout are ignored).  Each sequence is
+ *           attended on its own (queries see only keys of the same sequence; causal is
+ *           top-left aligned within it) and has its own smoothing means and quantization
+ *           groups, exactly as if it were a batch of one.  The array is read during the
+ *           call only.  Sequence lengths are at most 2^23.
+ *   dtype   SAGE_DTYPE_FP16 (q, k, v and o fp16).  SAGE_DTYPE_BF16 is reserved and
+ *           returns SAGE_ERR_UNSUPPORTED.
+ * Every tensor is contiguous in its stated shape.  All other fields as for sage_attn_fwd.
+ */
+#define SAGE_LAYOUT_HND 0
+#define SAGE_LAYOUT_NHD 1
+#define SAGE_DTYPE_FP16 0
+#define SAGE_DTYPE_BF16 1
+
+typedef struct {
+  int B;                  /* batch size, or number of sequences when cu_seqlens != NULL */
+  int H, Hkv, N, d;
+  int causal, qk_bits, pv_bits;
+  int layout;             /* SAGE_LAYOUT_* */
+  int dtype;              /* SAGE_DTYPE_* */
+  const int* cu_seqlens;  /* host int32 [B + 1] or NULL */
+} sage_problem_t;
+
+/* Workspace bytes for *p (written to *bytes); the _ex calls below take at least this much. */
+int sage_attn_workspace_bytes_ex(const sage_problem_t* p, size_t* bytes);
+
+/* sage_attn_fwd / sage_attn_prologue / sage_attn_attend for any problem *p (same error and
+ * stream rules).  The prologue and attend halves must be given the same *p and workspace. */
+int sage_attn_fwd_ex(const sage_problem_t* p, const void* q, const void* k, const void* v,
+                     void* o, void* workspace, size_t workspace_bytes, void* stream);
+int sage_attn_prologue_ex(const sage_problem_t* p, const void* q, const void* k, const void* v,
+                          void* workspace, size_t workspace_bytes, void* stream);
+int sage_attn_attend_ex(const sage_problem_t* p, void* o, void* workspace,
+                        size_t workspace_bytes, void* stream);
 
 /* Bytes of workspace sage_attn_fwd needs for this problem (written to *bytes). */
 int sage_attn_workspace_bytes(int B, int H, int Hkv, int N, int d, int causal, int qk_bits,

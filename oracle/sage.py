@@ -361,6 +361,52 @@ def attend_block(pro: Prologue, b: int, h: int, qb: int, return_state: bool = Fa
     return out
 
 
+def fp8_midpoint_slack(pro: Prologue, b: int, h: int, qb: int, rel: float = 2.0 ** -14) -> np.ndarray:
+    """How far O of Q block qb may move when P~ decisions that sit on an E4M3 rounding midpoint go
+    the other way: fp64 [rows, d].
+
+    Reading: a P~ element whose p * P_r lies within `rel` (relative) of the midpoint between two
+    E4M3 values has two correct codes -- a computation of the logits in fp32 (any faithful one,
+    as on the GPU) may land on either side.  Both results are outputs of the method, so a parity
+    check accepts either: each such element may change its row's output in channel c by at most
+    (the gap between the two codes) * |V_q[j, c]| * delta_V[c] / (P_r * l), later rescalings being
+    factors <= 1.  Zero where no decision is ambiguous (almost everywhere).
+    """
+    g = pro.geom
+    hk = pro.kv_head(h)
+    z = logits(pro, b, h, qb)
+    rows = z.shape[0]
+    vals = np.unique(fp8.decode(np.arange(256, dtype=np.uint8)))
+    vals = vals[np.isfinite(vals) & (vals >= 0)]
+    mids = (vals[1:] + vals[:-1]) / 2.0
+    gaps = vals[1:] - vals[:-1]
+    vmag = np.abs(fp8.decode(pro.v_codes[b, hk])) * pro.v_delta[b, hk].astype(F64)[None, :]
+    p_r = F64(g.p_range)
+    m = np.full(rows, -np.inf)
+    l = np.zeros(rows)
+    slack = np.zeros((rows, pro.d))
+    for kb in range(pro.nkb):
+        c0, c1 = kb * g.bk, min(pro.N, (kb + 1) * g.bk)
+        zb = z[:, c0:c1]
+        m_new = np.maximum(m, zb.max(axis=1))
+        finite = np.isfinite(m_new)
+        alpha = np.where(np.isfinite(m), np.exp(m - np.where(finite, m_new, 0.0)), 0.0)
+        p = np.where(finite[:, None], np.exp(zb - np.where(finite, m_new, 0.0)[:, None]), 0.0)
+        l = l * alpha + p.sum(axis=1)
+        x = p * p_r
+        i = np.clip(np.searchsorted(mids, x), 0, len(mids) - 1)
+        near = np.zeros(x.shape, bool)
+        gap = np.zeros(x.shape)
+        for j in (i - 1, i):                            # the two closest midpoints
+            jj = np.clip(j, 0, len(mids) - 1)
+            hit = np.abs(x - mids[jj]) <= rel * np.maximum(x, mids[jj])
+            gap = np.where(hit, np.maximum(gap, gaps[jj]), gap)
+            near |= hit
+        slack += (np.where(near, gap, 0.0)) @ vmag[c0:c1]
+        m = m_new
+    return slack / (p_r * np.where(l > 0, l, 1.0))[:, None]
+
+
 def sage_attention(q, k, v, causal: bool = False, qk_bits: int = 8, geom: Geometry = DEFAULT,
                    **switches) -> np.ndarray:
     """Whole forward pass: fp64 O [B, H, N, d] (the GPU rounds it to fp16)."""
@@ -371,6 +417,28 @@ def sage_attention(q, k, v, causal: bool = False, qk_bits: int = 8, geom: Geomet
             for qb in range(pro.nqb):
                 r0, r1 = qb * geom.bq, min(pro.N, (qb + 1) * geom.bq)
                 out[b, h, r0:r1] = attend_block(pro, b, h, qb)
+    return out
+
+
+def sage_attention_varlen(q, k, v, cu_seqlens, causal: bool = False, qk_bits: int = 8,
+                          geom: Geometry = DEFAULT, **switches) -> np.ndarray:
+    """Variable-length batch (the blog page's precision-control tip on varlen inputs): q [T, H, d],
+    k/v [T, Hkv, d] hold the sequences back to back, sequence s being rows cu[s] .. cu[s+1]-1.
+
+    Reading (the page names the feature, not its arithmetic): each sequence is one batch entry
+    of its own -- its keys alone are attended, smoothed (mu_K over its tokens, mu_Q per 128-row
+    block from its first row) and grouped -- so the result is the fixed-length forward pass on
+    each slice.  Returns fp64 [T, H, d].
+    """
+    q = np.asarray(q)
+    k = np.asarray(k)
+    v = np.asarray(v)
+    cu = [int(x) for x in cu_seqlens]
+    out = np.zeros(q.shape)
+    for s in range(len(cu) - 1):
+        a, b = cu[s], cu[s + 1]
+        qs, ks, vs = (np.ascontiguousarray(x[a:b].transpose(1, 0, 2))[None] for x in (q, k, v))
+        out[a:b] = sage_attention(qs, ks, vs, causal, qk_bits, geom, **switches)[0].transpose(1, 0, 2)
     return out
 
 

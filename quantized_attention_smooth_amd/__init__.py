@@ -8,6 +8,8 @@ library is missing or fails to load, importing this package raises ImportError.
 
     from quantized_attention_smooth_amd import sageattn
     o = sageattn(q, k, v, is_causal=True, qk_bits=8, pv_bits=8)   # like F.scaled_dot_product_attention
+    o = sageattn(q, k, v, tensor_layout="NHD")                     # q [B, N, H, d]
+    o = sageattn_varlen(q, k, v, cu_seqlens, is_causal=True)       # packed q [T, H, d]
 """
 from __future__ import annotations
 
@@ -16,8 +18,8 @@ import os
 
 import torch
 
-__all__ = ["sageattn", "fwd", "prologue", "attend", "workspace_bytes", "get_config", "quant_debug", "qk_tile_debug",
-           "LIB_PATH", "SageError"]
+__all__ = ["sageattn", "sageattn_varlen", "fwd", "prologue", "attend", "workspace_bytes", "get_config",
+           "quant_debug", "qk_tile_debug", "Problem", "LIB_PATH", "SageError"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsage_mi355x.so")
 
@@ -30,7 +32,11 @@ SAGE_ERR_HIP = -4
 #: every symbol include/sage_attn.h declares
 EXPORTS = ("sage_get_config", "sage_attn_workspace_bytes", "sage_attn_fwd", "sage_attn_prologue",
            "sage_attn_attend", "sage_quant_debug", "sage_qk_tile_debug", "sage_status_string",
-           "sage_last_error")
+           "sage_last_error", "sage_attn_workspace_bytes_ex", "sage_attn_fwd_ex", "sage_attn_prologue_ex",
+           "sage_attn_attend_ex")
+
+LAYOUTS = {"HND": 0, "NHD": 1}
+DTYPES = {torch.float16: 0, torch.bfloat16: 1}
 
 
 class SageConfig(ctypes.Structure):
@@ -38,6 +44,36 @@ class SageConfig(ctypes.Structure):
                 ("q_slice", ctypes.c_int), ("q_period", ctypes.c_int), ("q_run", ctypes.c_int),
                 ("k_slice", ctypes.c_int), ("k_period", ctypes.c_int), ("k_run", ctypes.c_int),
                 ("p_range", ctypes.c_float), ("v_range", ctypes.c_float), ("fp8_format", ctypes.c_int)]
+
+
+class SageProblem(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int), ("H", ctypes.c_int), ("Hkv", ctypes.c_int), ("N", ctypes.c_int),
+                ("d", ctypes.c_int), ("causal", ctypes.c_int), ("qk_bits", ctypes.c_int), ("pv_bits", ctypes.c_int),
+                ("layout", ctypes.c_int), ("dtype", ctypes.c_int), ("cu_seqlens", ctypes.POINTER(ctypes.c_int))]
+
+
+class Problem:
+    """sage_problem_t plus the host cu_seqlens array it points to (kept alive here)."""
+
+    def __init__(self, B, H, Hkv, N, d, causal=False, qk_bits=8, pv_bits=8, layout="HND", dtype=torch.float16,
+                 cu_seqlens=None):
+        self._cu = None
+        cu_ptr = None
+        if cu_seqlens is not None:
+            vals = [int(x) for x in (cu_seqlens.tolist() if hasattr(cu_seqlens, "tolist") else cu_seqlens)]
+            self._cu = (ctypes.c_int * len(vals))(*vals)
+            cu_ptr = ctypes.cast(self._cu, ctypes.POINTER(ctypes.c_int))
+            if len(vals) != B + 1:
+                raise ValueError(f"cu_seqlens needs B + 1 = {B + 1} entries, got {len(vals)}")
+        if layout not in LAYOUTS:
+            raise ValueError(f"tensor_layout must be one of {sorted(LAYOUTS)}")
+        if dtype not in DTYPES:
+            raise ValueError("dtype must be torch.float16 or torch.bfloat16")
+        self.c = SageProblem(B, H, Hkv, N, d, int(causal), qk_bits, pv_bits, LAYOUTS[layout], DTYPES[dtype], cu_ptr)
+
+    @property
+    def ref(self):
+        return ctypes.byref(self.c)
 
 
 class SageError(RuntimeError):
@@ -61,12 +97,18 @@ def _load() -> ctypes.CDLL:
     lib.sage_attn_attend.argtypes = [P, I, I, I, I, I, I, I, I, P, S, P]
     lib.sage_quant_debug.argtypes = [P, P, P, I, I, I, I, I, I, I, I, P, S, P] + [P] * 9
     lib.sage_qk_tile_debug.argtypes = [P, P, P, I, I, I, I, I, I, I, I, P, S, P, I, I, I, I, P]
+    PP = ctypes.POINTER(SageProblem)
+    lib.sage_attn_workspace_bytes_ex.argtypes = [PP, ctypes.POINTER(S)]
+    lib.sage_attn_fwd_ex.argtypes = [PP, P, P, P, P, P, S, P]
+    lib.sage_attn_prologue_ex.argtypes = [PP, P, P, P, P, S, P]
+    lib.sage_attn_attend_ex.argtypes = [PP, P, P, S, P]
     lib.sage_status_string.argtypes = [I]
     lib.sage_status_string.restype = ctypes.c_char_p
     lib.sage_last_error.argtypes = []
     lib.sage_last_error.restype = ctypes.c_char_p
     for name in ("sage_get_config", "sage_attn_workspace_bytes", "sage_attn_fwd", "sage_attn_prologue",
-                 "sage_attn_attend", "sage_quant_debug", "sage_qk_tile_debug"):
+                 "sage_attn_attend", "sage_quant_debug", "sage_qk_tile_debug", "sage_attn_workspace_bytes_ex",
+                 "sage_attn_fwd_ex", "sage_attn_prologue_ex", "sage_attn_attend_ex"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -155,23 +197,97 @@ def attend(o, workspace, shape, Hkv: int, is_causal: bool = False, qk_bits: int 
                                  workspace.numel(), _stream(o.device)))
 
 
+def problem_ws_bytes(pb: Problem) -> int:
+    n = ctypes.c_size_t(0)
+    _check(_lib.sage_attn_workspace_bytes_ex(pb.ref, ctypes.byref(n)))
+    return n.value
+
+
+def _check_qkv(q, k, v, ndim: int):
+    if q.dim() != ndim or k.dim() != ndim or v.dim() != ndim:
+        raise ValueError(f"q, k, v must be {ndim}-D")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in DTYPES:
+        raise ValueError("q, k, v must share one dtype, float16 or bfloat16")
+    if not (q.is_cuda and k.is_cuda and v.is_cuda) or not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must be on the same GPU")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous")
+    if k.shape != v.shape:
+        raise ValueError(f"k shape {tuple(k.shape)} differs from v shape {tuple(v.shape)}")
+
+
+def fwd_ex(pb: Problem, q, k, v, o, workspace) -> None:
+    """sage_attn_fwd_ex on caller-provided tensors (o and workspace are written)."""
+    _check(_lib.sage_attn_fwd_ex(pb.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(workspace), workspace.numel(),
+                                 _stream(q.device)))
+
+
+def prologue_ex(pb: Problem, q, k, v, workspace) -> None:
+    _check(_lib.sage_attn_prologue_ex(pb.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(workspace), workspace.numel(),
+                                      _stream(q.device)))
+
+
+def attend_ex(pb: Problem, o, workspace) -> None:
+    _check(_lib.sage_attn_attend_ex(pb.ref, _ptr(o), _ptr(workspace), workspace.numel(), _stream(o.device)))
+
+
 def sageattn(q, k, v, attn_mask=None, dropout_p: float = 0.0, is_causal: bool = False, scale=None,
-             qk_bits: int = 8, pv_bits: int = 8, workspace=None):
+             qk_bits: int = 8, pv_bits: int = 8, tensor_layout: str = "HND", workspace=None):
     """Quantized drop-in for F.scaled_dot_product_attention(q, k, v, is_causal=...).
 
-    q [B, H, N, d], k/v [B, Hkv, N, d], fp16, contiguous; d in {64, 128}; qk_bits 8 (INT8
-    codes) or 4 (INT4-range codes); pv_bits 8 (FP8 P~ and V, the fast mode) or 16 (fp16 P
-    and V, the high-fidelity mode).  Grouped-query attention maps head h to kv head
-    h // (H // Hkv).  Returns fp16 [B, H, N, d].
+    tensor_layout "HND": q [B, H, N, d], k/v [B, Hkv, N, d]; "NHD": q [B, N, H, d],
+    k/v [B, N, Hkv, d].  fp16, contiguous; d in {64, 128}; qk_bits 8 (INT8 codes) or 4
+    (INT4-range codes); pv_bits 8 (FP8 P~ and V, the fast mode) or 16 (fp16 P and V, the
+    high-fidelity mode).  Grouped-query attention maps head h to kv head h // (H // Hkv).
+    Returns o shaped and laid out like q.
     """
     if attn_mask is not None or dropout_p != 0.0 or scale is not None:
         raise NotImplementedError("attn_mask, dropout and custom scale are not supported")
-    B, H, Hkv, N, d = _shapes(q, k, v)
-    nbytes = workspace_bytes(B, H, Hkv, N, d, is_causal, qk_bits, pv_bits)
+    if tensor_layout == "HND" and q.dtype == torch.float16:
+        B, H, Hkv, N, d = _shapes(q, k, v)
+    else:
+        _check_qkv(q, k, v, 4)
+        if tensor_layout == "HND":
+            (B, H, N, d), Hkv = q.shape, k.shape[1]
+            ok = k.shape[0] == B and k.shape[2] == N and k.shape[3] == d
+        elif tensor_layout == "NHD":
+            (B, N, H, d), Hkv = q.shape, k.shape[2]
+            ok = k.shape[0] == B and k.shape[1] == N and k.shape[3] == d
+        else:
+            raise ValueError(f"tensor_layout must be one of {sorted(LAYOUTS)}")
+        if not ok:
+            raise ValueError(f"k/v shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
+    pb = Problem(B, H, Hkv, N, d, is_causal, qk_bits, pv_bits, tensor_layout, q.dtype)
+    nbytes = problem_ws_bytes(pb)
     if workspace is None or workspace.numel() < nbytes:
         workspace = alloc_workspace(nbytes, q.device)
     o = torch.empty_like(q)
-    fwd(q, k, v, o, workspace, is_causal, qk_bits, pv_bits)
+    fwd_ex(pb, q, k, v, o, workspace)
+    return o
+
+
+def sageattn_varlen(q, k, v, cu_seqlens, is_causal: bool = False, qk_bits: int = 8, pv_bits: int = 8,
+                    workspace=None):
+    """Variable-length batch: q [T, H, d], k/v [T, Hkv, d] hold the sequences back to back;
+    sequence s is tokens cu_seqlens[s] .. cu_seqlens[s + 1] - 1 (cu_seqlens: a host list or CPU
+    tensor of B + 1 increasing ints from 0 to T).  Each sequence is attended, smoothed and
+    quantized on its own.  Returns o [T, H, d]."""
+    _check_qkv(q, k, v, 3)
+    T, H, d = q.shape
+    Hkv = k.shape[1]
+    if k.shape[0] != T or k.shape[2] != d:
+        raise ValueError(f"k/v shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
+    if hasattr(cu_seqlens, "is_cuda") and cu_seqlens.is_cuda:
+        raise ValueError("cu_seqlens must be on the host (a list or a CPU tensor)")
+    cu = [int(x) for x in (cu_seqlens.tolist() if hasattr(cu_seqlens, "tolist") else cu_seqlens)]
+    if len(cu) < 2 or cu[-1] != T:
+        raise ValueError(f"cu_seqlens must end at the token count {T}")
+    pb = Problem(len(cu) - 1, H, Hkv, 0, d, is_causal, qk_bits, pv_bits, "HND", q.dtype, cu)
+    nbytes = problem_ws_bytes(pb)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = alloc_workspace(nbytes, q.device)
+    o = torch.empty_like(q)
+    fwd_ex(pb, q, k, v, o, workspace)
     return o
 
 

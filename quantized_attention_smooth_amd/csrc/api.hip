@@ -7,6 +7,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <vector>
+
 #include "../../include/sage_attn.h"
 #include "sage_internal.h"
 
@@ -19,34 +21,124 @@ int hip_fail(hipError_t e, const char* what) {
   return SAGE_ERR_HIP;
 }
 
-// Shape checks shared by every entry point; fills D on success.
-int check_dims(int B, int H, int Hkv, int N, int d, int causal, int qk_bits, int pv_bits, sage::Dims* D) {
-  if (B < 1 || H < 1 || Hkv < 1 || N < 1) return SAGE_ERR_INVALID_ARG;
+// Checks shared by every entry point; fills D (and, for varlen, the sequence table) on success.
+int check_problem(const sage_problem_t* p, sage::Dims* D, std::vector<sage::Seq>* table) {
+  if (p == nullptr) return SAGE_ERR_INVALID_ARG;
+  const int B = p->B, H = p->H, Hkv = p->Hkv, d = p->d;
+  const bool varlen = p->cu_seqlens != nullptr;
+  if (B < 1 || H < 1 || Hkv < 1 || (!varlen && p->N < 1)) return SAGE_ERR_INVALID_ARG;
   if (H % Hkv != 0) return SAGE_ERR_INVALID_ARG;
-  if (causal != 0 && causal != 1) return SAGE_ERR_INVALID_ARG;
+  if (p->causal != 0 && p->causal != 1) return SAGE_ERR_INVALID_ARG;
+  if (p->layout != SAGE_LAYOUT_HND && p->layout != SAGE_LAYOUT_NHD) return SAGE_ERR_INVALID_ARG;
+  if (p->dtype != SAGE_DTYPE_FP16 && p->dtype != SAGE_DTYPE_BF16) return SAGE_ERR_INVALID_ARG;
   if (d != 64 && d != 128) return SAGE_ERR_UNSUPPORTED;
-  if (qk_bits != 4 && qk_bits != 8) return SAGE_ERR_UNSUPPORTED;
-  if (pv_bits != 8 && pv_bits != 16) return SAGE_ERR_UNSUPPORTED;
-  if (N > (1 << 23)) return SAGE_ERR_UNSUPPORTED;   // exact fixed-point K sums need N <= 2^23
-  const long long npad = ((long long)N + 127) / 128 * 128;
-  // every element count the kernels index must fit comfortably in 64 bits, and the number of
-  // workgroups in a 1-D grid must fit in 32 bits
-  const double heads = (double)B * (double)H;
-  if (heads * (double)npad * (double)d > 9.0e18) return SAGE_ERR_INVALID_ARG;
-  if (heads * (double)(npad / 128) * (double)npad * 4.0 > 9.0e18) return SAGE_ERR_INVALID_ARG;
-  if (heads * (double)(npad / 128) > 2147483647.0) return SAGE_ERR_INVALID_ARG;
-  if ((double)B * Hkv > 65535.0 || heads > 65535.0) return SAGE_ERR_INVALID_ARG;   // grid.y/z limits
-  D->B = B; D->H = H; D->Hkv = Hkv; D->N = N; D->d = d; D->causal = causal; D->qk_bits = qk_bits; D->pv_bits = pv_bits;
+  if (p->qk_bits != 4 && p->qk_bits != 8) return SAGE_ERR_UNSUPPORTED;
+  if (p->pv_bits != 8 && p->pv_bits != 16) return SAGE_ERR_UNSUPPORTED;
+  if (p->dtype != SAGE_DTYPE_FP16) return SAGE_ERR_UNSUPPORTED;
+  if ((double)B * Hkv > 65535.0 || (double)B * H > 65535.0) return SAGE_ERR_INVALID_ARG;   // grid.y/z limits
+
+  // per-sequence lengths: one N for all, or the differences of cu_seqlens
+  long long nmax = 0, tot_pad = 0, tot_ds = 0, total = 0;
+  if (varlen) {
+    if (p->cu_seqlens[0] != 0) return SAGE_ERR_INVALID_ARG;
+    table->resize(B);
+  }
+  for (int s = 0; s < B; ++s) {
+    const long long n = varlen ? (long long)p->cu_seqlens[s + 1] - p->cu_seqlens[s] : p->N;
+    if (n < 1) return SAGE_ERR_INVALID_ARG;
+    if (n > (1 << 23)) return SAGE_ERR_UNSUPPORTED;   // exact fixed-point K sums need n <= 2^23
+    const long long nb = (n + 127) / 128;
+    if (varlen) {
+      sage::Seq& e = (*table)[s];
+      e.n = (int)n;
+      e.tok0 = p->cu_seqlens[s];
+      e.pad0 = (int)tot_pad;
+      e.unused = 0;
+      e.ds0 = tot_ds;
+    }
+    nmax = n > nmax ? n : nmax;
+    total += n;
+    tot_pad += nb * 128;
+    tot_ds += (long long)H * (long long)sage::ds_head_elems(p->causal != 0, (int)nb, (int)(nb * 128));
+    // every count the kernels index must fit comfortably in 64 bits; row offsets in 32 bits
+    if (tot_pad > 2147483647LL || total > 2147483647LL) return SAGE_ERR_INVALID_ARG;
+    if ((double)tot_pad * H * d > 9.0e18 || (double)tot_ds * 4.0 > 9.0e18) return SAGE_ERR_INVALID_ARG;
+  }
+  const long long npad = (nmax + 127) / 128 * 128;
+  if ((double)B * H * (double)(npad / 128) > 2147483647.0) return SAGE_ERR_INVALID_ARG;   // 1-D grid
+  D->B = B; D->H = H; D->Hkv = Hkv; D->N = (int)nmax; D->d = d; D->causal = p->causal;
+  D->qk_bits = p->qk_bits; D->pv_bits = p->pv_bits;
   D->Npad = (int)npad;
   D->nqb = D->Npad / 128;
   D->nkb = D->Npad / 128;
+  D->varlen = varlen ? 1 : 0;
+  D->tot_pad = tot_pad;
+  D->tot_ds = tot_ds;
+  // element strides (channels contiguous)
+  sage::Strides& st = D->st;
+  const long long N = nmax;
+  if (varlen) {                        // packed [T, heads, d]
+    st.qb = 0; st.qt = (long long)H * d; st.qh = d;
+    st.kb = 0; st.kt = (long long)Hkv * d; st.kh = d;
+  } else if (p->layout == SAGE_LAYOUT_HND) {   // [B, heads, N, d]
+    st.qb = (long long)H * N * d; st.qt = d; st.qh = N * d;
+    st.kb = (long long)Hkv * N * d; st.kt = d; st.kh = N * d;
+  } else {                             // [B, N, heads, d]
+    st.qb = N * H * d; st.qt = (long long)H * d; st.qh = d;
+    st.kb = N * Hkv * d; st.kt = (long long)Hkv * d; st.kh = d;
+  }
   return SAGE_OK;
+}
+
+sage_problem_t fixed_problem(int B, int H, int Hkv, int N, int d, int causal, int qk_bits, int pv_bits) {
+  sage_problem_t p;
+  memset(&p, 0, sizeof(p));
+  p.B = B; p.H = H; p.Hkv = Hkv; p.N = N; p.d = d; p.causal = causal; p.qk_bits = qk_bits; p.pv_bits = pv_bits;
+  p.layout = SAGE_LAYOUT_HND;
+  p.dtype = SAGE_DTYPE_FP16;
+  p.cu_seqlens = nullptr;
+  return p;
+}
+
+int check_dims(int B, int H, int Hkv, int N, int d, int causal, int qk_bits, int pv_bits, sage::Dims* D) {
+  const sage_problem_t p = fixed_problem(B, H, Hkv, N, d, causal, qk_bits, pv_bits);
+  return check_problem(&p, D, nullptr);
 }
 
 int check_ws(void* ws, size_t ws_bytes, const sage::Layout& L) {
   if (ws == nullptr) return SAGE_ERR_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(ws) % sage::WS_ALIGN != 0) return SAGE_ERR_WORKSPACE;
   if (ws_bytes < L.total) return SAGE_ERR_WORKSPACE;
+  return SAGE_OK;
+}
+
+// What an entry point runs.
+enum Work { kPrologue = 1, kAttend = 2, kBoth = 3 };
+
+int run(const sage_problem_t* p, const void* q, const void* k, const void* v, void* o, void* ws, size_t ws_bytes,
+        void* stream, int work) {
+  sage::Dims D;
+  std::vector<sage::Seq> table;
+  int st = check_problem(p, &D, &table);
+  if (st != SAGE_OK) return st;
+  const sage::Layout L = sage::make_layout(D);
+  st = check_ws(ws, ws_bytes, L);
+  if (st != SAGE_OK) return st;
+  const sage::Ptrs P = sage::carve(ws, L, q, k, v, o);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  if (D.varlen) {
+    e = sage::launch_seq_table(table.data(), D.B, P.seqs, s);
+    if (e != hipSuccess) return hip_fail(e, "sequence table launch");
+  }
+  if (work & kPrologue) {
+    e = sage::launch_prologue(D, P, s);
+    if (e != hipSuccess) return hip_fail(e, "prologue launch");
+  }
+  if (work & kAttend) {
+    e = sage::launch_attention(D, P, s);
+    if (e != hipSuccess) return hip_fail(e, "attention launch");
+  }
   return SAGE_OK;
 }
 
@@ -71,61 +163,56 @@ int sage_get_config(sage_config_t* out) {
   return SAGE_OK;
 }
 
-int sage_attn_workspace_bytes(int B, int H, int Hkv, int N, int d, int causal, int qk_bits, int pv_bits,
-                              size_t* bytes) {
+int sage_attn_workspace_bytes_ex(const sage_problem_t* p, size_t* bytes) {
   if (bytes == nullptr) return SAGE_ERR_INVALID_ARG;
   sage::Dims D;
-  const int st = check_dims(B, H, Hkv, N, d, causal, qk_bits, pv_bits, &D);
+  std::vector<sage::Seq> table;
+  const int st = check_problem(p, &D, &table);
   if (st != SAGE_OK) return st;
   *bytes = sage::make_layout(D).total;
   return SAGE_OK;
 }
 
+int sage_attn_fwd_ex(const sage_problem_t* p, const void* q, const void* k, const void* v, void* o,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o) return SAGE_ERR_INVALID_ARG;
+  return run(p, q, k, v, o, workspace, workspace_bytes, stream, kBoth);
+}
+
+int sage_attn_prologue_ex(const sage_problem_t* p, const void* q, const void* k, const void* v, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v) return SAGE_ERR_INVALID_ARG;
+  return run(p, q, k, v, nullptr, workspace, workspace_bytes, stream, kPrologue);
+}
+
+int sage_attn_attend_ex(const sage_problem_t* p, void* o, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!o) return SAGE_ERR_INVALID_ARG;
+  return run(p, nullptr, nullptr, nullptr, o, workspace, workspace_bytes, stream, kAttend);
+}
+
+int sage_attn_workspace_bytes(int B, int H, int Hkv, int N, int d, int causal, int qk_bits, int pv_bits,
+                              size_t* bytes) {
+  const sage_problem_t p = fixed_problem(B, H, Hkv, N, d, causal, qk_bits, pv_bits);
+  return sage_attn_workspace_bytes_ex(&p, bytes);
+}
+
 int sage_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, int Hkv, int N, int d,
                   int causal, int qk_bits, int pv_bits, void* workspace, size_t workspace_bytes, void* stream) {
-  if (!q || !k || !v || !o) return SAGE_ERR_INVALID_ARG;
-  sage::Dims D;
-  int st = check_dims(B, H, Hkv, N, d, causal, qk_bits, pv_bits, &D);
-  if (st != SAGE_OK) return st;
-  const sage::Layout L = sage::make_layout(D);
-  st = check_ws(workspace, workspace_bytes, L);
-  if (st != SAGE_OK) return st;
-  const sage::Ptrs P = sage::carve(workspace, L, q, k, v, o);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = sage::launch_prologue(D, P, s);
-  if (e != hipSuccess) return hip_fail(e, "prologue launch");
-  e = sage::launch_attention(D, P, s);
-  if (e != hipSuccess) return hip_fail(e, "attention launch");
-  return SAGE_OK;
+  const sage_problem_t p = fixed_problem(B, H, Hkv, N, d, causal, qk_bits, pv_bits);
+  return sage_attn_fwd_ex(&p, q, k, v, o, workspace, workspace_bytes, stream);
 }
 
 int sage_attn_prologue(const void* q, const void* k, const void* v, int B, int H, int Hkv, int N, int d,
                        int causal, int qk_bits, int pv_bits, void* workspace, size_t workspace_bytes,
                        void* stream) {
-  if (!q || !k || !v) return SAGE_ERR_INVALID_ARG;
-  sage::Dims D;
-  int st = check_dims(B, H, Hkv, N, d, causal, qk_bits, pv_bits, &D);
-  if (st != SAGE_OK) return st;
-  const sage::Layout L = sage::make_layout(D);
-  st = check_ws(workspace, workspace_bytes, L);
-  if (st != SAGE_OK) return st;
-  const sage::Ptrs P = sage::carve(workspace, L, q, k, v, nullptr);
-  const hipError_t e = sage::launch_prologue(D, P, static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? SAGE_OK : hip_fail(e, "prologue launch");
+  const sage_problem_t p = fixed_problem(B, H, Hkv, N, d, causal, qk_bits, pv_bits);
+  return sage_attn_prologue_ex(&p, q, k, v, workspace, workspace_bytes, stream);
 }
 
 int sage_attn_attend(void* o, int B, int H, int Hkv, int N, int d, int causal, int qk_bits, int pv_bits,
                      void* workspace, size_t workspace_bytes, void* stream) {
-  if (!o) return SAGE_ERR_INVALID_ARG;
-  sage::Dims D;
-  int st = check_dims(B, H, Hkv, N, d, causal, qk_bits, pv_bits, &D);
-  if (st != SAGE_OK) return st;
-  const sage::Layout L = sage::make_layout(D);
-  st = check_ws(workspace, workspace_bytes, L);
-  if (st != SAGE_OK) return st;
-  const sage::Ptrs P = sage::carve(workspace, L, nullptr, nullptr, nullptr, o);
-  const hipError_t e = sage::launch_attention(D, P, static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? SAGE_OK : hip_fail(e, "attention launch");
+  const sage_problem_t p = fixed_problem(B, H, Hkv, N, d, causal, qk_bits, pv_bits);
+  return sage_attn_attend_ex(&p, o, workspace, workspace_bytes, stream);
 }
 
 int sage_quant_debug(const void* q, const void* k, const void* v, int B, int H, int Hkv, int N, int d, int causal,
@@ -177,8 +264,11 @@ int sage_qk_tile_debug(const void* q, const void* k, const void* v, int B, int H
 const char* sage_status_string(int status) {
   switch (status) {
     case SAGE_OK: return "ok";
-    case SAGE_ERR_INVALID_ARG: return "invalid argument (null pointer, size < 1, H % Hkv != 0 or size overflow)";
-    case SAGE_ERR_UNSUPPORTED: return "unsupported configuration (d must be 64 or 128, qk_bits 4 or 8, pv_bits 8 or 16, N <= 2^23)";
+    case SAGE_ERR_INVALID_ARG:
+      return "invalid argument (null pointer, size < 1, H % Hkv != 0, bad layout/dtype code, cu_seqlens not starting "
+             "at 0 or not increasing, or size overflow)";
+    case SAGE_ERR_UNSUPPORTED:
+      return "unsupported configuration (d must be 64 or 128, qk_bits 4 or 8, pv_bits 8 or 16, sequence length <= 2^23)";
     case SAGE_ERR_WORKSPACE: return "workspace missing, too small or not 256-byte aligned";
     case SAGE_ERR_HIP: return "HIP runtime error (see sage_last_error)";
     default: return "unknown status";

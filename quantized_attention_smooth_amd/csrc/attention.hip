@@ -24,8 +24,9 @@
 //     error to one block, as on the hardware the pages target.
 //   * K/V code tiles stream HBM -> LDS with direct-to-LDS loads (global_load_lds_dwordx4),
 //     double buffered, 16-byte chunks XOR-swizzled against LDS bank conflicts.
-//   * Workgroup ids are remapped so each XCD (own L2) works through whole heads; causal
-//     grids start with the longest (diagonal-most) query blocks.
+//   * Workgroup ids are remapped so each XCD (own L2) works through whole heads (of every
+//     sequence of the batch); causal grids start with each sequence's longest (diagonal-most)
+//     query blocks.
 //   * fp16 P V (PV16; the high-fidelity "qk_int8_pv_fp16" mode of the blog page "SageAttention：
 //     大模型量化注意力加速实践指南", section on precision control): V stays fp16 and P = e^(z - m)
 //     is rounded to fp16 into the B operand of v_mfma_f32_32x32x16_f16 (8 k-slots per lane: a
@@ -60,8 +61,8 @@ struct AttnArgs {
   const float* vscale;
   const float* ds;
   __half* o;
-  int B, H, Hkv, N, Npad, nqb, nkb;
-  bool causal;          // Delta_S rows stored triangularly
+  Geo g;                // sequences, strides; g.causal: Delta_S rows stored triangularly
+  int B, nqb;           // sequences; Q blocks of the longest one
   float k2;             // log2(e) / sqrt(d)
   int dbg_b, dbg_h, dbg_qb, dbg_kb;
   int32_t* dbg_out;
@@ -115,20 +116,16 @@ typedef __attribute__((address_space(3))) void lds_void;
 template <int D>
 constexpr int kTileInstrs = BK * D / 16 / 64 / WAVES;
 
-// K codes of block kb (and its Delta_S row slice, wave 0) into stage st.  The Delta_S load
-// goes first, so a wait for "all but the last kTileInstrs" loads of wave 0 leaves only K
-// chunks outstanding.
+// K codes of one block (ktile: its first row) and its Delta_S row slice (wave 0) into stage st.
+// The Delta_S load goes first, so a wait for "all but the last kTileInstrs" loads of wave 0
+// leaves only K chunks outstanding.
 template <int D, bool PV16>
-__device__ inline void issue_k(const AttnArgs& a, Smem<D, PV16>& sm, int st, size_t bkv, size_t bh, int qb, int kb,
-                               int w, int lane) {
+__device__ inline void issue_k(const int8_t* ktile, const float* dsrc, Smem<D, PV16>& sm, int st, int w, int lane) {
   constexpr int CPR = D / 16;                 // 16-byte chunks per K row
-  if (w == 0 && lane < BK / 4) {
-    const float* src = a.ds + bh * ds_head_elems(a.causal, a.nqb, a.Npad) + ds_row_offset(a.causal, qb, a.Npad) +
-                       (size_t)kb * BK;
-    __builtin_amdgcn_global_load_lds(src + (uint32_t)(lane * 4), (lds_void*)sm.ds[st], 16, 0, 0);
-  }
+  if (w == 0 && lane < BK / 4)
+    __builtin_amdgcn_global_load_lds(dsrc + (uint32_t)(lane * 4), (lds_void*)sm.ds[st], 16, 0, 0);
   // wave-uniform tile base (scalar registers) plus 32-bit per-lane byte offsets
-  const int8_t* kbase = a.kcodes + (bkv * a.Npad + (size_t)kb * BK) * D;
+  const int8_t* kbase = ktile;
 #pragma unroll
   for (int m = 0; m < kTileInstrs<D>; ++m) {
     const int blk = m * WAVES + w;            // which 1 KB of the tile this wave writes
@@ -142,10 +139,10 @@ __device__ inline void issue_k(const AttnArgs& a, Smem<D, PV16>& sm, int st, siz
 // V of block kb into stage st: FP8 codes (64-byte rows) or fp16 V (32-byte rows, twice the
 // instructions).
 template <int D, bool PV16>
-__device__ inline void issue_v(const AttnArgs& a, Smem<D, PV16>& sm, int st, size_t bkv, int kb, int w, int lane) {
+__device__ inline void issue_v(const uint8_t* vtile, Smem<D, PV16>& sm, int st, int w, int lane) {
   constexpr int RB = PV16 ? 32 : VGROUP;      // bytes per LDS row (group, channel)
   constexpr int CR = RB / 16;                 // 16-byte chunks per row
-  const uint8_t* vbase = a.vcodes + (bkv * (size_t)a.Npad + (size_t)kb * BK) * D * (PV16 ? 2 : 1);
+  const uint8_t* vbase = vtile;
 #pragma unroll
   for (int m = 0; m < kTileInstrs<D> * (PV16 ? 2 : 1); ++m) {
     const int blk = m * WAVES + w;
@@ -217,20 +214,35 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
   __shared__ Smem<D, PV16> sm;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, col = lane & 31, half = lane >> 5;
 
+  const int H = a.g.H, Hkv = a.g.Hkv;
   int b, h, qb;
+  Seq sq;
   if (DUMP) {
     b = a.dbg_b; h = a.dbg_h; qb = a.dbg_qb;
+    sq = a.g.seq(b);
   } else {
-    const int total = a.B * a.H * a.nqb;
+    // head-major order: each XCD's contiguous share holds whole heads of every sequence, so
+    // varlen batches split evenly and a kv head's codes stay in one XCD's L2
+    const int total = a.B * H * a.nqb;
     const int L = xcd_remap(blockIdx.x, total);
-    const int bhi = L / a.nqb, qi = L % a.nqb;
-    b = bhi / a.H; h = bhi % a.H;
-    qb = CAUSAL ? a.nqb - 1 - qi : qi;
+    const int hbi = L / a.nqb, qi = L % a.nqb;
+    h = hbi / a.B; b = hbi % a.B;
+    sq = a.g.seq(b);
+    if (qi >= seq_blocks(sq)) return;           // beyond this sequence (varlen)
+    qb = CAUSAL ? seq_blocks(sq) - 1 - qi : qi;
   }
-  const size_t bh = (size_t)b * a.H + h;
-  const size_t bkv = (size_t)b * a.Hkv + h / (a.H / a.Hkv);
+  const int hk = h / (H / Hkv);
+  const int N = sq.n, nkb = seq_blocks(sq);
   const int il = w * QW + col;                  // query within the block
-  const int i = qb * BQ + il;
+  const int i = qb * BQ + il;                   // query within the sequence
+  // this (sequence, head)'s workspace sections
+  const size_t qrows = rows_off(sq, H, h), krows = rows_off(sq, Hkv, hk);
+  const int8_t* kc = a.kcodes + krows * D;
+  const uint8_t* vc = a.vcodes + krows * D * (PV16 ? 2 : 1);
+  const float* kscl = a.kscale + blocks_off(sq, Hkv, hk) * 2;
+  const float* dsrow = a.ds + ds_off(sq, a.g.causal, h) + ds_row_offset(a.g.causal, qb, nkb * BK);
+  auto ktile = [&](int kb) { return kc + (size_t)kb * BK * D; };
+  auto vtile = [&](int kb) { return vc + (size_t)kb * BK * D * (PV16 ? 2 : 1); };
 
   // the wave's 32 query rows as the B operand of S^T = K Q^T (16 bytes per k-step)
   // (INT4 range: 32 bytes per 64-channel step, held as two consecutive v4i)
@@ -238,12 +250,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
 #pragma unroll
   for (int s = 0; s < D / 32; ++s) {
     const int ch = QK4 ? 64 * (s >> 1) + 32 * half + 16 * (s & 1) : 32 * s + 16 * half;
-    qreg[s] = *reinterpret_cast<const v4i*>(a.qcodes + (bh * a.Npad + i) * D + ch);
+    qreg[s] = *reinterpret_cast<const v4i*>(a.qcodes + (qrows + i) * D + ch);
   }
-  const float qd = a.qscale[bh * a.Npad + i];
+  const float qd = a.qscale[qrows + i];
 
   if (DUMP) {
-    issue_k<D, PV16>(a, sm, 0, bkv, bh, qb, a.dbg_kb, w, lane);
+    issue_k<D, PV16>(ktile(a.dbg_kb), dsrow + (size_t)a.dbg_kb * BK, sm, 0, w, lane);
     wait_loads();
     __syncthreads();
     v16i sacc[BK / 32];
@@ -258,14 +270,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
     return;
   }
 
-  const int nblk = CAUSAL ? qb + 1 : a.nkb;
+  const int nblk = CAUSAL ? qb + 1 : nkb;
   float m_run = -INFINITY, l_part = 0.f;
   v16f og[D / 32];
 #pragma unroll
   for (int ct = 0; ct < D / 32; ++ct) og[ct] = (v16f){};
 
-  issue_v<D, PV16>(a, sm, 0, bkv, 0, w, lane);
-  issue_k<D, PV16>(a, sm, 0, bkv, bh, qb, 0, w, lane);
+  issue_v<D, PV16>(vtile(0), sm, 0, w, lane);
+  issue_k<D, PV16>(ktile(0), dsrow, sm, 0, w, lane);
   wait_loads();
   __syncthreads();
 
@@ -277,8 +289,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
     const int st = kb & 1;
     const bool more = kb + 1 < nblk;
     if (more) {
-      if (!PV16) issue_v<D, PV16>(a, sm, st ^ 1, bkv, kb + 1, w, lane);
-      issue_k<D, PV16>(a, sm, st ^ 1, bkv, bh, qb, kb + 1, w, lane);
+      if (!PV16) issue_v<D, PV16>(vtile(kb + 1), sm, st ^ 1, w, lane);
+      issue_k<D, PV16>(ktile(kb + 1), dsrow + (size_t)(kb + 1) * BK, sm, st ^ 1, w, lane);
     }
 
     v16i sacc[BK / 32];
@@ -288,7 +300,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
     // both lane halves' delta_K through one wave-uniform (scalar) load, so that waiting for it
     // does not also wait for the tile prefetch just issued
     typedef __attribute__((address_space(4))) const float cfloat;   // read-only here: scalar load
-    const cfloat* kdp = (const cfloat*)(a.kscale + (bkv * a.nkb + kb) * 2);
+    const cfloat* kdp = (const cfloat*)(kscl + kb * 2);
     const float kd0 = kdp[0], kd1 = kdp[1];
     const float kd = half ? kd1 : kd0;
     const float cmul = qd * kd * a.k2;
@@ -309,7 +321,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
           float x = fmaf(sf, cmul, dsa[r]);
           if (MASK) {
             const int j = kb * BK + j0 + r;
-            if ((CAUSAL && j > i) || j >= a.N) x = -INFINITY;
+            if ((CAUSAL && j > i) || j >= N) x = -INFINITY;
           }
           z[t][4 * qq + r] = x;
         }
@@ -376,7 +388,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
 
       wait_loads();
       __syncthreads();
-      if (more) issue_v<D, PV16>(a, sm, 0, bkv, kb + 1, w, lane);
+      if (more) issue_v<D, PV16>(vtile(kb + 1), sm, 0, w, lane);
       return;
     }
 
@@ -422,7 +434,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
   };
 
   // the last block needs masking when causal (diagonal block) or when N is not a multiple of BK
-  const bool mask_last = CAUSAL || (a.N % BK) != 0;
+  const bool mask_last = CAUSAL || (N % BK) != 0;
   const int nfull = mask_last ? nblk - 1 : nblk;
   for (int kb = 0; kb < nfull; ++kb) block(kb, std::false_type{});
   if (mask_last) block(nblk - 1, std::true_type{});
@@ -431,9 +443,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
   // fp16: no V scale)
   const float l = xhalf_sum(l_part);
   const float inv_l = l > 0.f ? 1.f / l : 0.f;
-  if (i < a.N) {
-    __half* orow = a.o + (bh * a.N + i) * D;
-    const float* vs = a.vscale + bkv * D;
+  if (i < N) {
+    __half* orow = a.o + b * a.g.st.qb + (long long)(sq.tok0 + i) * a.g.st.qt + h * a.g.st.qh;
+    const float* vs = a.vscale + ((size_t)b * Hkv + hk) * D;
 #pragma unroll
     for (int ct = 0; ct < D / 32; ++ct) {
 #pragma unroll
@@ -453,6 +465,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
 
 AttnArgs make_args(const Dims& D, const Ptrs& P) {
   AttnArgs a{};
+  a.g = make_geo(D, P.seqs);
+  a.B = D.B;
+  a.nqb = D.nqb;
   a.qcodes = P.qcodes;
   a.kcodes = P.kcodes;
   a.vcodes = P.vcodes;
@@ -461,8 +476,6 @@ AttnArgs make_args(const Dims& D, const Ptrs& P) {
   a.vscale = P.vscale;
   a.ds = P.ds;
   a.o = P.o;
-  a.B = D.B; a.H = D.H; a.Hkv = D.Hkv; a.N = D.N; a.Npad = D.Npad; a.nqb = D.nqb; a.nkb = D.nkb;
-  a.causal = D.causal != 0;
   a.k2 = (float)(1.4426950408889634 / sqrt((double)D.d));
   return a;
 }

@@ -87,21 +87,26 @@ __global__ void init_stats(unsigned long long* ksum, unsigned int* vamax, int n)
 // ---------------------------------------------------------------------------------------
 // K channel sums (exact: fp64 within a workgroup, int64 fixed point across) and V channel
 // abs-max, per (b, kv head).  VSTATS = false (V kept in fp16) skips V entirely.
-// grid (ceil(N / 256), B*Hkv), 256 threads; thread = (row slot, 8-channel chunk).
+// grid (ceil(longest / 256), B*Hkv), 256 threads; thread = (row slot, 8-channel chunk).
 // ---------------------------------------------------------------------------------------
 template <int D, bool VSTATS>
 __global__ __launch_bounds__(256) void kv_stats(const __half* __restrict__ k, const __half* __restrict__ v,
                                                 unsigned long long* __restrict__ ksum,
-                                                unsigned int* __restrict__ vamax, int N) {
+                                                unsigned int* __restrict__ vamax, Geo g) {
   constexpr int TPR = D / 8;      // threads per row
   constexpr int RPP = 256 / TPR;  // rows per pass
   constexpr int TOK = 256;        // tokens per workgroup
   __shared__ double ls[RPP][D];
   __shared__ float lm[RPP][D];
   const int tid = threadIdx.x, cq = tid % TPR, r0 = tid / TPR;
-  const size_t bh = blockIdx.y;
-  const __half* kb = k + bh * (size_t)N * D;
-  const __half* vb = v + bh * (size_t)N * D;
+  const size_t bh = blockIdx.y;                 // (sequence, kv head)
+  const int sidx = (int)bh / g.Hkv, hk = (int)bh % g.Hkv;
+  const Seq sq = g.seq(sidx);
+  const int N = sq.n;
+  if ((int)blockIdx.x * TOK >= N) return;
+  const long long base = sidx * g.st.kb + (long long)sq.tok0 * g.st.kt + hk * g.st.kh;
+  const __half* kb = k + base;
+  const __half* vb = v + base;
   // Sums of at most TOK fp16 values are exact in fp64: every term is a multiple of 2^-24 and the
   // total stays below 2^24 < 2^(53 - 24).  The workgroup's exact total is then handed to the
   // cross-workgroup reduction as an int64 count of 2^-24 units.
@@ -114,11 +119,11 @@ __global__ __launch_bounds__(256) void kv_stats(const __half* __restrict__ k, co
   for (int p = 0; p < TOK / RPP; ++p) {
     const int row = tok0 + p * RPP + r0;
     if (row < N) {
-      const Half8 kk = load8(kb + (size_t)row * D + cq * 8);
+      const Half8 kk = load8(kb + row * g.st.kt + cq * 8);
 #pragma unroll
       for (int e = 0; e < 8; ++e) s[e] += (double)__half2float(kk.h[e]);
       if (VSTATS) {
-        const Half8 vv = load8(vb + (size_t)row * D + cq * 8);
+        const Half8 vv = load8(vb + row * g.st.kt + cq * 8);
 #pragma unroll
         for (int e = 0; e < 8; ++e) mx[e] = fmaxf(mx[e], fabsf(__half2float(vv.h[e])));
       }
@@ -148,8 +153,8 @@ __global__ __launch_bounds__(256) void kv_stats(const __half* __restrict__ k, co
 __device__ inline int v16_lds_row(int row) { return row ^ ((row >> 3) & 7); }
 
 template <int D>
-__device__ inline void store_v16(const __half* __restrict__ vbase, uint8_t* vt, uint8_t* __restrict__ vout,
-                                 size_t bh, int kb, int N, int Npad, int tid, int cq, int r0) {
+__device__ inline void store_v16(const __half* __restrict__ vbase, long long tstride, uint8_t* vt,
+                                 uint8_t* __restrict__ dst, int kb, int N, int tid, int cq, int r0) {
   constexpr int TPR = D / 8, RPP = 256 / TPR, G4 = BK / 4 / RPP;
 #pragma unroll
   for (int p = 0; p < G4; ++p) {
@@ -161,7 +166,7 @@ __device__ inline void store_v16(const __half* __restrict__ vbase, uint8_t* vt, 
     for (int i = 0; i < 4; ++i) {
       const int row = kb * BK + jl0 + i;
       if (row < N) {
-        const Half8 vv = load8(vbase + (size_t)row * D + cq * 8);
+        const Half8 vv = load8(vbase + row * tstride + cq * 8);
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[i][e] = __half_as_ushort(vv.h[e]);
       } else {
@@ -178,7 +183,6 @@ __device__ inline void store_v16(const __half* __restrict__ vbase, uint8_t* vt, 
     }
   }
   __syncthreads();
-  uint8_t* dst = vout + (bh * (size_t)(Npad / 16) + (size_t)kb * (BK / 16)) * D * 32;
   for (int ch = tid; ch < BK * D * 2 / 16; ch += 256) {
     const int row = ch >> 1;
     *reinterpret_cast<uint4*>(dst + ch * 16) =
@@ -188,7 +192,7 @@ __device__ inline void store_v16(const __half* __restrict__ vbase, uint8_t* vt, 
 
 // ---------------------------------------------------------------------------------------
 // K smoothing + quantization and V FP8 quantization for one KV block of 128 keys.
-// grid (nkb, B*Hkv), 256 threads.
+// grid (blocks of the longest sequence, B*Hkv), 256 threads.
 // K group: keys 8a + 4h + r of the block share the scale of lane half h (one scale per
 // lane of the 32x32 integer MFMA accumulator that holds those keys).
 // V codes are written transposed per 64-key group in the FP8 MFMA k-slot order; with PV16
@@ -200,16 +204,22 @@ __global__ __launch_bounds__(256) void kv_quant(const __half* __restrict__ k, co
                                                 const unsigned int* __restrict__ vamax,
                                                 int8_t* __restrict__ kcodes, uint8_t* __restrict__ vcodes,
                                                 float* __restrict__ kscale, float* __restrict__ muk_out,
-                                                float* __restrict__ vscale, int N, int Npad, int nkb, float R) {
+                                                float* __restrict__ vscale, Geo g, float R) {
   constexpr int TPR = D / 8, RPP = 256 / TPR, PASSES = BK / RPP;
   static_assert(RPP % 8 == 0, "a thread's rows must share (row % 8)");
   __shared__ float red[WAVES][2];
   __shared__ __attribute__((aligned(16))) uint8_t vt[BK * D * (PV16 ? 2 : 1)];
   const int tid = threadIdx.x, cq = tid % TPR, r0 = tid / TPR, lane = tid % 64, w = tid / 64;
   const int kb = blockIdx.x;
-  const size_t bh = blockIdx.y;
-  const __half* kbase = k + bh * (size_t)N * D;
-  const __half* vbase = v + bh * (size_t)N * D;
+  const size_t bh = blockIdx.y;                 // (sequence, kv head)
+  const int sidx = (int)bh / g.Hkv, hk = (int)bh % g.Hkv;
+  const Seq sq = g.seq(sidx);
+  if (kb >= seq_blocks(sq)) return;
+  const int N = sq.n;
+  const long long ts = g.st.kt;
+  const __half* kbase = k + sidx * g.st.kb + (long long)sq.tok0 * ts + hk * g.st.kh;
+  const __half* vbase = v + sidx * g.st.kb + (long long)sq.tok0 * ts + hk * g.st.kh;
+  const size_t rows = rows_off(sq, g.Hkv, hk);  // this head's padded rows in the code arrays
 
   float mu[8], vinv[8];
 #pragma unroll
@@ -226,21 +236,21 @@ __global__ __launch_bounds__(256) void kv_quant(const __half* __restrict__ k, co
   }
 
   // gamma_K = RN32(K - mu_K); every row of this thread has the same (row % 8)
-  float g[PASSES][8];
+  float gk[PASSES][8];
   float am = 0.f;
 #pragma unroll
   for (int p = 0; p < PASSES; ++p) {
     const int row = kb * BK + p * RPP + r0;
     if (row < N) {
-      const Half8 kk = load8(kbase + (size_t)row * D + cq * 8);
+      const Half8 kk = load8(kbase + row * ts + cq * 8);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        g[p][e] = __half2float(kk.h[e]) - mu[e];
-        am = fmaxf(am, fabsf(g[p][e]));
+        gk[p][e] = __half2float(kk.h[e]) - mu[e];
+        am = fmaxf(am, fabsf(gk[p][e]));
       }
     } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) g[p][e] = 0.f;
+      for (int e = 0; e < 8; ++e) gk[p][e] = 0.f;
     }
   }
   const int hgrp = (r0 & 7) >> 2;
@@ -255,19 +265,19 @@ __global__ __launch_bounds__(256) void kv_quant(const __half* __restrict__ k, co
   if (tid < 2) {
     float a = 0.f;
     for (int i = 0; i < WAVES; ++i) a = fmaxf(a, red[i][tid]);
-    kscale[(bh * nkb + kb) * 2 + tid] = a / R;
+    kscale[(blocks_off(sq, g.Hkv, hk) + kb) * 2 + tid] = a / R;
   }
 #pragma unroll
   for (int p = 0; p < PASSES; ++p) {
     const int row = kb * BK + p * RPP + r0;   // < Npad: rows past N get zero codes
     float x[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = fminf(fmaxf(rintf(g[p][e] * inv), -R), R);
-    store_codes(kcodes + (bh * Npad + row) * D, cq, x, R < 8.f);
+    for (int e = 0; e < 8; ++e) x[e] = fminf(fmaxf(rintf(gk[p][e] * inv), -R), R);
+    store_codes(kcodes + (rows + row) * D, cq, x, R < 8.f);
   }
 
   if (PV16) {
-    store_v16<D>(vbase, vt, vcodes, bh, kb, N, Npad, tid, cq, r0);
+    store_v16<D>(vbase, ts, vt, vcodes + (rows + (size_t)kb * BK) * D * 2, kb, N, tid, cq, r0);
     return;
   }
 
@@ -287,7 +297,7 @@ __global__ __launch_bounds__(256) void kv_quant(const __half* __restrict__ k, co
     for (int i = 0; i < 4; ++i) {
       const int row = kb * BK + jl0 + i;
       if (row < N) {
-        const Half8 vv = load8(vbase + (size_t)row * D + cq * 8);
+        const Half8 vv = load8(vbase + row * ts + cq * 8);
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[i][e] = fminf(fmaxf(__half2float(vv.h[e]) * vinv[e], -V_RANGE), V_RANGE);
       } else {
@@ -305,7 +315,7 @@ __global__ __launch_bounds__(256) void kv_quant(const __half* __restrict__ k, co
     }
   }
   __syncthreads();
-  uint8_t* dst = vcodes + (bh * (size_t)(Npad / VGROUP) + (size_t)kb * 2) * D * VGROUP;
+  uint8_t* dst = vcodes + (rows + (size_t)kb * BK) * D;
   for (int ch = tid; ch < 2 * D * VGROUP / 16; ch += 256) {
     const int rowc = ch >> 2, c = rowc % D;    // row = group * D + channel
     const int src = rowc * VGROUP + (((ch & 3) ^ ((c >> 3) & 3)) << 4);
@@ -315,19 +325,24 @@ __global__ __launch_bounds__(256) void kv_quant(const __half* __restrict__ k, co
 
 // ---------------------------------------------------------------------------------------
 // Q smoothing (per 128-row block mean) + per-row quantization.
-// grid (nqb, B*H), 256 threads.
+// grid (blocks of the longest sequence, B*H), 256 threads.
 // ---------------------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void q_quant(const __half* __restrict__ q, int8_t* __restrict__ qcodes,
                                                float* __restrict__ qscale, float* __restrict__ muq,
-                                               uint16_t* __restrict__ muqs, int N, int Npad, int nqb, float R) {
+                                               uint16_t* __restrict__ muqs, Geo g, float R) {
   constexpr int TPR = D / 8, RPP = 256 / TPR, PASSES = BQ / RPP;
   __shared__ double ls[RPP][D];
   __shared__ float lmu[D];
   const int tid = threadIdx.x, cq = tid % TPR, r0 = tid / TPR;
   const int qb = blockIdx.x;
-  const size_t bh = blockIdx.y;
-  const __half* qbase = q + bh * (size_t)N * D;
+  const int sidx = (int)blockIdx.y / g.H, h = (int)blockIdx.y % g.H;
+  const Seq sq = g.seq(sidx);
+  if (qb >= seq_blocks(sq)) return;
+  const int N = sq.n;
+  const long long ts = g.st.qt;
+  const __half* qbase = q + sidx * g.st.qb + (long long)sq.tok0 * ts + h * g.st.qh;
+  const size_t rows = rows_off(sq, g.H, h), blk = blocks_off(sq, g.H, h) + qb;
   const int nvalid = min(BQ, N - qb * BQ);
 
   // block sums in fp64 are exact (at most 128 fp16 terms, multiples of 2^-24, below 2^24)
@@ -339,7 +354,7 @@ __global__ __launch_bounds__(256) void q_quant(const __half* __restrict__ q, int
   for (int p = 0; p < PASSES; ++p) {
     const int row = qb * BQ + p * RPP + r0;
     if (row < N) {
-      const Half8 qq = load8(qbase + (size_t)row * D + cq * 8);
+      const Half8 qq = load8(qbase + row * ts + cq * 8);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         x[p][e] = __half2float(qq.h[e]);
@@ -358,13 +373,13 @@ __global__ __launch_bounds__(256) void q_quant(const __half* __restrict__ q, int
     for (int r = 0; r < RPP; ++r) t += ls[r][c];
     const float m = (float)(t / (double)nvalid);
     lmu[c] = m;
-    muq[(bh * nqb + qb) * D + c] = m;
+    muq[blk * D + c] = m;
     // exact three-part bf16 split of the mean, the A operand of the Delta_S GEMM
     const __bf16 b1 = (__bf16)m;
     const float r1 = m - (float)b1;
     const __bf16 b2 = (__bf16)r1;
     const __bf16 b3 = (__bf16)(r1 - (float)b2);
-    uint16_t* dst = muqs + ((bh * nqb + qb) * 3) * D + c;
+    uint16_t* dst = muqs + blk * 3 * D + c;
     dst[0] = __builtin_bit_cast(uint16_t, b1);
     dst[D] = __builtin_bit_cast(uint16_t, b2);
     dst[2 * D] = __builtin_bit_cast(uint16_t, b3);
@@ -389,8 +404,8 @@ __global__ __launch_bounds__(256) void q_quant(const __half* __restrict__ q, int
     float y[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) y[e] = fminf(fmaxf(rintf(x[p][e] * inv), -R), R);
-    store_codes(qcodes + (bh * Npad + row) * D, cq, y, R < 8.f);
-    if (cq == 0) qscale[bh * Npad + row] = am / R;
+    store_codes(qcodes + (rows + row) * D, cq, y, R < 8.f);
+    if (cq == 0) qscale[rows + row] = am / R;
   }
 }
 
@@ -442,23 +457,29 @@ __device__ inline Split3 split3(const float (&x)[8]) {
   return s;
 }
 
-// Q-tile form, for few Q blocks per key: grid (Npad/256 key tiles, ceil(nqb/32) Q-block tiles,
-// B*H), 256 threads; each wave owns 32 Q blocks x 64 keys (two 32x32 MFMA tiles) and splits
+// Q-tile form, for few Q blocks per key: grid (Npad/256 key tiles, ceil(nqb/32) Q-block tiles of
+// the longest sequence, B*H), 256 threads; each wave owns 32 Q blocks x 64 keys (two 32x32 MFMA tiles) and splits
 // both operands itself.  Causal rows stop at key (qb + 1) * 128.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) void delta_s_qtile(const __half* __restrict__ k, const float* __restrict__ muk,
                                                const float* __restrict__ muq, float* __restrict__ ds,
-                                               int H, int Hkv, int N, int Npad, int nqb, float k2) {
+                                               Geo g, float k2) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, r = lane & 31, hl = lane >> 5;
+  const int H = g.H, Hkv = g.Hkv;
   const int bh = blockIdx.z, b = bh / H, h = bh % H, hk = h / (H / Hkv);
   const size_t bkv = (size_t)b * Hkv + hk;
+  const Seq sq = g.seq(b);
+  const int N = sq.n, nqb = seq_blocks(sq), Npad = nqb * BQ;
   const int q0 = blockIdx.y * 32;                      // first Q block of this tile
   const int j0 = blockIdx.x * 256 + w * 64;            // first key of this wave
+  if (q0 >= nqb || j0 >= Npad) return;                 // beyond this sequence
   const int qlast = min(q0 + 31, nqb - 1);
   if (CAUSAL && j0 >= (qlast + 1) * BQ) return;        // every row of the tile stops earlier
   const int qb = q0 + r;                               // A row (operand) of this lane
   const bool qvalid = qb < nqb;
-  const __half* kb = k + bkv * (size_t)N * D;
+  const long long ts = g.st.kt;
+  const __half* kb = k + b * g.st.kb + (long long)sq.tok0 * ts + hk * g.st.kh;
+  const float* muqh = muq + blocks_off(sq, H, h) * D;
   f32x16 acc[2] = {};
 #pragma unroll 2
   for (int ks = 0; ks < D / 16; ++ks) {
@@ -467,7 +488,7 @@ __global__ __launch_bounds__(256) void delta_s_qtile(const __half* __restrict__ 
     {
       float4 m0 = make_float4(0.f, 0.f, 0.f, 0.f), m1 = m0;
       if (qvalid) {
-        const float* src = muq + ((size_t)bh * nqb + qb) * D + c0;
+        const float* src = muqh + (size_t)qb * D + c0;
         m0 = *reinterpret_cast<const float4*>(src);
         m1 = *reinterpret_cast<const float4*>(src + 4);
       }
@@ -483,7 +504,7 @@ __global__ __launch_bounds__(256) void delta_s_qtile(const __half* __restrict__ 
       const int j = j0 + 32 * t + r;                   // B column (key) of this lane
       float xb[8];
       if (j < N) {
-        const Half8 kk = load8(kb + (size_t)j * D + c0);
+        const Half8 kk = load8(kb + j * ts + c0);
 #pragma unroll
         for (int e = 0; e < 8; ++e) xb[e] = __half2float(kk.h[e]) - mkv[e];   // gamma_K, RN32
       } else {
@@ -502,7 +523,7 @@ __global__ __launch_bounds__(256) void delta_s_qtile(const __half* __restrict__ 
     }
   }
   // lane holds rows q0 + 8a + 4hl + e (e < 4) of key column j0 + 32t + r
-  float* dsh = ds + (size_t)bh * ds_head_elems(CAUSAL, nqb, Npad);
+  float* dsh = ds + ds_off(sq, CAUSAL, h);
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const int j = j0 + 32 * t + r;
@@ -523,9 +544,8 @@ struct AParts {                                  // one lane's mu_Q parts for a 
 };
 
 template <int D>
-__device__ inline void load_aparts(AParts<D>& A, const uint16_t* __restrict__ muqs, size_t bh, int nqb, int qa,
-                                   int hl) {
-  const uint16_t* ap = muqs + ((bh * nqb + min(qa, nqb - 1)) * 3) * D;
+__device__ inline void load_aparts(AParts<D>& A, const uint16_t* __restrict__ head, int nqb, int qa, int hl) {
+  const uint16_t* ap = head + (size_t)min(qa, nqb - 1) * 3 * D;   // head: this query head's parts
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks)
 #pragma unroll
@@ -538,13 +558,19 @@ __device__ inline void load_aparts(AParts<D>& A, const uint16_t* __restrict__ mu
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) void delta_s_kblock(const __half* __restrict__ k, const float* __restrict__ muk,
                                                const uint16_t* __restrict__ muqs, float* __restrict__ ds,
-                                               int H, int Hkv, int N, int Npad, int nqb, float k2) {
+                                               Geo g, float k2) {
   __shared__ DsSmem<D> sm;
   constexpr int KS = D / 16;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 31, hl = lane >> 5;
+  const int H = g.H, Hkv = g.Hkv;
   const int kb = blockIdx.x;
   const int bkv = blockIdx.y, b = bkv / Hkv, hk = bkv % Hkv, G = H / Hkv;
-  const __half* kbase = k + (size_t)bkv * N * D;
+  const Seq sq = g.seq(b);
+  const int N = sq.n, nqb = seq_blocks(sq), Npad = nqb * BQ;
+  if (kb >= nqb) return;                                      // beyond this sequence
+  const long long ts = g.st.kt;
+  const __half* kbase = k + b * g.st.kb + (long long)sq.tok0 * ts + hk * g.st.kh;
+  auto muq_head = [&](int hq) { return muqs + blocks_off(sq, H, hk * G + hq) * 3 * D; };
 
   // gamma_K parts of the block's 128 keys -> LDS
   constexpr int CH = D / 8;                                   // 8-channel chunks per key
@@ -554,7 +580,7 @@ __global__ __launch_bounds__(256) void delta_s_kblock(const __half* __restrict__
     const int j = kb * BK + key;
     float x[8];
     if (j < N) {
-      const Half8 kk = load8(kbase + (size_t)j * D + c8 * 8);
+      const Half8 kk = load8(kbase + j * ts + c8 * 8);
       const float4 m0 = *reinterpret_cast<const float4*>(muk + (size_t)bkv * D + c8 * 8);
       const float4 m1 = *reinterpret_cast<const float4*>(muk + (size_t)bkv * D + c8 * 8 + 4);
       const float mm[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
@@ -595,12 +621,11 @@ __global__ __launch_bounds__(256) void delta_s_kblock(const __half* __restrict__
   if (total > 0) {
     int hq, q0;
     pair(0, hq, q0);
-    load_aparts<D>(A, muqs, (size_t)b * H + hk * G + hq, nqb, q0 + r, hl);
+    load_aparts<D>(A, muq_head(hq), nqb, q0 + r, hl);
   }
   for (int n = 0; n < total; ++n) {
     int hq, q0;
     pair(n, hq, q0);
-    const size_t bh = (size_t)b * H + hk * G + hq;
     f32x16 acc[2] = {};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -625,9 +650,9 @@ __global__ __launch_bounds__(256) void delta_s_kblock(const __half* __restrict__
     if (n + 1 < total) {
       int hq2, q02;
       pair(n + 1, hq2, q02);
-      load_aparts<D>(A, muqs, (size_t)b * H + hk * G + hq2, nqb, q02 + r, hl);
+      load_aparts<D>(A, muq_head(hq2), nqb, q02 + r, hl);
     }
-    float* dsh = ds + bh * ds_head_elems(CAUSAL, nqb, Npad);
+    float* dsh = ds + ds_off(sq, CAUSAL, hk * G + hq);
     // lane holds Q blocks q0 + 8a + 4hl + e (e < 4) of key column j
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -706,42 +731,62 @@ __global__ void unpermute_v(const uint8_t* __restrict__ vc, uint8_t* __restrict_
   }
 }
 
+// the sequence table of a varlen batch, 64 entries per launch, passed by value
+struct SeqChunk {
+  Seq e[64];
+  int first, count;
+};
+__global__ void write_seq_table(SeqChunk c, Seq* dst) {
+  if ((int)threadIdx.x < c.count) dst[c.first + threadIdx.x] = c.e[threadIdx.x];
+}
+
 template <int D>
 hipError_t launch_prologue_d(const Dims& Dm, const Ptrs& P, hipStream_t s) {
   const float R = Dm.qk_bits == 4 ? 7.f : 127.f;
+  const Geo g = make_geo(Dm, P.seqs);
   const int nkv = Dm.B * Dm.Hkv * D;
   init_stats<<<(nkv + 255) / 256, 256, 0, s>>>(P.ksum, P.vamax, nkv);
   const dim3 gs((Dm.N + 255) / 256, Dm.B * Dm.Hkv), gq(Dm.nkb, Dm.B * Dm.Hkv);
   if (Dm.pv_bits == 16) {
-    kv_stats<D, false><<<gs, 256, 0, s>>>(P.k, P.v, P.ksum, P.vamax, Dm.N);
+    kv_stats<D, false><<<gs, 256, 0, s>>>(P.k, P.v, P.ksum, P.vamax, g);
     kv_quant<D, true><<<gq, 256, 0, s>>>(P.k, P.v, P.ksum, P.vamax, P.kcodes, P.vcodes, P.kscale, P.muk,
-                                         P.vscale, Dm.N, Dm.Npad, Dm.nkb, R);
+                                         P.vscale, g, R);
   } else {
-    kv_stats<D, true><<<gs, 256, 0, s>>>(P.k, P.v, P.ksum, P.vamax, Dm.N);
+    kv_stats<D, true><<<gs, 256, 0, s>>>(P.k, P.v, P.ksum, P.vamax, g);
     kv_quant<D, false><<<gq, 256, 0, s>>>(P.k, P.v, P.ksum, P.vamax, P.kcodes, P.vcodes, P.kscale, P.muk,
-                                          P.vscale, Dm.N, Dm.Npad, Dm.nkb, R);
+                                          P.vscale, g, R);
   }
-  q_quant<D><<<dim3(Dm.nqb, Dm.B * Dm.H), 256, 0, s>>>(P.q, P.qcodes, P.qscale, P.muq, P.muqs, Dm.N, Dm.Npad,
-                                                         Dm.nqb, R);
+  q_quant<D><<<dim3(Dm.nqb, Dm.B * Dm.H), 256, 0, s>>>(P.q, P.qcodes, P.qscale, P.muq, P.muqs, g, R);
   const float k2 = (float)(1.4426950408889634 / sqrt((double)D));
   // the K-block form pays off when each key block serves many Q blocks
   if ((size_t)(Dm.H / Dm.Hkv) * Dm.nqb >= 1024) {
-    const dim3 g(Dm.nkb, Dm.B * Dm.Hkv);
+    const dim3 gr(Dm.nkb, Dm.B * Dm.Hkv);
     if (Dm.causal)
-      delta_s_kblock<D, true><<<g, 256, 0, s>>>(P.k, P.muk, P.muqs, P.ds, Dm.H, Dm.Hkv, Dm.N, Dm.Npad, Dm.nqb, k2);
+      delta_s_kblock<D, true><<<gr, 256, 0, s>>>(P.k, P.muk, P.muqs, P.ds, g, k2);
     else
-      delta_s_kblock<D, false><<<g, 256, 0, s>>>(P.k, P.muk, P.muqs, P.ds, Dm.H, Dm.Hkv, Dm.N, Dm.Npad, Dm.nqb, k2);
+      delta_s_kblock<D, false><<<gr, 256, 0, s>>>(P.k, P.muk, P.muqs, P.ds, g, k2);
   } else {
-    const dim3 g((Dm.Npad + 255) / 256, (Dm.nqb + 31) / 32, Dm.B * Dm.H);
+    const dim3 gr((Dm.Npad + 255) / 256, (Dm.nqb + 31) / 32, Dm.B * Dm.H);
     if (Dm.causal)
-      delta_s_qtile<D, true><<<g, 256, 0, s>>>(P.k, P.muk, P.muq, P.ds, Dm.H, Dm.Hkv, Dm.N, Dm.Npad, Dm.nqb, k2);
+      delta_s_qtile<D, true><<<gr, 256, 0, s>>>(P.k, P.muk, P.muq, P.ds, g, k2);
     else
-      delta_s_qtile<D, false><<<g, 256, 0, s>>>(P.k, P.muk, P.muq, P.ds, Dm.H, Dm.Hkv, Dm.N, Dm.Npad, Dm.nqb, k2);
+      delta_s_qtile<D, false><<<gr, 256, 0, s>>>(P.k, P.muk, P.muq, P.ds, g, k2);
   }
   return hipGetLastError();
 }
 
 }  // namespace
+
+hipError_t launch_seq_table(const Seq* host, int n, Seq* dev, hipStream_t s) {
+  for (int first = 0; first < n; first += 64) {
+    SeqChunk c{};
+    c.first = first;
+    c.count = n - first < 64 ? n - first : 64;
+    for (int i = 0; i < c.count; ++i) c.e[i] = host[first + i];
+    write_seq_table<<<1, 64, 0, s>>>(c, dev);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_prologue(const Dims& D, const Ptrs& P, hipStream_t s) {
   return D.d == 128 ? launch_prologue_d<128>(D, P, s) : launch_prologue_d<64>(D, P, s);

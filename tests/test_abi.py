@@ -128,3 +128,45 @@ def test_python_wrapper_rejects_unsupported(pkg):
         pkg.sageattn(q, q, q)                     # CPU tensors
     with pytest.raises(ValueError):
         pkg.sageattn(q.float(), q, q)
+
+
+def test_problem_descriptor_validation(pkg):
+    lib = pkg._lib
+    n = ctypes.c_size_t(0)
+    ok = pkg.Problem(2, 4, 2, 300, 64, True, 8, 8, "NHD")
+    assert lib.sage_attn_workspace_bytes_ex(ok.ref, ctypes.byref(n)) == 0
+    assert n.value == pkg.workspace_bytes(2, 4, 2, 300, 64, True, 8)     # layout does not change the workspace
+    bad = pkg.Problem(2, 4, 2, 300, 64, True, 8, 8, "NHD")
+    bad.c.layout = 2
+    assert lib.sage_attn_workspace_bytes_ex(bad.ref, ctypes.byref(n)) == -1
+    bad.c.layout, bad.c.dtype = 0, 7
+    assert lib.sage_attn_workspace_bytes_ex(bad.ref, ctypes.byref(n)) == -1
+    assert lib.sage_attn_workspace_bytes_ex(None, ctypes.byref(n)) == -1
+    for cu, status in (([0, 5, 9], 0), ([1, 5, 9], -1), ([0, 5, 5], -1), ([0, 5, 3], -1),
+                       ([0, 1, (1 << 23) + 2], -2)):
+        p = pkg.Problem(2, 4, 2, 0, 64, True, 8, 8, "HND", cu_seqlens=cu)
+        assert lib.sage_attn_workspace_bytes_ex(p.ref, ctypes.byref(n)) == status, cu
+    fake = ctypes.c_void_p(0x1000)
+    p = pkg.Problem(2, 4, 2, 0, 64, True, 8, 8, "HND", cu_seqlens=[0, 5, 9])
+    assert lib.sage_attn_fwd_ex(p.ref, fake, fake, None, fake, ctypes.c_void_p(0x100000), 1 << 30, None) == -1
+    assert lib.sage_attn_fwd_ex(p.ref, fake, fake, fake, fake, None, 1 << 30, None) == -3
+
+
+def test_varlen_workspace_is_per_sequence(pkg):
+    """A varlen batch needs the fixed-length sections of each sequence plus its table: one
+    sequence of n tokens takes at least the workspace of the fixed-length problem of length n."""
+    n = ctypes.c_size_t(0)
+    p = pkg.Problem(1, 4, 2, 0, 128, True, 8, 8, "HND", cu_seqlens=[0, 1000])
+    assert pkg._lib.sage_attn_workspace_bytes_ex(p.ref, ctypes.byref(n)) == 0
+    assert n.value >= pkg.workspace_bytes(1, 4, 2, 1000, 128, True, 8)
+    p2 = pkg.Problem(2, 4, 2, 0, 128, True, 8, 8, "HND", cu_seqlens=[0, 1000, 1100])
+    m = ctypes.c_size_t(0)
+    assert pkg._lib.sage_attn_workspace_bytes_ex(p2.ref, ctypes.byref(m)) == 0
+    assert m.value > n.value
+
+
+def test_bf16_is_reported_unsupported_for_now(pkg):
+    n = ctypes.c_size_t(0)
+    import torch
+    p = pkg.Problem(1, 2, 2, 256, 64, False, 8, 8, "HND", dtype=torch.bfloat16)
+    assert pkg._lib.sage_attn_workspace_bytes_ex(p.ref, ctypes.byref(n)) == -2

@@ -7,7 +7,10 @@ Bars (the oracle is the reference):
     moves O by at most 2^-11 of sum p |v| / l per element, far inside it;
   * raw int32 QK^T tiles from the attention kernel's MFMA path: bit-exact;
   * Delta_S: within fp32 accumulation error of the fp64 value;
-  * O: max|O_gpu - O_oracle| / max|O_oracle| <= 2e-3 and cosine similarity >= 0.999.
+  * O: max|O_gpu - O_oracle| / max|O_oracle| <= 2e-3 and cosine similarity >= 0.999.  In the
+    FP8 mode an element may move further by the oracle's fp8_midpoint_slack: P~ decisions that sit
+    within 2^-14 of an E4M3 rounding midpoint have two correct codes (fp32 logits on the GPU,
+    fp64 in the oracle), and either is accepted; elsewhere the slack is zero.
 Small cases compare every element; the full-size workloads compare full prologue tensors of
 sampled heads and the outputs of sampled query blocks (first, middle, last) of those heads.
 """
@@ -48,14 +51,25 @@ def _head_slice(q, k, v, b, h, H, Hkv):
             np.ascontiguousarray(v[b:b + 1, hk:hk + 1]))
 
 
-def _check_o(o_gpu, o_ref, what):
+def _check_o(o_gpu, o_ref, what, slack=None):
     o_gpu = o_gpu.astype(np.float64)
-    err = np.abs(o_gpu - o_ref).max()
+    diff = np.abs(o_gpu - o_ref)
+    err = diff.max()
     scale = np.abs(o_ref).max()
     cos = (o_gpu * o_ref).sum() / math.sqrt((o_gpu ** 2).sum() * (o_ref ** 2).sum())
-    _say(f"  {what}: max|dO|/max|O| = {err / scale:.3e}  cos = {cos:.6f}")
-    assert err <= O_REL_TOL * scale, f"{what}: max abs err {err} > {O_REL_TOL} * {scale}"
+    allowed = O_REL_TOL * scale + (0.0 if slack is None else slack)
+    beyond = diff > O_REL_TOL * scale
+    _say(f"  {what}: max|dO|/max|O| = {err / scale:.3e}  cos = {cos:.6f}"
+         + (f"  ({int(beyond.sum())} elements within midpoint slack)" if beyond.any() else ""))
+    worst = np.unravel_index(np.argmax(diff - allowed), diff.shape)
+    assert np.all(diff <= allowed), (f"{what}: |dO| {diff[worst]} at {worst} > {O_REL_TOL} * {scale} + slack "
+                                     f"{0.0 if slack is None else slack[worst]}")
     assert cos >= COS_MIN, f"{what}: cos {cos}"
+
+
+def _slack(pro, b, h, qb, pv_bits=8):
+    """fp8_midpoint_slack of one Q block (None in the fp16 mode, which has no P~ codes)."""
+    return osage.fp8_midpoint_slack(pro, b, h, qb) if pv_bits == 8 else None
 
 
 def _check_prologue(dbg, pro, b, h, hk_gpu, what):
@@ -131,6 +145,7 @@ def test_small_case_full_parity(sa, name, w, pv_bits):
     dev, o_gpu, dbg = _run(sa, q, k, v, w.causal, w.qk_bits, pv_bits=pv_bits)
     pro = osage.prologue(q, k, v, w.causal, w.qk_bits, quant_pv=qpv)
     o_ref = np.zeros((w.B, w.H, w.N, w.d))
+    slack = np.zeros_like(o_ref)
     for b in range(w.B):
         for h in range(w.H):
             hk = h // (w.H // w.Hkv)
@@ -139,7 +154,9 @@ def test_small_case_full_parity(sa, name, w, pv_bits):
             for qb in range(pro.nqb):
                 r0, r1 = qb * 128, min(w.N, qb * 128 + 128)
                 o_ref[b, h, r0:r1] = osage.attend_block(pro, b, h, qb)
-    _check_o(o_gpu, o_ref, name)
+                if qpv:
+                    slack[b, h, r0:r1] = osage.fp8_midpoint_slack(pro, b, h, qb)
+    _check_o(o_gpu, o_ref, name, slack)
     # raw int32 tiles of (b=last, h=last) for every (qb, kb)
     b, h = w.B - 1, w.H - 1
     for qb in range(pro.nqb):
@@ -216,7 +233,7 @@ def test_full_size_sampled_parity(sa, name, pv_bits):
         for qb in sorted({0, nqb // 2, nqb - 1}):
             r0, r1 = qb * 128, min(w.N, qb * 128 + 128)
             ref = osage.attend_block(ph, 0, 0, qb)
-            _check_o(o[b, h, r0:r1].cpu().numpy(), ref, f"{name} b{b} h{h} qb{qb}")
+            _check_o(o[b, h, r0:r1].cpu().numpy(), ref, f"{name} b{b} h{h} qb{qb}", _slack(ph, 0, 0, qb, pv_bits))
             kb = qb // 2
             tile = sa.qk_tile_debug(qd, kd, vd, b, h, qb, kb, w.causal, w.qk_bits, pv_bits).cpu().numpy()
             c0, c1 = kb * 128, min(w.N, kb * 128 + 128)
@@ -269,4 +286,84 @@ def test_many_q_blocks_per_key_block(sa, causal):
         ph = osage.prologue(*_head_slice(q, k, v, 0, h, w.H, w.Hkv), causal, 8)
         _check_prologue(dbg, ph, 0, h, 0, f"many-q-blocks h{h}")
         ref = np.concatenate([osage.attend_block(ph, 0, 0, qb) for qb in range(ph.nqb)])
-        _check_o(o[0, h], ref, f"many-q-blocks h{h}")
+        slack = np.concatenate([osage.fp8_midpoint_slack(ph, 0, 0, qb) for qb in range(ph.nqb)])
+        _check_o(o[0, h], ref, f"many-q-blocks h{h}", slack)
+
+
+# ------------------------------------------------------------------------------------------
+# variable-length batches and the NHD layout
+# ------------------------------------------------------------------------------------------
+VARLEN = [
+    ("varlen-d128-causal-int8", [1, 127, 128, 129, 300], 4, 2, 128, True, 8, 8),
+    ("varlen-d64-int4", [200, 64, 700], 2, 1, 64, False, 4, 8),
+    ("varlen-d128-causal-pv16", [130, 257, 5], 2, 2, 128, True, 8, 16),
+    ("varlen-d64-int4-pv16", [384, 33], 4, 4, 64, False, 4, 16),
+]
+
+
+@pytest.mark.parametrize("name,lens,H,Hkv,d,causal,bits,pv", VARLEN, ids=[c[0] for c in VARLEN])
+def test_varlen_parity(sa, name, lens, H, Hkv, d, causal, bits, pv):
+    """Every sequence against the oracle, and bit-identical to a fixed-length call on that
+    sequence alone (the varlen path must reproduce the per-sequence computation exactly)."""
+    from workloads import VarlenWorkload, make_varlen_inputs
+    w = VarlenWorkload(name, tuple(lens), H, Hkv, d, causal, bits, q_bias_std=1.0)
+    _say(f"[case {name}] lens {lens} H{H} Hkv{Hkv} d{d} causal={causal} bits={bits} pv={pv}")
+    q, k, v = make_varlen_inputs(w, seed=5)
+    cu = w.cu_seqlens
+    qd, kd, vd = _to_dev(q, k, v)
+    o = sa.sageattn_varlen(qd, kd, vd, cu, is_causal=causal, qk_bits=bits, pv_bits=pv)
+    torch.cuda.synchronize()
+    ref = osage.sage_attention_varlen(q, k, v, cu, causal, bits, quant_pv=pv == 8)
+    o_np = o.cpu().numpy()
+    for s in range(w.B):
+        a, b = cu[s], cu[s + 1]
+        slack = None
+        if pv == 8:                                  # per head and Q block of this sequence
+            slack = np.zeros((b - a, H, d))
+            for h in range(H):
+                hk = h // (H // Hkv)
+                sl = lambda x, hh: np.ascontiguousarray(x[a:b, hh:hh + 1].transpose(1, 0, 2))[None]
+                ph = osage.prologue(sl(q, h), sl(k, hk), sl(v, hk), causal, bits)
+                for qb in range(ph.nqb):
+                    slack[qb * 128:(qb + 1) * 128, h] = osage.fp8_midpoint_slack(ph, 0, 0, qb)
+        _check_o(o_np[a:b], ref[a:b], f"{name} seq {s} (n={b - a})", slack)
+        fixed = sa.sageattn(*(x[a:b].transpose(0, 1).contiguous()[None] for x in (qd, kd, vd)),
+                            is_causal=causal, qk_bits=bits, pv_bits=pv)
+        assert torch.equal(fixed[0].transpose(0, 1), o[a:b]), f"{name} seq {s}: varlen != fixed-length"
+
+
+@pytest.mark.parametrize("w", [custom(2, 4, 2, 300, 128, True, 8, q_bias_std=1.0),
+                               custom(1, 2, 1, 257, 64, False, 4)], ids=["d128-causal-gqa", "d64-int4"])
+@pytest.mark.parametrize("pv", [8, 16])
+def test_nhd_layout_matches_hnd(sa, w, pv):
+    q, k, v = _to_dev(*make_inputs(w, seed=6))
+    o_hnd = sa.sageattn(q, k, v, is_causal=w.causal, qk_bits=w.qk_bits, pv_bits=pv)
+    t = lambda x: x.transpose(1, 2).contiguous()
+    o_nhd = sa.sageattn(t(q), t(k), t(v), is_causal=w.causal, qk_bits=w.qk_bits, pv_bits=pv, tensor_layout="NHD")
+    torch.cuda.synchronize()
+    assert o_nhd.shape == (w.B, w.N, w.H, w.d)
+    assert torch.equal(o_nhd, t(o_hnd))
+
+
+def test_varlen_full_size_sampled(sa):
+    """The 16-prompt mixed-length batch: sampled sequences (first, longest, last), heads 0 and
+    H - 1, first / middle / last query blocks against the oracle run on that sequence."""
+    from workloads import VARLEN_WORKLOADS, make_varlen_inputs
+    w = VARLEN_WORKLOADS["varlen"]
+    _say(f"[case varlen] {w.B} sequences, T={w.T}, max {w.N}, H{w.H} Hkv{w.Hkv} d{w.d} causal={w.causal}")
+    q, k, v = make_varlen_inputs(w, seed=0)
+    cu = w.cu_seqlens
+    qd, kd, vd = _to_dev(q, k, v)
+    o = sa.sageattn_varlen(qd, kd, vd, cu, is_causal=w.causal, qk_bits=w.qk_bits)
+    torch.cuda.synchronize()
+    longest = int(np.argmax(w.lens))
+    for s in sorted({0, longest, w.B - 1}):
+        a, b = cu[s], cu[s + 1]
+        for h in (0, w.H - 1):
+            hk = h // (w.H // w.Hkv)
+            sl = lambda x, hh: np.ascontiguousarray(x[a:b, hh:hh + 1].transpose(1, 0, 2))[None]
+            ph = osage.prologue(sl(q, h), sl(k, hk), sl(v, hk), w.causal, w.qk_bits)
+            for qb in sorted({0, ph.nqb // 2, ph.nqb - 1}):
+                r0, r1 = qb * 128, min(ph.N, qb * 128 + 128)
+                ref = osage.attend_block(ph, 0, 0, qb)
+                _check_o(o[a + r0:a + r1, h].cpu().numpy(), ref, f"varlen seq {s} h{h} qb{qb}", _slack(ph, 0, 0, qb))

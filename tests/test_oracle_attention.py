@@ -173,3 +173,44 @@ def test_brute_force_tiny(causal, R):
     o = sage.sage_attention(q, k, v, causal, 8 if R == 127 else 4, g)
     ref = _brute(q, k, v, causal, R, 8, 8, 8, 8, 4, 448.0, 448.0)
     assert np.abs(o - ref).max() < 1e-9 * max(1.0, np.abs(ref).max())
+
+
+def _attend_perturbed(pro, b, h, qb, eps):
+    """The online softmax and FP8 P~V of one Q block with every p scaled by (1 + eps) before its
+    FP8 rounding (l keeps the exact p): a stand-in for any faithful computation of the logits."""
+    g = pro.geom
+    hk = pro.kv_head(h)
+    z = sage.logits(pro, b, h, qb)
+    vq = fp8.decode(pro.v_codes[b, hk])
+    m = np.full(z.shape[0], -np.inf)
+    l = np.zeros(z.shape[0])
+    acc = np.zeros((z.shape[0], pro.d))
+    for kb in range(pro.nkb):
+        zb = z[:, kb * g.bk:min(pro.N, (kb + 1) * g.bk)]
+        m_new = np.maximum(m, zb.max(axis=1))
+        alpha = np.where(np.isfinite(m), np.exp(m - m_new), 0.0)
+        p = np.exp(zb - m_new[:, None])
+        l = l * alpha + p.sum(axis=1)
+        pt = fp8.round_sat((p * (1.0 + eps) * g.p_range).astype(np.float32))
+        acc = acc * alpha[:, None] + pt @ vq[kb * g.bk:min(pro.N, (kb + 1) * g.bk)]
+        m = m_new
+    return acc * pro.v_delta[b, hk].astype(np.float64)[None, :] / (g.p_range * l[:, None])
+
+
+def test_fp8_midpoint_slack_bounds_flipped_decisions():
+    """Perturbing every p by 2^-15 (relative) flips the P~ codes that sit within that distance of
+    an E4M3 midpoint; the output must move by no more than fp8_midpoint_slack (rel 2^-14) allows,
+    and some codes must actually flip (the bound is exercised)."""
+    q, k, v = make_inputs(custom(1, 2, 1, 300, 64, True, 8, q_bias_std=1.0), seed=31)
+    pro = sage.prologue(q, k, v, True, 8)
+    moved = 0
+    for h in range(2):
+        for qb in range(pro.nqb):
+            base = sage.attend_block(pro, 0, h, qb)
+            slack = sage.fp8_midpoint_slack(pro, 0, h, qb, rel=2.0 ** -14)
+            assert np.all(slack >= 0)
+            for eps in (2.0 ** -15, -2.0 ** -15):
+                d = np.abs(_attend_perturbed(pro, 0, h, qb, eps) - base)
+                assert np.all(d <= slack + 1e-12)
+                moved += int(np.count_nonzero(d > 1e-12))
+    assert moved > 0

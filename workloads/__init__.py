@@ -13,6 +13,10 @@ and a kernel sweep at N = 8K, d = 128.  Recipe (all configs):
   then the per-(head, channel) K bias; then the per-(head, channel) Q bias; then the
   outlier (head, channel) mask; finally cast to fp16 with round-to-nearest-even.
   Biases have shape [1, heads, 1, d]: shared by batch and tokens.  V gets no bias.
+
+Variable-length batches (make_varlen_inputs) pack sequences back to back, [T, heads, d]; the
+same draw order applies, but every sequence gets its own K and Q biases (different prompts
+have different channel offsets, which is what per-sequence smoothing has to absorb).
 """
 
 from __future__ import annotations
@@ -88,4 +92,72 @@ def make_inputs(w: Workload | str, seed: int = 0):
             h, c = divmod(int(p), w.d)
             q[:, h, :, c] *= np.float32(w.outlier_scale)
             k[:, h * w.Hkv // w.H, :, c] *= np.float32(w.outlier_scale)
+    return q.astype(np.float16), k.astype(np.float16), v.astype(np.float16)
+
+
+@dataclass(frozen=True)
+class VarlenWorkload:
+    name: str
+    lens: tuple
+    H: int
+    Hkv: int
+    d: int
+    causal: bool
+    qk_bits: int
+    k_bias_std: float = 4.0
+    q_bias_std: float = 0.0
+
+    @property
+    def B(self) -> int:
+        return len(self.lens)
+
+    @property
+    def T(self) -> int:
+        return int(sum(self.lens))
+
+    @property
+    def N(self) -> int:
+        return int(max(self.lens))
+
+    @property
+    def cu_seqlens(self) -> list:
+        return [0] + [int(x) for x in np.cumsum(self.lens)]
+
+    @property
+    def ops(self) -> float:
+        """Numerator of the effective-TOPS metric summed over sequences: 4*H*n^2*d each,
+        halved when causal."""
+        o = sum(4.0 * self.H * n * n * self.d for n in self.lens)
+        return o / 2 if self.causal else o
+
+
+def varlen_lengths(n_seq: int, lo: int, hi: int, seed: int) -> tuple:
+    """n_seq lengths drawn log-uniformly from [lo, hi] (rounded to integers)."""
+    rng = np.random.default_rng(seed)
+    return tuple(int(round(x)) for x in np.exp(rng.uniform(np.log(lo), np.log(hi), n_seq)))
+
+
+VARLEN_WORKLOADS = {
+    # a prefill batch of 16 prompts of mixed length (256 .. 16K tokens, log-uniform), causal GQA
+    "varlen": VarlenWorkload("varlen", varlen_lengths(16, 256, 16384, seed=7), 32, 8, 128, True, 8,
+                             q_bias_std=1.0),
+}
+
+
+def make_varlen_inputs(w: VarlenWorkload, seed: int = 0):
+    """q [T,H,d], k/v [T,Hkv,d] as numpy float16 (recipe above, biases per sequence)."""
+    rng = np.random.default_rng(seed)
+    T = w.T
+    q = rng.standard_normal((T, w.H, w.d), dtype=np.float32)
+    k = rng.standard_normal((T, w.Hkv, w.d), dtype=np.float32)
+    v = rng.standard_normal((T, w.Hkv, w.d), dtype=np.float32)
+    cu = w.cu_seqlens
+    if w.k_bias_std:
+        kb = (w.k_bias_std * rng.standard_normal((w.B, w.Hkv, w.d))).astype(np.float32)
+        for s in range(w.B):
+            k[cu[s]:cu[s + 1]] += kb[s]
+    if w.q_bias_std:
+        qb = (w.q_bias_std * rng.standard_normal((w.B, w.H, w.d))).astype(np.float32)
+        for s in range(w.B):
+            q[cu[s]:cu[s + 1]] += qb[s]
     return q.astype(np.float16), k.astype(np.float16), v.astype(np.float16)

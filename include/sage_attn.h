@@ -104,8 +104,11 @@ int sage_get_config(sage_config_t* out);
  *           top-left aligned within it) and has its own smoothing means and quantization
  *           groups, exactly as if it were a batch of one.  The array is read during the
  *           call only.  Sequence lengths are at most 2^23.
- *   dtype   SAGE_DTYPE_FP16 (q, k, v and o fp16).  SAGE_DTYPE_BF16 is reserved and
- *           returns SAGE_ERR_UNSUPPORTED.
+ *   dtype   SAGE_DTYPE_FP16 or SAGE_DTYPE_BF16: q, k, v and o all of that type.  With bf16
+ *           the smoothing means stay exact (column sums in a multi-limb integer accumulator,
+ *           then RN32(RN64(sum) / n) as for fp16), O is rounded to bf16, and with pv_bits = 16
+ *           P and V enter the bf16 MFMA (V keeps its input type; P is rounded to bf16).
+ *           Inputs must be finite.
  * Every tensor is contiguous in its stated shape.  All other fields as for sage_attn_fwd.
  */
 #define SAGE_LAYOUT_HND 0
@@ -182,6 +185,13 @@ int sage_quant_debug(const void* q, const void* k, const void* v, int B, int H, 
                      size_t workspace_bytes, void* stream, void* mu_k, void* k_codes,
                      void* k_scales, void* v_codes, void* v_scales, void* mu_q, void* q_codes,
                      void* q_scales, void* delta_s);
+
+/* sage_quant_debug for a fixed-length problem *p in any layout and dtype (varlen problems
+ * return SAGE_ERR_INVALID_ARG); the outputs have the plain layouts above. */
+int sage_quant_debug_ex(const sage_problem_t* p, const void* q, const void* k, const void* v,
+                        void* workspace, size_t workspace_bytes, void* stream, void* mu_k,
+                        void* k_codes, void* k_scales, void* v_codes, void* v_scales, void* mu_q,
+                        void* q_codes, void* q_scales, void* delta_s);
 
 /*
  * Test/debug: run the prologue, then the attention kernel's own integer-MFMA QK^T code

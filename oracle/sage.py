@@ -116,16 +116,29 @@ def fixed_point_colsum(x16: np.ndarray) -> np.ndarray:
     return xi.sum(axis=0, dtype=np.int64)
 
 
-def exact_mean(x16: np.ndarray) -> np.ndarray:
-    """O1: RN32(RN64(exact column sum) / (n * 2**24)) of an fp16 [n, d] array.
+def is_bf16(x: np.ndarray) -> bool:
+    """bf16 inputs are passed as float32 arrays whose values are all bf16 numbers (numpy has no
+    bf16 type): the low 16 bits of every element are zero."""
+    x = np.asarray(x)
+    return x.dtype == F32 and not np.any(x.view(np.uint32) & 0xFFFF)
+
+
+def exact_mean(x: np.ndarray) -> np.ndarray:
+    """O1: RN32(RN64(RN64(exact column sum) / n)) of an fp16 or bf16 [n, d] array.
 
     Reading: the pages fix neither the order nor the precision of the mean; this rule makes
     the result independent of summation order, so a parallel reduction can match it bit
-    for bit.
+    for bit.  fp16: the exact sum is an int64 count of 2**-24 units.  bf16 spans 2**-133 ..
+    2**128, beyond any int64 fixed point: math.fsum returns the correctly rounded fp64 value of
+    the exact sum directly.
     """
-    n = x16.shape[0]
-    s = fixed_point_colsum(x16)
-    return (s.astype(F64) / F64(n * 2.0 ** 24)).astype(F32)
+    n = x.shape[0]
+    if x.dtype == np.float16:
+        s = fixed_point_colsum(x)
+        return (s.astype(F64) / F64(n * 2.0 ** 24)).astype(F32)
+    assert is_bf16(x), "inputs must be fp16 or bf16 values (float32 arrays)"
+    s = np.array([math.fsum(x[:, c].astype(F64)) for c in range(x.shape[1])], F64)
+    return (s / F64(n)).astype(F32)
 
 
 def smooth(x16: np.ndarray, mu: np.ndarray) -> np.ndarray:
@@ -226,7 +239,8 @@ class Prologue:
 def prologue(q, k, v, causal: bool = False, qk_bits: int = 8, geom: Geometry = DEFAULT, *,
              quant_qk: bool = True, quant_pv: bool = True, smooth_q: bool = True,
              smooth_k: bool = True) -> Prologue:
-    """Steps O1-O4 and O8 on fp16 inputs q [B,H,N,d], k/v [B,Hkv,N,d] (numpy float16).
+    """Steps O1-O4 and O8 on fp16 inputs q [B,H,N,d], k/v [B,Hkv,N,d] (numpy float16), or on
+    bf16 inputs (float32 arrays of bf16 values, see is_bf16).
 
     The switches turn parts of the method off; they exist so that tests can reduce the
     oracle to textbook attention (all off) and check each part against it.
@@ -234,7 +248,8 @@ def prologue(q, k, v, causal: bool = False, qk_bits: int = 8, geom: Geometry = D
     q = np.asarray(q)
     k = np.asarray(k)
     v = np.asarray(v)
-    assert q.dtype == np.float16 and k.dtype == np.float16 and v.dtype == np.float16
+    assert q.dtype == k.dtype == v.dtype
+    assert q.dtype == np.float16 or (is_bf16(q) and is_bf16(k) and is_bf16(v)), "fp16 or bf16 inputs"
     B, H, N, d = q.shape
     Hkv = k.shape[1]
     assert k.shape == (B, Hkv, N, d) and v.shape == (B, Hkv, N, d) and H % Hkv == 0

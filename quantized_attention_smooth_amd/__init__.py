@@ -33,7 +33,7 @@ SAGE_ERR_HIP = -4
 EXPORTS = ("sage_get_config", "sage_attn_workspace_bytes", "sage_attn_fwd", "sage_attn_prologue",
            "sage_attn_attend", "sage_quant_debug", "sage_qk_tile_debug", "sage_status_string",
            "sage_last_error", "sage_attn_workspace_bytes_ex", "sage_attn_fwd_ex", "sage_attn_prologue_ex",
-           "sage_attn_attend_ex")
+           "sage_attn_attend_ex", "sage_quant_debug_ex")
 
 LAYOUTS = {"HND": 0, "NHD": 1}
 DTYPES = {torch.float16: 0, torch.bfloat16: 1}
@@ -102,13 +102,14 @@ def _load() -> ctypes.CDLL:
     lib.sage_attn_fwd_ex.argtypes = [PP, P, P, P, P, P, S, P]
     lib.sage_attn_prologue_ex.argtypes = [PP, P, P, P, P, S, P]
     lib.sage_attn_attend_ex.argtypes = [PP, P, P, S, P]
+    lib.sage_quant_debug_ex.argtypes = [PP, P, P, P, P, S, P] + [P] * 9
     lib.sage_status_string.argtypes = [I]
     lib.sage_status_string.restype = ctypes.c_char_p
     lib.sage_last_error.argtypes = []
     lib.sage_last_error.restype = ctypes.c_char_p
     for name in ("sage_get_config", "sage_attn_workspace_bytes", "sage_attn_fwd", "sage_attn_prologue",
                  "sage_attn_attend", "sage_quant_debug", "sage_qk_tile_debug", "sage_attn_workspace_bytes_ex",
-                 "sage_attn_fwd_ex", "sage_attn_prologue_ex", "sage_attn_attend_ex"):
+                 "sage_attn_fwd_ex", "sage_attn_prologue_ex", "sage_attn_attend_ex", "sage_quant_debug_ex"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -292,9 +293,13 @@ def sageattn_varlen(q, k, v, cu_seqlens, is_causal: bool = False, qk_bits: int =
 
 
 def quant_debug(q, k, v, is_causal: bool = False, qk_bits: int = 8, pv_bits: int = 8) -> dict:
-    """Prologue outputs in plain layouts (see sage_quant_debug in include/sage_attn.h); with
-    pv_bits = 16 there are no V codes or scales and those entries are None."""
-    B, H, Hkv, N, d = _shapes(q, k, v)
+    """Prologue outputs in plain layouts (see sage_quant_debug in include/sage_attn.h); q, k, v
+    [B, heads, N, d] fp16 or bf16.  With pv_bits = 16 there are no V codes or scales and those
+    entries are None."""
+    _check_qkv(q, k, v, 4)
+    (B, H, N, d), Hkv = q.shape, k.shape[1]
+    if k.shape[0] != B or k.shape[2] != N or k.shape[3] != d:
+        raise ValueError(f"k/v shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
     nqb = -(-N // get_config()["bq"])
     dev = q.device
     out = {
@@ -310,10 +315,11 @@ def quant_debug(q, k, v, is_causal: bool = False, qk_bits: int = 8, pv_bits: int
     }
     if pv_bits == 16:
         out["v_codes"] = out["v_scales"] = None
-    ws = alloc_workspace(workspace_bytes(B, H, Hkv, N, d, is_causal, qk_bits, pv_bits), dev)
+    pb = Problem(B, H, Hkv, N, d, is_causal, qk_bits, pv_bits, "HND", q.dtype)
+    ws = alloc_workspace(problem_ws_bytes(pb), dev)
     names = ("mu_k", "k_codes", "k_scales", "v_codes", "v_scales", "mu_q", "q_codes", "q_scales", "delta_s")
-    _check(_lib.sage_quant_debug(_ptr(q), _ptr(k), _ptr(v), B, H, Hkv, N, d, int(is_causal), qk_bits, pv_bits,
-                                 _ptr(ws), ws.numel(), _stream(dev), *[_ptr(out[n]) for n in names]))
+    _check(_lib.sage_quant_debug_ex(pb.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(ws), ws.numel(), _stream(dev),
+                                    *[_ptr(out[n]) for n in names]))
     return out
 
 

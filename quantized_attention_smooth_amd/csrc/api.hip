@@ -24,6 +24,7 @@ int hip_fail(hipError_t e, const char* what) {
 // Checks shared by every entry point; fills D (and, for varlen, the sequence table) on success.
 int check_problem(const sage_problem_t* p, sage::Dims* D, std::vector<sage::Seq>* table) {
   if (p == nullptr) return SAGE_ERR_INVALID_ARG;
+  if (p->cu_seqlens != nullptr && table == nullptr) return SAGE_ERR_INVALID_ARG;
   const int B = p->B, H = p->H, Hkv = p->Hkv, d = p->d;
   const bool varlen = p->cu_seqlens != nullptr;
   if (B < 1 || H < 1 || Hkv < 1 || (!varlen && p->N < 1)) return SAGE_ERR_INVALID_ARG;
@@ -34,7 +35,6 @@ int check_problem(const sage_problem_t* p, sage::Dims* D, std::vector<sage::Seq>
   if (d != 64 && d != 128) return SAGE_ERR_UNSUPPORTED;
   if (p->qk_bits != 4 && p->qk_bits != 8) return SAGE_ERR_UNSUPPORTED;
   if (p->pv_bits != 8 && p->pv_bits != 16) return SAGE_ERR_UNSUPPORTED;
-  if (p->dtype != SAGE_DTYPE_FP16) return SAGE_ERR_UNSUPPORTED;
   if ((double)B * Hkv > 65535.0 || (double)B * H > 65535.0) return SAGE_ERR_INVALID_ARG;   // grid.y/z limits
 
   // per-sequence lengths: one N for all, or the differences of cu_seqlens
@@ -72,6 +72,7 @@ int check_problem(const sage_problem_t* p, sage::Dims* D, std::vector<sage::Seq>
   D->nqb = D->Npad / 128;
   D->nkb = D->Npad / 128;
   D->varlen = varlen ? 1 : 0;
+  D->bf16 = p->dtype == SAGE_DTYPE_BF16 ? 1 : 0;
   D->tot_pad = tot_pad;
   D->tot_ds = tot_ds;
   // element strides (channels contiguous)
@@ -215,14 +216,14 @@ int sage_attn_attend(void* o, int B, int H, int Hkv, int N, int d, int causal, i
   return sage_attn_attend_ex(&p, o, workspace, workspace_bytes, stream);
 }
 
-int sage_quant_debug(const void* q, const void* k, const void* v, int B, int H, int Hkv, int N, int d, int causal,
-                     int qk_bits, int pv_bits, void* workspace, size_t workspace_bytes, void* stream, void* mu_k,
-                     void* k_codes, void* k_scales, void* v_codes, void* v_scales, void* mu_q, void* q_codes,
-                     void* q_scales, void* delta_s) {
-  if (!q || !k || !v) return SAGE_ERR_INVALID_ARG;
-  if (pv_bits == 16 && (v_codes || v_scales)) return SAGE_ERR_INVALID_ARG;   // V is not quantized
+int sage_quant_debug_ex(const sage_problem_t* p, const void* q, const void* k, const void* v, void* workspace,
+                        size_t workspace_bytes, void* stream, void* mu_k, void* k_codes, void* k_scales,
+                        void* v_codes, void* v_scales, void* mu_q, void* q_codes, void* q_scales, void* delta_s) {
+  if (!q || !k || !v || p == nullptr) return SAGE_ERR_INVALID_ARG;
+  if (p->cu_seqlens != nullptr) return SAGE_ERR_INVALID_ARG;                  // fixed length only
+  if (p->pv_bits == 16 && (v_codes || v_scales)) return SAGE_ERR_INVALID_ARG;   // V is not quantized
   sage::Dims D;
-  int st = check_dims(B, H, Hkv, N, d, causal, qk_bits, pv_bits, &D);
+  int st = check_problem(p, &D, nullptr);
   if (st != SAGE_OK) return st;
   const sage::Layout L = sage::make_layout(D);
   st = check_ws(workspace, workspace_bytes, L);
@@ -238,6 +239,15 @@ int sage_quant_debug(const void* q, const void* k, const void* v, int B, int H, 
                               static_cast<float*>(delta_s));
   if (e != hipSuccess) return hip_fail(e, "debug copy");
   return SAGE_OK;
+}
+
+int sage_quant_debug(const void* q, const void* k, const void* v, int B, int H, int Hkv, int N, int d, int causal,
+                     int qk_bits, int pv_bits, void* workspace, size_t workspace_bytes, void* stream, void* mu_k,
+                     void* k_codes, void* k_scales, void* v_codes, void* v_scales, void* mu_q, void* q_codes,
+                     void* q_scales, void* delta_s) {
+  const sage_problem_t p = fixed_problem(B, H, Hkv, N, d, causal, qk_bits, pv_bits);
+  return sage_quant_debug_ex(&p, q, k, v, workspace, workspace_bytes, stream, mu_k, k_codes, k_scales, v_codes,
+                             v_scales, mu_q, q_codes, q_scales, delta_s);
 }
 
 int sage_qk_tile_debug(const void* q, const void* k, const void* v, int B, int H, int Hkv, int N, int d, int causal,

@@ -49,6 +49,21 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef __bf16 b8 __attribute__((ext_vector_type(8)));
+typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+
+// The 16-bit float of the fp16 P V path: fp16, or bf16 for bf16 inputs (V keeps its input type)
+template <bool BF> struct PV16T;
+template <> struct PV16T<false> {
+  typedef h8 v8;
+  typedef h2 v2;
+  static __device__ v16f mfma(v8 a, v8 b, v16f c) { return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0); }
+};
+template <> struct PV16T<true> {
+  typedef b8 v8;
+  typedef b2 v2;
+  static __device__ v16f mfma(v8 a, v8 b, v16f c) { return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0); }
+};
 
 constexpr float kLog2Pr = 8.807354922057604f;   // log2(448)
 
@@ -209,8 +224,9 @@ __device__ inline int xcd_remap(int bid, int total) {
   return x * q + min(x, r) + k;
 }
 
-template <int D, bool CAUSAL, bool DUMP, bool QK4, bool PV16>
+template <int D, bool CAUSAL, bool DUMP, bool QK4, bool PV16, bool BF>
 __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
+  typedef PV16T<BF> PT;
   __shared__ Smem<D, PV16> sm;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, col = lane & 31, half = lane >> 5;
 
@@ -355,7 +371,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
       float lsum = 0.f;
 #pragma unroll
       for (int t = 0; t < BK / 32; ++t) {
-        h8 pb[2];
+        typename PT::v8 pb[2];
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq) {
           const float p0 = __builtin_amdgcn_exp2f(z[t][4 * qq + 0] - mo);
@@ -363,8 +379,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
           const float p2 = __builtin_amdgcn_exp2f(z[t][4 * qq + 2] - mo);
           const float p3 = __builtin_amdgcn_exp2f(z[t][4 * qq + 3] - mo);
           lsum += (p0 + p1) + (p2 + p3);
-          const h2 lo = __builtin_convertvector((f2){p0, p1}, h2);
-          const h2 hi = __builtin_convertvector((f2){p2, p3}, h2);
+          const typename PT::v2 lo = __builtin_convertvector((f2){p0, p1}, typename PT::v2);
+          const typename PT::v2 hi = __builtin_convertvector((f2){p2, p3}, typename PT::v2);
           const int o = 4 * (qq & 1);
           pb[qq >> 1][o + 0] = lo[0];
           pb[qq >> 1][o + 1] = lo[1];
@@ -377,8 +393,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
           const int hc = (half ^ v16swz(c)) * 16;
 #pragma unroll
           for (int m = 0; m < 2; ++m) {
-            const h8 va = *reinterpret_cast<const h8*>(sm.v[0] + ((2 * t + m) * D + c) * 32 + hc);
-            og[ct] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pb[m], og[ct], 0, 0, 0);
+            const typename PT::v8 va = *reinterpret_cast<const typename PT::v8*>(sm.v[0] + ((2 * t + m) * D + c) * 32 + hc);
+            og[ct] = PT::mfma(va, pb[m], og[ct]);
           }
         }
         // keep the scheduler from hoisting later tiles' V reads (registers) above this one
@@ -452,12 +468,17 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
       for (int qq = 0; qq < 4; ++qq) {
         const int c0 = 32 * ct + 8 * qq + 4 * half;
         const float4 sc = PV16 ? make_float4(1.f, 1.f, 1.f, 1.f) : *reinterpret_cast<const float4*>(vs + c0);
-        union { __half hh[4]; uint2 u; } pk;
-        pk.hh[0] = __float2half_rn(og[ct][4 * qq + 0] * sc.x * inv_l);
-        pk.hh[1] = __float2half_rn(og[ct][4 * qq + 1] * sc.y * inv_l);
-        pk.hh[2] = __float2half_rn(og[ct][4 * qq + 2] * sc.z * inv_l);
-        pk.hh[3] = __float2half_rn(og[ct][4 * qq + 3] * sc.w * inv_l);
-        *reinterpret_cast<uint2*>(orow + c0) = pk.u;
+        const float y0 = og[ct][4 * qq + 0] * sc.x * inv_l, y1 = og[ct][4 * qq + 1] * sc.y * inv_l;
+        const float y2 = og[ct][4 * qq + 2] * sc.z * inv_l, y3 = og[ct][4 * qq + 3] * sc.w * inv_l;
+        uint2 pk;                               // RNE to the output type (the input type)
+        if (BF) {
+          const b2 lo = __builtin_convertvector((f2){y0, y1}, b2), hi = __builtin_convertvector((f2){y2, y3}, b2);
+          pk = make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+        } else {
+          const h2 lo = __builtin_convertvector((f2){y0, y1}, h2), hi = __builtin_convertvector((f2){y2, y3}, h2);
+          pk = make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+        }
+        *reinterpret_cast<uint2*>(orow + c0) = pk;
       }
     }
   }
@@ -480,19 +501,20 @@ AttnArgs make_args(const Dims& D, const Ptrs& P) {
   return a;
 }
 
-template <int DD, bool QK4, bool PV16>
+template <int DD, bool QK4, bool PV16, bool BF>
 hipError_t launch_d(const Dims& D, const AttnArgs& a, hipStream_t s) {
   const int grid = D.B * D.H * D.nqb;
   if (D.causal)
-    attn_fwd<DD, true, false, QK4, PV16><<<grid, 256, 0, s>>>(a);
+    attn_fwd<DD, true, false, QK4, PV16, BF><<<grid, 256, 0, s>>>(a);
   else
-    attn_fwd<DD, false, false, QK4, PV16><<<grid, 256, 0, s>>>(a);
+    attn_fwd<DD, false, false, QK4, PV16, BF><<<grid, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 
 template <bool QK4, bool PV16>
 hipError_t launch_qp(const Dims& D, const AttnArgs& a, hipStream_t s) {
-  return D.d == 128 ? launch_d<128, QK4, PV16>(D, a, s) : launch_d<64, QK4, PV16>(D, a, s);
+  if (D.bf16) return D.d == 128 ? launch_d<128, QK4, PV16, true>(D, a, s) : launch_d<64, QK4, PV16, true>(D, a, s);
+  return D.d == 128 ? launch_d<128, QK4, PV16, false>(D, a, s) : launch_d<64, QK4, PV16, false>(D, a, s);
 }
 
 }  // namespace
@@ -507,11 +529,11 @@ hipError_t launch_qk_tile(const Dims& D, const Ptrs& P, int b, int h, int qb, in
   AttnArgs a = make_args(D, P);
   a.dbg_b = b; a.dbg_h = h; a.dbg_qb = qb; a.dbg_kb = kb; a.dbg_out = out;
   if (D.qk_bits == 4) {
-    if (D.d == 128) attn_fwd<128, false, true, true, false><<<1, 256, 0, s>>>(a);
-    else attn_fwd<64, false, true, true, false><<<1, 256, 0, s>>>(a);
+    if (D.d == 128) attn_fwd<128, false, true, true, false, false><<<1, 256, 0, s>>>(a);
+    else attn_fwd<64, false, true, true, false, false><<<1, 256, 0, s>>>(a);
   } else {
-    if (D.d == 128) attn_fwd<128, false, true, false, false><<<1, 256, 0, s>>>(a);
-    else attn_fwd<64, false, true, false, false><<<1, 256, 0, s>>>(a);
+    if (D.d == 128) attn_fwd<128, false, true, false, false, false><<<1, 256, 0, s>>>(a);
+    else attn_fwd<64, false, true, false, false, false><<<1, 256, 0, s>>>(a);
   }
   return hipGetLastError();
 }

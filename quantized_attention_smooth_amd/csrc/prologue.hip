@@ -16,19 +16,29 @@
 // round-half-even of one fp32 product with the correctly rounded fp32 reciprocal R / amax;
 // scales are the correctly rounded fp32 quotient amax / R.  None of these depend on the
 // order of the parallel reduction, so codes and scales are reproducible bit for bit.
+#include <type_traits>
+
 #include "sage_internal.h"
 
 namespace sage {
 
 namespace {
 
-struct Half8 {
-  __half h[8];
+// 8 consecutive input elements (fp16 or bf16) as raw bits, converted on use
+template <typename T> __device__ inline float bits_to_float(uint16_t b);
+template <> __device__ inline float bits_to_float<__half>(uint16_t b) { return __half2float(__ushort_as_half(b)); }
+template <> __device__ inline float bits_to_float<__bf16>(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+template <typename T>
+struct In8 {
+  uint16_t b[8];
+  __device__ float f(int e) const { return bits_to_float<T>(b[e]); }
 };
 
-__device__ inline Half8 load8(const __half* p) {
-  Half8 r;
-  *reinterpret_cast<uint4*>(&r) = *reinterpret_cast<const uint4*>(p);
+template <typename T>
+__device__ inline In8<T> load8(const T* p) {
+  In8<T> r;
+  *reinterpret_cast<uint4*>(r.b) = *reinterpret_cast<const uint4*>(p);
   return r;
 }
 
@@ -74,30 +84,99 @@ __device__ inline void store_codes(int8_t* row, int cq, const float (&x)[8], boo
 }
 
 // ---------------------------------------------------------------------------------------
+// Exact sums of bf16 values.  A bf16 number is an integer m < 2^8 times 2^p in units of 2^-133
+// (p = biased exponent - 1 for normal numbers, 0 for subnormals), so a column sum of up to
+// 2^23 of them is an integer below 2^284.  It is kept as kLimbs signed int64 limbs of weight
+// 2^(24 i): each value adds m * 2^(p mod 24) < 2^32 to limb p div 24, so no limb can overflow
+// (2^23 terms * 2^32 < 2^63) whatever the order of the additions.  superacc_value turns the
+// limbs into the correctly rounded fp64 value of the sum (round to nearest even), which is
+// what the mean needs: mu = RN32(RN64(sum) / n), the same rule as for fp16 inputs.
+// ---------------------------------------------------------------------------------------
+constexpr int kLimbs = 12;
+
+__device__ inline void superacc_add(unsigned long long* acc, uint16_t bits) {
+  const int e = (bits >> 7) & 0xFF;
+  const int m = e ? (bits & 0x7F) | 0x80 : bits & 0x7F;
+  const int p = e ? e - 1 : 0;
+  const long long c = (long long)m << (p % 24);
+  atomicAdd(acc + p / 24, (unsigned long long)((bits & 0x8000) ? -c : c));
+}
+
+__device__ inline double superacc_value(const unsigned long long* limbs) {
+  long long M[kLimbs];
+  long long carry = 0;
+#pragma unroll
+  for (int i = 0; i < kLimbs; ++i) {            // normalise: every limb in [0, 2^24)
+    const long long x = (long long)limbs[i] + carry;
+    carry = x >> 24;                            // arithmetic shift: floor division
+    M[i] = x - (carry << 24);
+  }
+  const bool neg = carry < 0;                   // the total is -2^288 + sum M_i 2^(24 i)
+  if (neg) {                                    // magnitude: 2^288 - sum M_i 2^(24 i)
+    long long c1 = 1;
+#pragma unroll
+    for (int i = 0; i < kLimbs; ++i) {
+      const long long x = ((1LL << 24) - 1 - M[i]) + c1;
+      c1 = x >> 24;
+      M[i] = x & ((1LL << 24) - 1);
+    }
+  }
+  int t = -1;
+#pragma unroll
+  for (int i = 0; i < kLimbs; ++i)
+    if (M[i] != 0) t = i;
+  if (t < 0) return 0.0;
+  // 96-bit window of the top four limbs, the rest as a sticky bit
+  unsigned __int128 W = 0;
+  bool sticky = false;
+#pragma unroll
+  for (int i = kLimbs - 1; i >= 0; --i) {
+    if (i <= t && i >= t - 3) W = (W << 24) | (unsigned __int128)M[i];
+    else if (i < t - 3 && M[i] != 0) sticky = true;
+  }
+  for (int i = t - 3; i < 0; ++i) W <<= 24;     // windows that start below limb 0
+  const unsigned long long hi = (unsigned long long)(W >> 64), lo = (unsigned long long)W;
+  const int bitlen = hi ? 128 - __clzll(hi) : 64 - __clzll(lo);
+  int shift = bitlen - 53;                      // >= 20: the top limb is nonzero
+  unsigned long long mant = (unsigned long long)(W >> shift);
+  const unsigned __int128 rem = W & (((unsigned __int128)1 << shift) - 1);
+  const unsigned __int128 half = (unsigned __int128)1 << (shift - 1);
+  if (rem > half || (rem == half && (sticky || (mant & 1)))) {
+    if (++mant >> 53) { mant >>= 1; ++shift; }
+  }
+  const double r = ldexp((double)mant, shift + 24 * (t - 3) - 133);
+  return neg ? -r : r;
+}
+
+// ---------------------------------------------------------------------------------------
 // zero the atomically reduced statistics
 // ---------------------------------------------------------------------------------------
-__global__ void init_stats(unsigned long long* ksum, unsigned int* vamax, int n) {
+__global__ void init_stats(unsigned long long* ksum, unsigned int* vamax, int n, int limbs) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) {
-    ksum[i] = 0ull;
+    for (int l = 0; l < limbs; ++l) ksum[(size_t)i * limbs + l] = 0ull;
     vamax[i] = 0u;
   }
 }
 
 // ---------------------------------------------------------------------------------------
-// K channel sums (exact: fp64 within a workgroup, int64 fixed point across) and V channel
-// abs-max, per (b, kv head).  VSTATS = false (V kept in fp16) skips V entirely.
+// K channel sums and V channel abs-max, per (sequence, kv head).  The sums are exact: fp16
+// inputs in fp64 within a workgroup and int64 fixed point across; bf16 inputs in the limb
+// accumulator above (LDS within a workgroup, int64 atomics across).  VSTATS = false (V kept in
+// 16-bit floats) skips V entirely.
 // grid (ceil(longest / 256), B*Hkv), 256 threads; thread = (row slot, 8-channel chunk).
 // ---------------------------------------------------------------------------------------
-template <int D, bool VSTATS>
-__global__ __launch_bounds__(256) void kv_stats(const __half* __restrict__ k, const __half* __restrict__ v,
+template <int D, bool VSTATS, typename T>
+__global__ __launch_bounds__(256) void kv_stats(const T* __restrict__ k, const T* __restrict__ v,
                                                 unsigned long long* __restrict__ ksum,
                                                 unsigned int* __restrict__ vamax, Geo g) {
   constexpr int TPR = D / 8;      // threads per row
   constexpr int RPP = 256 / TPR;  // rows per pass
   constexpr int TOK = 256;        // tokens per workgroup
-  __shared__ double ls[RPP][D];
+  constexpr bool BF = std::is_same<T, __bf16>::value;
+  __shared__ double ls[BF ? 1 : RPP][D];
   __shared__ float lm[RPP][D];
+  __shared__ unsigned long long acc[BF ? D * kLimbs : 1];
   const int tid = threadIdx.x, cq = tid % TPR, r0 = tid / TPR;
   const size_t bh = blockIdx.y;                 // (sequence, kv head)
   const int sidx = (int)bh / g.Hkv, hk = (int)bh % g.Hkv;
@@ -105,8 +184,8 @@ __global__ __launch_bounds__(256) void kv_stats(const __half* __restrict__ k, co
   const int N = sq.n;
   if ((int)blockIdx.x * TOK >= N) return;
   const long long base = sidx * g.st.kb + (long long)sq.tok0 * g.st.kt + hk * g.st.kh;
-  const __half* kb = k + base;
-  const __half* vb = v + base;
+  const T* kb = k + base;
+  const T* vb = v + base;
   // Sums of at most TOK fp16 values are exact in fp64: every term is a multiple of 2^-24 and the
   // total stays below 2^24 < 2^(53 - 24).  The workgroup's exact total is then handed to the
   // cross-workgroup reduction as an int64 count of 2^-24 units.
@@ -114,30 +193,49 @@ __global__ __launch_bounds__(256) void kv_stats(const __half* __restrict__ k, co
   float mx[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) { s[e] = 0.0; mx[e] = 0.f; }
+  if (BF) {
+    for (int i = tid; i < D * kLimbs; i += 256) acc[i] = 0ull;
+    __syncthreads();
+  }
   const int tok0 = blockIdx.x * TOK;
 #pragma unroll 4
   for (int p = 0; p < TOK / RPP; ++p) {
     const int row = tok0 + p * RPP + r0;
     if (row < N) {
-      const Half8 kk = load8(kb + row * g.st.kt + cq * 8);
+      const auto kk = load8(kb + row * g.st.kt + cq * 8);
+      if (BF) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s[e] += (double)__half2float(kk.h[e]);
+        for (int e = 0; e < 8; ++e) superacc_add(&acc[(cq * 8 + e) * kLimbs], kk.b[e]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s[e] += (double)kk.f(e);
+      }
       if (VSTATS) {
-        const Half8 vv = load8(vb + row * g.st.kt + cq * 8);
+        const auto vv = load8(vb + row * g.st.kt + cq * 8);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) mx[e] = fmaxf(mx[e], fabsf(__half2float(vv.h[e])));
+        for (int e = 0; e < 8; ++e) mx[e] = fmaxf(mx[e], fabsf(vv.f(e)));
       }
     }
   }
 #pragma unroll
-  for (int e = 0; e < 8; ++e) { ls[r0][cq * 8 + e] = s[e]; lm[r0][cq * 8 + e] = mx[e]; }
+  for (int e = 0; e < 8; ++e) {
+    if (!BF) ls[r0][cq * 8 + e] = s[e];
+    lm[r0][cq * 8 + e] = mx[e];
+  }
   __syncthreads();
   for (int c = tid; c < D; c += 256) {
     double t = 0.0;
     float m = 0.f;
-    for (int r = 0; r < RPP; ++r) { t += ls[r][c]; m = fmaxf(m, lm[r][c]); }
-    atomicAdd(&ksum[bh * D + c], (unsigned long long)(long long)(t * 16777216.0));   // exact integer
+    for (int r = 0; r < RPP; ++r) {
+      if (!BF) t += ls[r][c];
+      m = fmaxf(m, lm[r][c]);
+    }
+    if (!BF) atomicAdd(&ksum[bh * D + c], (unsigned long long)(long long)(t * 16777216.0));   // exact integer
     if (VSTATS) atomicMax(&vamax[bh * D + c], __float_as_uint(m));   // order of non-negative floats
+  }
+  if (BF) {
+    for (int i = tid; i < D * kLimbs; i += 256)
+      if (acc[i] != 0ull) atomicAdd(&ksum[bh * D * kLimbs + i], acc[i]);
   }
 }
 
@@ -152,8 +250,8 @@ __global__ __launch_bounds__(256) void kv_stats(const __half* __restrict__ k, co
 // ---------------------------------------------------------------------------------------
 __device__ inline int v16_lds_row(int row) { return row ^ ((row >> 3) & 7); }
 
-template <int D>
-__device__ inline void store_v16(const __half* __restrict__ vbase, long long tstride, uint8_t* vt,
+template <int D, typename T>
+__device__ inline void store_v16(const T* __restrict__ vbase, long long tstride, uint8_t* vt,
                                  uint8_t* __restrict__ dst, int kb, int N, int tid, int cq, int r0) {
   constexpr int TPR = D / 8, RPP = 256 / TPR, G4 = BK / 4 / RPP;
 #pragma unroll
@@ -166,9 +264,9 @@ __device__ inline void store_v16(const __half* __restrict__ vbase, long long tst
     for (int i = 0; i < 4; ++i) {
       const int row = kb * BK + jl0 + i;
       if (row < N) {
-        const Half8 vv = load8(vbase + row * tstride + cq * 8);
+        const auto vv = load8(vbase + row * tstride + cq * 8);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[i][e] = __half_as_ushort(vv.h[e]);
+        for (int e = 0; e < 8; ++e) x[i][e] = vv.b[e];
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[i][e] = 0;
@@ -198,8 +296,8 @@ __device__ inline void store_v16(const __half* __restrict__ vbase, long long tst
 // V codes are written transposed per 64-key group in the FP8 MFMA k-slot order; with PV16
 // V itself (fp16) is written transposed per 16-key group in the fp16 MFMA k-slot order.
 // ---------------------------------------------------------------------------------------
-template <int D, bool PV16>
-__global__ __launch_bounds__(256) void kv_quant(const __half* __restrict__ k, const __half* __restrict__ v,
+template <int D, bool PV16, typename T>
+__global__ __launch_bounds__(256) void kv_quant(const T* __restrict__ k, const T* __restrict__ v,
                                                 const unsigned long long* __restrict__ ksum,
                                                 const unsigned int* __restrict__ vamax,
                                                 int8_t* __restrict__ kcodes, uint8_t* __restrict__ vcodes,
@@ -217,16 +315,20 @@ __global__ __launch_bounds__(256) void kv_quant(const __half* __restrict__ k, co
   if (kb >= seq_blocks(sq)) return;
   const int N = sq.n;
   const long long ts = g.st.kt;
-  const __half* kbase = k + sidx * g.st.kb + (long long)sq.tok0 * ts + hk * g.st.kh;
-  const __half* vbase = v + sidx * g.st.kb + (long long)sq.tok0 * ts + hk * g.st.kh;
+  const T* kbase = k + sidx * g.st.kb + (long long)sq.tok0 * ts + hk * g.st.kh;
+  const T* vbase = v + sidx * g.st.kb + (long long)sq.tok0 * ts + hk * g.st.kh;
   const size_t rows = rows_off(sq, g.Hkv, hk);  // this head's padded rows in the code arrays
 
   float mu[8], vinv[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const int c = cq * 8 + e;
-    const long long S = (long long)ksum[bh * D + c];
-    mu[e] = (float)((double)S / ((double)N * 16777216.0));
+    if (std::is_same<T, __bf16>::value) {
+      mu[e] = (float)(superacc_value(&ksum[(bh * D + c) * kLimbs]) / (double)N);
+    } else {
+      const long long S = (long long)ksum[bh * D + c];
+      mu[e] = (float)((double)S / ((double)N * 16777216.0));
+    }
     const float va = PV16 ? 0.f : __uint_as_float(vamax[bh * D + c]);
     vinv[e] = va > 0.f ? V_RANGE / va : 0.f;
     if (kb == 0 && r0 == 0) {
@@ -242,10 +344,10 @@ __global__ __launch_bounds__(256) void kv_quant(const __half* __restrict__ k, co
   for (int p = 0; p < PASSES; ++p) {
     const int row = kb * BK + p * RPP + r0;
     if (row < N) {
-      const Half8 kk = load8(kbase + row * ts + cq * 8);
+      const auto kk = load8(kbase + row * ts + cq * 8);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        gk[p][e] = __half2float(kk.h[e]) - mu[e];
+        gk[p][e] = kk.f(e) - mu[e];
         am = fmaxf(am, fabsf(gk[p][e]));
       }
     } else {
@@ -297,9 +399,9 @@ __global__ __launch_bounds__(256) void kv_quant(const __half* __restrict__ k, co
     for (int i = 0; i < 4; ++i) {
       const int row = kb * BK + jl0 + i;
       if (row < N) {
-        const Half8 vv = load8(vbase + row * ts + cq * 8);
+        const auto vv = load8(vbase + row * ts + cq * 8);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[i][e] = fminf(fmaxf(__half2float(vv.h[e]) * vinv[e], -V_RANGE), V_RANGE);
+        for (int e = 0; e < 8; ++e) x[i][e] = fminf(fmaxf(vv.f(e) * vinv[e], -V_RANGE), V_RANGE);
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[i][e] = 0.f;
@@ -327,13 +429,15 @@ __global__ __launch_bounds__(256) void kv_quant(const __half* __restrict__ k, co
 // Q smoothing (per 128-row block mean) + per-row quantization.
 // grid (blocks of the longest sequence, B*H), 256 threads.
 // ---------------------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(256) void q_quant(const __half* __restrict__ q, int8_t* __restrict__ qcodes,
+template <int D, typename T>
+__global__ __launch_bounds__(256) void q_quant(const T* __restrict__ q, int8_t* __restrict__ qcodes,
                                                float* __restrict__ qscale, float* __restrict__ muq,
                                                uint16_t* __restrict__ muqs, Geo g, float R) {
   constexpr int TPR = D / 8, RPP = 256 / TPR, PASSES = BQ / RPP;
-  __shared__ double ls[RPP][D];
+  constexpr bool BF = std::is_same<T, __bf16>::value;
+  __shared__ double ls[BF ? 1 : RPP][D];
   __shared__ float lmu[D];
+  __shared__ unsigned long long acc[BF ? D * kLimbs : 1];
   const int tid = threadIdx.x, cq = tid % TPR, r0 = tid / TPR;
   const int qb = blockIdx.x;
   const int sidx = (int)blockIdx.y / g.H, h = (int)blockIdx.y % g.H;
@@ -341,36 +445,48 @@ __global__ __launch_bounds__(256) void q_quant(const __half* __restrict__ q, int
   if (qb >= seq_blocks(sq)) return;
   const int N = sq.n;
   const long long ts = g.st.qt;
-  const __half* qbase = q + sidx * g.st.qb + (long long)sq.tok0 * ts + h * g.st.qh;
+  const T* qbase = q + sidx * g.st.qb + (long long)sq.tok0 * ts + h * g.st.qh;
   const size_t rows = rows_off(sq, g.H, h), blk = blocks_off(sq, g.H, h) + qb;
   const int nvalid = min(BQ, N - qb * BQ);
 
-  // block sums in fp64 are exact (at most 128 fp16 terms, multiples of 2^-24, below 2^24)
+  // block sums are exact: fp16 in fp64 (at most 128 terms, multiples of 2^-24, below 2^24),
+  // bf16 in the limb accumulator
   float x[PASSES][8];
   double s[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) s[e] = 0.0;
+  if (BF) {
+    for (int i = tid; i < D * kLimbs; i += 256) acc[i] = 0ull;
+    __syncthreads();
+  }
 #pragma unroll
   for (int p = 0; p < PASSES; ++p) {
     const int row = qb * BQ + p * RPP + r0;
     if (row < N) {
-      const Half8 qq = load8(qbase + row * ts + cq * 8);
+      const auto qq = load8(qbase + row * ts + cq * 8);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        x[p][e] = __half2float(qq.h[e]);
-        s[e] += (double)x[p][e];
+        x[p][e] = qq.f(e);
+        if (BF) superacc_add(&acc[(cq * 8 + e) * kLimbs], qq.b[e]);
+        else s[e] += (double)x[p][e];
       }
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[p][e] = 0.f;
     }
   }
+  if (!BF) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) ls[r0][cq * 8 + e] = s[e];
+    for (int e = 0; e < 8; ++e) ls[r0][cq * 8 + e] = s[e];
+  }
   __syncthreads();
   for (int c = tid; c < D; c += 256) {
     double t = 0.0;
-    for (int r = 0; r < RPP; ++r) t += ls[r][c];
+    if (BF) {
+      t = superacc_value(&acc[c * kLimbs]);
+    } else {
+      for (int r = 0; r < RPP; ++r) t += ls[r][c];
+    }
     const float m = (float)(t / (double)nvalid);
     lmu[c] = m;
     muq[blk * D + c] = m;
@@ -460,8 +576,8 @@ __device__ inline Split3 split3(const float (&x)[8]) {
 // Q-tile form, for few Q blocks per key: grid (Npad/256 key tiles, ceil(nqb/32) Q-block tiles of
 // the longest sequence, B*H), 256 threads; each wave owns 32 Q blocks x 64 keys (two 32x32 MFMA tiles) and splits
 // both operands itself.  Causal rows stop at key (qb + 1) * 128.
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void delta_s_qtile(const __half* __restrict__ k, const float* __restrict__ muk,
+template <int D, bool CAUSAL, typename T>
+__global__ __launch_bounds__(256) void delta_s_qtile(const T* __restrict__ k, const float* __restrict__ muk,
                                                const float* __restrict__ muq, float* __restrict__ ds,
                                                Geo g, float k2) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, r = lane & 31, hl = lane >> 5;
@@ -478,7 +594,7 @@ __global__ __launch_bounds__(256) void delta_s_qtile(const __half* __restrict__ 
   const int qb = q0 + r;                               // A row (operand) of this lane
   const bool qvalid = qb < nqb;
   const long long ts = g.st.kt;
-  const __half* kb = k + b * g.st.kb + (long long)sq.tok0 * ts + hk * g.st.kh;
+  const T* kb = k + b * g.st.kb + (long long)sq.tok0 * ts + hk * g.st.kh;
   const float* muqh = muq + blocks_off(sq, H, h) * D;
   f32x16 acc[2] = {};
 #pragma unroll 2
@@ -504,9 +620,9 @@ __global__ __launch_bounds__(256) void delta_s_qtile(const __half* __restrict__ 
       const int j = j0 + 32 * t + r;                   // B column (key) of this lane
       float xb[8];
       if (j < N) {
-        const Half8 kk = load8(kb + j * ts + c0);
+        const auto kk = load8(kb + j * ts + c0);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) xb[e] = __half2float(kk.h[e]) - mkv[e];   // gamma_K, RN32
+        for (int e = 0; e < 8; ++e) xb[e] = kk.f(e) - mkv[e];   // gamma_K, RN32
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) xb[e] = 0.f;
@@ -555,8 +671,8 @@ __device__ inline void load_aparts(AParts<D>& A, const uint16_t* __restrict__ he
     }
 }
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void delta_s_kblock(const __half* __restrict__ k, const float* __restrict__ muk,
+template <int D, bool CAUSAL, typename T>
+__global__ __launch_bounds__(256) void delta_s_kblock(const T* __restrict__ k, const float* __restrict__ muk,
                                                const uint16_t* __restrict__ muqs, float* __restrict__ ds,
                                                Geo g, float k2) {
   __shared__ DsSmem<D> sm;
@@ -569,7 +685,7 @@ __global__ __launch_bounds__(256) void delta_s_kblock(const __half* __restrict__
   const int N = sq.n, nqb = seq_blocks(sq), Npad = nqb * BQ;
   if (kb >= nqb) return;                                      // beyond this sequence
   const long long ts = g.st.kt;
-  const __half* kbase = k + b * g.st.kb + (long long)sq.tok0 * ts + hk * g.st.kh;
+  const T* kbase = k + b * g.st.kb + (long long)sq.tok0 * ts + hk * g.st.kh;
   auto muq_head = [&](int hq) { return muqs + blocks_off(sq, H, hk * G + hq) * 3 * D; };
 
   // gamma_K parts of the block's 128 keys -> LDS
@@ -580,12 +696,12 @@ __global__ __launch_bounds__(256) void delta_s_kblock(const __half* __restrict__
     const int j = kb * BK + key;
     float x[8];
     if (j < N) {
-      const Half8 kk = load8(kbase + j * ts + c8 * 8);
+      const auto kk = load8(kbase + j * ts + c8 * 8);
       const float4 m0 = *reinterpret_cast<const float4*>(muk + (size_t)bkv * D + c8 * 8);
       const float4 m1 = *reinterpret_cast<const float4*>(muk + (size_t)bkv * D + c8 * 8 + 4);
       const float mm[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = __half2float(kk.h[e]) - mm[e];   // gamma_K, RN32
+      for (int e = 0; e < 8; ++e) x[e] = kk.f(e) - mm[e];   // gamma_K, RN32
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[e] = 0.f;
@@ -740,37 +856,40 @@ __global__ void write_seq_table(SeqChunk c, Seq* dst) {
   if ((int)threadIdx.x < c.count) dst[c.first + threadIdx.x] = c.e[threadIdx.x];
 }
 
-template <int D>
+template <int D, typename T>
 hipError_t launch_prologue_d(const Dims& Dm, const Ptrs& P, hipStream_t s) {
   const float R = Dm.qk_bits == 4 ? 7.f : 127.f;
   const Geo g = make_geo(Dm, P.seqs);
+  const T* q = reinterpret_cast<const T*>(P.q);
+  const T* k = reinterpret_cast<const T*>(P.k);
+  const T* v = reinterpret_cast<const T*>(P.v);
   const int nkv = Dm.B * Dm.Hkv * D;
-  init_stats<<<(nkv + 255) / 256, 256, 0, s>>>(P.ksum, P.vamax, nkv);
+  init_stats<<<(nkv + 255) / 256, 256, 0, s>>>(P.ksum, P.vamax, nkv, Dm.bf16 ? kLimbs : 1);
   const dim3 gs((Dm.N + 255) / 256, Dm.B * Dm.Hkv), gq(Dm.nkb, Dm.B * Dm.Hkv);
   if (Dm.pv_bits == 16) {
-    kv_stats<D, false><<<gs, 256, 0, s>>>(P.k, P.v, P.ksum, P.vamax, g);
-    kv_quant<D, true><<<gq, 256, 0, s>>>(P.k, P.v, P.ksum, P.vamax, P.kcodes, P.vcodes, P.kscale, P.muk,
-                                         P.vscale, g, R);
+    kv_stats<D, false, T><<<gs, 256, 0, s>>>(k, v, P.ksum, P.vamax, g);
+    kv_quant<D, true, T><<<gq, 256, 0, s>>>(k, v, P.ksum, P.vamax, P.kcodes, P.vcodes, P.kscale, P.muk,
+                                            P.vscale, g, R);
   } else {
-    kv_stats<D, true><<<gs, 256, 0, s>>>(P.k, P.v, P.ksum, P.vamax, g);
-    kv_quant<D, false><<<gq, 256, 0, s>>>(P.k, P.v, P.ksum, P.vamax, P.kcodes, P.vcodes, P.kscale, P.muk,
-                                          P.vscale, g, R);
+    kv_stats<D, true, T><<<gs, 256, 0, s>>>(k, v, P.ksum, P.vamax, g);
+    kv_quant<D, false, T><<<gq, 256, 0, s>>>(k, v, P.ksum, P.vamax, P.kcodes, P.vcodes, P.kscale, P.muk,
+                                             P.vscale, g, R);
   }
-  q_quant<D><<<dim3(Dm.nqb, Dm.B * Dm.H), 256, 0, s>>>(P.q, P.qcodes, P.qscale, P.muq, P.muqs, g, R);
+  q_quant<D, T><<<dim3(Dm.nqb, Dm.B * Dm.H), 256, 0, s>>>(q, P.qcodes, P.qscale, P.muq, P.muqs, g, R);
   const float k2 = (float)(1.4426950408889634 / sqrt((double)D));
   // the K-block form pays off when each key block serves many Q blocks
   if ((size_t)(Dm.H / Dm.Hkv) * Dm.nqb >= 1024) {
     const dim3 gr(Dm.nkb, Dm.B * Dm.Hkv);
     if (Dm.causal)
-      delta_s_kblock<D, true><<<gr, 256, 0, s>>>(P.k, P.muk, P.muqs, P.ds, g, k2);
+      delta_s_kblock<D, true, T><<<gr, 256, 0, s>>>(k, P.muk, P.muqs, P.ds, g, k2);
     else
-      delta_s_kblock<D, false><<<gr, 256, 0, s>>>(P.k, P.muk, P.muqs, P.ds, g, k2);
+      delta_s_kblock<D, false, T><<<gr, 256, 0, s>>>(k, P.muk, P.muqs, P.ds, g, k2);
   } else {
     const dim3 gr((Dm.Npad + 255) / 256, (Dm.nqb + 31) / 32, Dm.B * Dm.H);
     if (Dm.causal)
-      delta_s_qtile<D, true><<<gr, 256, 0, s>>>(P.k, P.muk, P.muq, P.ds, g, k2);
+      delta_s_qtile<D, true, T><<<gr, 256, 0, s>>>(k, P.muk, P.muq, P.ds, g, k2);
     else
-      delta_s_qtile<D, false><<<gr, 256, 0, s>>>(P.k, P.muk, P.muq, P.ds, g, k2);
+      delta_s_qtile<D, false, T><<<gr, 256, 0, s>>>(k, P.muk, P.muq, P.ds, g, k2);
   }
   return hipGetLastError();
 }
@@ -789,7 +908,8 @@ hipError_t launch_seq_table(const Seq* host, int n, Seq* dev, hipStream_t s) {
 }
 
 hipError_t launch_prologue(const Dims& D, const Ptrs& P, hipStream_t s) {
-  return D.d == 128 ? launch_prologue_d<128>(D, P, s) : launch_prologue_d<64>(D, P, s);
+  if (D.bf16) return D.d == 128 ? launch_prologue_d<128, __bf16>(D, P, s) : launch_prologue_d<64, __bf16>(D, P, s);
+  return D.d == 128 ? launch_prologue_d<128, __half>(D, P, s) : launch_prologue_d<64, __half>(D, P, s);
 }
 
 hipError_t launch_debug_copy(const Dims& D, const Ptrs& P, hipStream_t s, float* mu_k, int8_t* k_codes,

@@ -44,6 +44,7 @@ struct Dims {
   int nqb;    // query blocks of the longest sequence
   int nkb;    // KV blocks of the longest sequence
   int varlen; // sequence table in the workspace instead of the uniform closed form
+  int bf16;   // inputs and output bf16 (else fp16)
   long long tot_pad;   // sum of the padded lengths
   long long tot_ds;    // Delta_S elements of all sequences and heads
   Strides st;
@@ -66,7 +67,8 @@ struct Dims {
 //  kscale : fp32  per s: [Hkv][nb_s][2]        delta_K per (KV block, lane half)
 //  qscale : fp32  per s: [H][Npad_s]           delta_Q per query row
 //  muk    : fp32  [B][Hkv][d]
-//  ksum   : int64 [B][Hkv][d]                 exact fixed-point K column sums (2^-24 units)
+//  ksum   : int64 [B][Hkv][d]                 exact fixed-point K column sums (2^-24 units);
+//           bf16 inputs: [B][Hkv][d][12] limbs of 2^(24 i) (units 2^-133)
 //  vamax  : u32   [B][Hkv][d]                 bits of max|V| per channel (non-negative floats)
 //  vscale : fp32  [B][Hkv][d]                 delta_V
 //  muq    : fp32  per s: [H][nb_s][d]
@@ -105,7 +107,7 @@ inline Layout make_layout(const Dims& D) {
   L.kscale = take(Hkv * nb * 2 * 4);
   L.qscale = take(H * T * 4);
   L.muk = take(B * Hkv * d * 4);
-  L.ksum = take(B * Hkv * d * 8);
+  L.ksum = take(B * Hkv * d * 8 * (D.bf16 ? 12 : 1));   // bf16: 12 limbs per exact sum
   L.vamax = take(B * Hkv * d * 4);
   L.vscale = take(B * Hkv * d * 4);
   L.muq = take(H * nb * d * 4);

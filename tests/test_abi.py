@@ -165,8 +165,12 @@ def test_varlen_workspace_is_per_sequence(pkg):
     assert m.value > n.value
 
 
-def test_bf16_is_reported_unsupported_for_now(pkg):
-    n = ctypes.c_size_t(0)
+def test_bf16_workspace_holds_the_limb_sums(pkg):
+    """bf16 inputs keep each exact K column sum in 12 int64 limbs instead of one."""
     import torch
-    p = pkg.Problem(1, 2, 2, 256, 64, False, 8, 8, "HND", dtype=torch.bfloat16)
-    assert pkg._lib.sage_attn_workspace_bytes_ex(p.ref, ctypes.byref(n)) == -2
+    n16, nbf = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    p16 = pkg.Problem(1, 2, 2, 256, 64, False, 8, 8, "HND", dtype=torch.float16)
+    pbf = pkg.Problem(1, 2, 2, 256, 64, False, 8, 8, "HND", dtype=torch.bfloat16)
+    assert pkg._lib.sage_attn_workspace_bytes_ex(p16.ref, ctypes.byref(n16)) == 0
+    assert pkg._lib.sage_attn_workspace_bytes_ex(pbf.ref, ctypes.byref(nbf)) == 0
+    assert nbf.value - n16.value >= 11 * 8 * 2 * 64

@@ -367,3 +367,100 @@ def test_varlen_full_size_sampled(sa):
                 r0, r1 = qb * 128, min(ph.N, qb * 128 + 128)
                 ref = osage.attend_block(ph, 0, 0, qb)
                 _check_o(o[a + r0:a + r1, h].cpu().numpy(), ref, f"varlen seq {s} h{h} qb{qb}", _slack(ph, 0, 0, qb))
+
+
+# ------------------------------------------------------------------------------------------
+# bf16 inputs and outputs
+# ------------------------------------------------------------------------------------------
+BF16_CASES = [
+    ("bf16-gqa-ragged-d128-causal-int8", custom(2, 4, 2, 300, 128, True, 8, q_bias_std=1.0), 8),
+    ("bf16-d64-int4", custom(1, 2, 1, 333, 64, False, 4, q_bias_std=1.0), 8),
+    ("bf16-d128-pv16", custom(1, 2, 2, 384, 128, False, 8), 16),
+    ("bf16-d64-causal-int4-pv16", custom(1, 2, 1, 200, 64, True, 4), 16),
+]
+
+
+def _bf16_dev(*xs):
+    return [torch.from_numpy(x).to(torch.bfloat16).cuda() for x in xs]
+
+
+def _bf16_allowance(q, k, v, causal, bits, pv_bits, pro, b, h, qb):
+    """What bf16 adds to the O bar of one Q block: rounding O to bf16 (half an ulp, at most
+    2^-8 |O|) and, in the bf16 P V mode, rounding P to bf16 (at most 2^-8 sum p |v| / l, which
+    is the oracle's unquantized-PV output on |V|)."""
+    ref = osage.attend_block(pro, b, h, qb)
+    extra = 2.0 ** -8 * np.abs(ref)
+    if pv_bits == 16:
+        pa = osage.prologue(q, k, np.abs(v), causal, bits, quant_pv=False)
+        extra = extra + 2.0 ** -8 * osage.attend_block(pa, b, h, qb)
+    else:
+        extra = extra + osage.fp8_midpoint_slack(pro, b, h, qb)
+    return ref, extra
+
+
+@pytest.mark.parametrize("name,w,pv", BF16_CASES, ids=[c[0] for c in BF16_CASES])
+def test_bf16_parity(sa, name, w, pv):
+    _say(f"[case {name}] B{w.B} H{w.H} Hkv{w.Hkv} N{w.N} d{w.d} causal={w.causal} bits={w.qk_bits} pv={pv}")
+    q, k, v = make_inputs(w, seed=0, dtype="bf16")
+    qd, kd, vd = _bf16_dev(q, k, v)
+    o = sa.sageattn(qd, kd, vd, is_causal=w.causal, qk_bits=w.qk_bits, pv_bits=pv)
+    assert o.dtype == torch.bfloat16
+    dbg = {n: (None if t is None else t.cpu().numpy()) for n, t in
+           sa.quant_debug(qd, kd, vd, w.causal, w.qk_bits, pv).items()}
+    o = o.float().cpu().numpy()
+    pro = osage.prologue(q, k, v, w.causal, w.qk_bits, quant_pv=pv == 8)
+    o_ref, allow = np.zeros(o.shape), np.zeros(o.shape)
+    for b in range(w.B):
+        for h in range(w.H):
+            hk = h // (w.H // w.Hkv)
+            ph = osage.prologue(*_head_slice(q, k, v, b, h, w.H, w.Hkv), w.causal, w.qk_bits, quant_pv=pv == 8)
+            _check_prologue(dbg, ph, b, h, hk, f"{name} b{b} h{h}")
+            for qb in range(pro.nqb):
+                r0, r1 = qb * 128, min(w.N, qb * 128 + 128)
+                o_ref[b, h, r0:r1], allow[b, h, r0:r1] = _bf16_allowance(q, k, v, w.causal, w.qk_bits, pv,
+                                                                         pro, b, h, qb)
+    _check_o(o, o_ref, name, allow)
+
+
+def test_bf16_extreme_range_means_exact(sa):
+    """bf16 keys and queries spread over 2^-133 .. 2^126, with a column whose +-4e37 entries
+    cancel exactly around 2^-100: the GPU's limb accumulator must give the oracle's means, codes
+    and scales bit for bit."""
+    from workloads import to_bf16
+    rng = np.random.default_rng(12)
+    N, d = 300, 64
+    def extreme(max_exp):
+        bits = rng.integers(0, 1 << 16, size=(N, d), dtype=np.uint32)
+        e = (bits >> 7) & 0xFF
+        bits = np.where(e > max_exp, (bits & 0x807F) | (rng.integers(100, 140, size=(N, d)).astype(np.uint32) << 7), bits)
+        bits = np.where(((bits >> 7) & 0xFF) == 0, bits | 0x80, bits)    # normal numbers only
+        x = (bits << 16).view(np.float32).copy()
+        x[:, 0] = 0.0
+        x[:100, 0] = to_bf16(rng.uniform(1e30, 4e37, 100).astype(np.float32))
+        x[100:200, 0] = -x[:100, 0]                                   # cancels exactly
+        x[200, 0] = np.float32(2.0 ** -100)                          # all that remains of the sum
+        return x.reshape(1, 1, N, d)
+    k = extreme(252)
+    q = extreme(200)
+    v = to_bf16(rng.standard_normal((1, 1, N, d)).astype(np.float32))
+    dev = _bf16_dev(q, k, v)
+    dbg = {n: t.cpu().numpy() for n, t in sa.quant_debug(*dev, False, 8).items() if t is not None}
+    dbg.pop("delta_s")                       # mu_Q . gamma_K overflows fp32 at these magnitudes
+    pro = osage.prologue(q, k, v, False, 8)
+    assert pro.mu_k[0, 0, 0] == np.float32(2.0 ** -100 / N)
+    _check_prologue(dbg, pro, 0, 0, 0, "bf16 extreme")
+
+
+def test_bf16_layouts_and_varlen_consistent(sa):
+    """bf16 through the NHD layout and a varlen batch: bit-identical to the fixed-length HND call
+    on the same tokens."""
+    w = custom(2, 4, 2, 300, 128, True, 8, q_bias_std=1.0)
+    q, k, v = _bf16_dev(*make_inputs(w, seed=3, dtype="bf16"))
+    o = sa.sageattn(q, k, v, is_causal=True)
+    t = lambda x: x.transpose(1, 2).contiguous()
+    o_nhd = sa.sageattn(t(q), t(k), t(v), is_causal=True, tensor_layout="NHD")
+    assert torch.equal(o_nhd, t(o))
+    pk = lambda x: t(x).reshape(-1, x.shape[1], x.shape[3])   # [B*N, heads, d], sequences back to back
+    o_var = sa.sageattn_varlen(pk(q), pk(k), pk(v), [0, 300, 600], is_causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o_var, pk(o))

@@ -129,3 +129,45 @@ def test_integer_scores_are_exact():
             brute[i, j] = sum(int(a) * int(b) for a, b in zip(q[0, 0, i], k[0, 0, j]))
     assert np.array_equal(s, brute)
     assert s[0, 0] == 127 * 127 * 128
+
+
+# ------------------------------------------------------------------------------------------
+# bf16 inputs: exact means over a 2^-133 .. 2^128 range
+# ------------------------------------------------------------------------------------------
+def _bf16_columns(seed):
+    """bf16 columns that stress an exact sum: random bit patterns (all finite exponents),
+    huge values that cancel exactly around a subnormal residue, and mixed magnitudes."""
+    from workloads import to_bf16
+    rng = np.random.default_rng(seed)
+    bits = rng.integers(0, 1 << 16, size=(64, 6), dtype=np.uint32)
+    bits = np.where(((bits >> 7) & 0xFF) == 0xFF, bits & 0x807F, bits)       # no inf / nan
+    x = (bits << 16).view(np.float32).copy()
+    x[:, 1] = 0.0
+    x[0:20, 1] = to_bf16(np.float32(3.0e38) * rng.uniform(0.5, 1.0, 20).astype(np.float32))
+    x[20:40, 1] = -x[0:20, 1]                                                  # cancels exactly
+    x[40, 1] = (np.array([3], np.uint32) << 16).view(np.float32)[0]            # a subnormal
+    x[:, 2] = to_bf16(rng.standard_normal(64).astype(np.float32) * np.float32(10.0) ** rng.integers(-30, 30, 64).astype(np.float32))
+    return x
+
+
+def test_bf16_exact_mean_is_rounded_rational_sum():
+    from fractions import Fraction
+    for seed in range(5):
+        x = _bf16_columns(seed)
+        assert sage.is_bf16(x)
+        got = sage.exact_mean(x)
+        for c in range(x.shape[1]):
+            exact = sum(Fraction(float(v)) for v in x[:, c])            # exact rational sum
+            ref = np.float32(np.float64(float(exact)) / np.float64(x.shape[0]))
+            assert got[c] == ref, (seed, c, got[c], ref)
+
+
+def test_bf16_exact_mean_order_free_and_matches_fp16_rule():
+    x = _bf16_columns(7)
+    perm = np.random.default_rng(8).permutation(x.shape[0])
+    assert np.array_equal(sage.exact_mean(x), sage.exact_mean(x[perm]))
+    # values exact in both formats (8 significant bits, 2^-8 .. 2^7) give the fp16 rule's result
+    rng = np.random.default_rng(9)
+    y = (rng.integers(-255, 256, size=(300, 16)) * 2.0 ** rng.integers(-8, 0, size=(300, 16))).astype(np.float32)
+    assert sage.is_bf16(y)
+    assert np.array_equal(sage.exact_mean(y), sage.exact_mean(y.astype(np.float16)))

@@ -65,12 +65,21 @@ WORKLOADS = {
 }
 
 
+def to_bf16(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest bf16 (ties to even); returned as float32 holding
+    bf16 values (numpy has no bf16 type; torch converts them to torch.bfloat16 exactly)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32)
+
+
 def custom(B, H, Hkv, N, d, causal=False, qk_bits=8, **kw) -> Workload:
     return Workload("custom", B, H, Hkv, N, d, causal, qk_bits, **kw)
 
 
-def make_inputs(w: Workload | str, seed: int = 0):
-    """q [B,H,N,d], k/v [B,Hkv,N,d] as numpy float16, drawn by the recipe above."""
+def make_inputs(w: Workload | str, seed: int = 0, dtype: str = "fp16"):
+    """q [B,H,N,d], k/v [B,Hkv,N,d] as numpy float16 (dtype "fp16"), or as float32 arrays of
+    bf16 values (dtype "bf16", see to_bf16), drawn by the recipe above."""
     if isinstance(w, str):
         w = WORKLOADS[w]
     rng = np.random.default_rng(seed)
@@ -92,6 +101,8 @@ def make_inputs(w: Workload | str, seed: int = 0):
             h, c = divmod(int(p), w.d)
             q[:, h, :, c] *= np.float32(w.outlier_scale)
             k[:, h * w.Hkv // w.H, :, c] *= np.float32(w.outlier_scale)
+    if dtype == "bf16":
+        return to_bf16(q), to_bf16(k), to_bf16(v)
     return q.astype(np.float16), k.astype(np.float16), v.astype(np.float16)
 
 

@@ -198,22 +198,30 @@ __global__ __launch_bounds__(256) void kv_stats(const T* __restrict__ k, const T
     __syncthreads();
   }
   const int tok0 = blockIdx.x * TOK;
-#pragma unroll 4
-  for (int p = 0; p < TOK / RPP; ++p) {
-    const int row = tok0 + p * RPP + r0;
-    if (row < N) {
-      const auto kk = load8(kb + row * g.st.kt + cq * 8);
+  // 4 passes at a time, loads issued before use: rows past N read row N - 1 (in bounds) and are
+  // skipped afterwards, so no load waits behind its own branch
+  constexpr int CH = 4;
+  for (int p0 = 0; p0 < TOK / RPP; p0 += CH) {
+    In8<T> kr[CH], vr[CH];
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const long long off = (long long)min(tok0 + (p0 + i) * RPP + r0, N - 1) * g.st.kt + cq * 8;
+      kr[i] = load8(kb + off);
+      if (VSTATS) vr[i] = load8(vb + off);
+    }
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      if (tok0 + (p0 + i) * RPP + r0 >= N) continue;
       if (BF) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) superacc_add(&acc[(cq * 8 + e) * kLimbs], kk.b[e]);
+        for (int e = 0; e < 8; ++e) superacc_add(&acc[(cq * 8 + e) * kLimbs], kr[i].b[e]);
       } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) s[e] += (double)kk.f(e);
+        for (int e = 0; e < 8; ++e) s[e] += (double)kr[i].f(e);
       }
       if (VSTATS) {
-        const auto vv = load8(vb + row * g.st.kt + cq * 8);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) mx[e] = fmaxf(mx[e], fabsf(vv.f(e)));
+        for (int e = 0; e < 8; ++e) mx[e] = fmaxf(mx[e], fabsf(vr[i].f(e)));
       }
     }
   }
@@ -260,17 +268,14 @@ __device__ inline void store_v16(const T* __restrict__ vbase, long long tstride,
     const int g = jl0 >> 4, kk = jl0 & 15;
     const int quad = 2 * ((kk >> 2) & 1) + (kk >> 3);   // slots 4 quad .. 4 quad + 3
     uint16_t x[4][8];
+    In8<T> vr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vr[i] = load8(vbase + min(kb * BK + jl0 + i, N - 1) * tstride + cq * 8);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int row = kb * BK + jl0 + i;
-      if (row < N) {
-        const auto vv = load8(vbase + row * tstride + cq * 8);
+      const bool valid = kb * BK + jl0 + i < N;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[i][e] = vv.b[e];
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[i][e] = 0;
-      }
+      for (int e = 0; e < 8; ++e) x[i][e] = valid ? vr[i].b[e] : (uint16_t)0;
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -320,16 +325,34 @@ __global__ __launch_bounds__(256) void kv_quant(const T* __restrict__ k, const T
   const size_t rows = rows_off(sq, g.Hkv, hk);  // this head's padded rows in the code arrays
 
   float mu[8], vinv[8];
+  // this thread's 8 channel sums and abs-maxima, loaded together (fp16: 64 + 32 contiguous bytes)
+  unsigned long long ks8[8];
+  uint32_t va8[8];
+  if (!std::is_same<T, __bf16>::value) {
+    const uint4* kp = reinterpret_cast<const uint4*>(ksum + bh * D + cq * 8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 w = kp[i];
+      ks8[2 * i] = ((unsigned long long)w.y << 32) | w.x;
+      ks8[2 * i + 1] = ((unsigned long long)w.w << 32) | w.z;
+    }
+  }
+  if (!PV16) {
+    const uint4* vp = reinterpret_cast<const uint4*>(vamax + bh * D + cq * 8);
+    const uint4 w0 = vp[0], w1 = vp[1];
+    va8[0] = w0.x; va8[1] = w0.y; va8[2] = w0.z; va8[3] = w0.w;
+    va8[4] = w1.x; va8[5] = w1.y; va8[6] = w1.z; va8[7] = w1.w;
+  }
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const int c = cq * 8 + e;
     if (std::is_same<T, __bf16>::value) {
       mu[e] = (float)(superacc_value(&ksum[(bh * D + c) * kLimbs]) / (double)N);
     } else {
-      const long long S = (long long)ksum[bh * D + c];
+      const long long S = (long long)ks8[e];
       mu[e] = (float)((double)S / ((double)N * 16777216.0));
     }
-    const float va = PV16 ? 0.f : __uint_as_float(vamax[bh * D + c]);
+    const float va = PV16 ? 0.f : __uint_as_float(va8[e]);
     vinv[e] = va > 0.f ? V_RANGE / va : 0.f;
     if (kb == 0 && r0 == 0) {
       muk_out[bh * D + c] = mu[e];
@@ -338,21 +361,19 @@ __global__ __launch_bounds__(256) void kv_quant(const T* __restrict__ k, const T
   }
 
   // gamma_K = RN32(K - mu_K); every row of this thread has the same (row % 8)
+  // loads issued before use (rows past N read row N - 1 and are zeroed afterwards)
   float gk[PASSES][8];
   float am = 0.f;
+  In8<T> kr[PASSES];
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) kr[p] = load8(kbase + min(kb * BK + p * RPP + r0, N - 1) * ts + cq * 8);
 #pragma unroll
   for (int p = 0; p < PASSES; ++p) {
-    const int row = kb * BK + p * RPP + r0;
-    if (row < N) {
-      const auto kk = load8(kbase + row * ts + cq * 8);
+    const bool valid = kb * BK + p * RPP + r0 < N;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        gk[p][e] = kk.f(e) - mu[e];
-        am = fmaxf(am, fabsf(gk[p][e]));
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) gk[p][e] = 0.f;
+    for (int e = 0; e < 8; ++e) {
+      gk[p][e] = valid ? kr[p].f(e) - mu[e] : 0.f;
+      am = fmaxf(am, fabsf(gk[p][e]));
     }
   }
   const int hgrp = (r0 & 7) >> 2;
@@ -395,17 +416,14 @@ __global__ __launch_bounds__(256) void kv_quant(const T* __restrict__ k, const T
     const int u = jl0 >> 6, jj = jl0 & 63;
     const int base = 32 * ((jj >> 2) & 1) + 16 * (jj >> 5) + 4 * ((jj >> 3) & 3);   // slot of key jj
     float x[4][8];
+    In8<T> vr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vr[i] = load8(vbase + min(kb * BK + jl0 + i, N - 1) * ts + cq * 8);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int row = kb * BK + jl0 + i;
-      if (row < N) {
-        const auto vv = load8(vbase + row * ts + cq * 8);
+      const bool valid = kb * BK + jl0 + i < N;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[i][e] = fminf(fmaxf(vv.f(e) * vinv[e], -V_RANGE), V_RANGE);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[i][e] = 0.f;
-      }
+      for (int e = 0; e < 8; ++e) x[i][e] = valid ? fminf(fmaxf(vr[i].f(e) * vinv[e], -V_RANGE), V_RANGE) : 0.f;
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -459,20 +477,23 @@ __global__ __launch_bounds__(256) void q_quant(const T* __restrict__ q, int8_t* 
     for (int i = tid; i < D * kLimbs; i += 256) acc[i] = 0ull;
     __syncthreads();
   }
+  // every load is issued before any is used: rows past N read row N - 1 (in bounds) and are
+  // zeroed afterwards, so no load sits behind a branch that would wait for it on its own
+  In8<T> raw[PASSES];
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p)
+    raw[p] = load8(qbase + min(qb * BQ + p * RPP + r0, N - 1) * ts + cq * 8);
 #pragma unroll
   for (int p = 0; p < PASSES; ++p) {
-    const int row = qb * BQ + p * RPP + r0;
-    if (row < N) {
-      const auto qq = load8(qbase + row * ts + cq * 8);
+    const bool valid = qb * BQ + p * RPP + r0 < N;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        x[p][e] = qq.f(e);
-        if (BF) superacc_add(&acc[(cq * 8 + e) * kLimbs], qq.b[e]);
-        else s[e] += (double)x[p][e];
-      }
-    } else {
+    for (int e = 0; e < 8; ++e) {
+      x[p][e] = valid ? raw[p].f(e) : 0.f;
+      if (!BF) s[e] += (double)x[p][e];
+    }
+    if (BF && valid) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[p][e] = 0.f;
+      for (int e = 0; e < 8; ++e) superacc_add(&acc[(cq * 8 + e) * kLimbs], raw[p].b[e]);
     }
   }
   if (!BF) {
@@ -690,21 +711,23 @@ __global__ __launch_bounds__(256) void delta_s_kblock(const T* __restrict__ k, c
 
   // gamma_K parts of the block's 128 keys -> LDS
   constexpr int CH = D / 8;                                   // 8-channel chunks per key
+  In8<T> kr[BK * CH / 256];                                   // loads first (clamped, masked later)
+#pragma unroll
+  for (int it = 0; it < BK * CH / 256; ++it) {
+    const int idx = it * 256 + tid;
+    kr[it] = load8(kbase + min(kb * BK + idx / CH, N - 1) * ts + (idx % CH) * 8);
+  }
 #pragma unroll
   for (int it = 0; it < BK * CH / 256; ++it) {
     const int idx = it * 256 + tid, key = idx / CH, c8 = idx % CH;
     const int j = kb * BK + key;
     float x[8];
-    if (j < N) {
-      const auto kk = load8(kbase + j * ts + c8 * 8);
+    {
       const float4 m0 = *reinterpret_cast<const float4*>(muk + (size_t)bkv * D + c8 * 8);
       const float4 m1 = *reinterpret_cast<const float4*>(muk + (size_t)bkv * D + c8 * 8 + 4);
       const float mm[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = kk.f(e) - mm[e];   // gamma_K, RN32
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = 0.f;
+      for (int e = 0; e < 8; ++e) x[e] = j < N ? kr[it].f(e) - mm[e] : 0.f;   // gamma_K, RN32
     }
     union { __bf16 b[8]; uint4 u; } p0, p1, p2;
 #pragma unroll

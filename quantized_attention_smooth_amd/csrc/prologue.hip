@@ -53,16 +53,19 @@ __device__ inline float wave_max(float x) {
 // group of a row occupies a 32-byte slot: 24 bytes of packed 6-bit codes (channel i of the group
 // at bits 6i..6i+5) and 8 zero bytes, so rows keep d bytes and the FP8/INT8 tile geometry.
 __device__ inline uint32_t e2m3_bits(float x) {        // x integer in [-7, 7]
+  // magnitudes 0..7 are E2M3 0x00 0x08 0x10 0x14 0x18 0x1A 0x1C 0x1E: one byte each of a
+  // 64-bit constant, picked by a shift (no branches)
   const int a = (int)fabsf(x);
-  const uint32_t mag = a == 0 ? 0u : a == 1 ? 8u : a < 4 ? 16u + 4u * (a - 2) : 24u + 2u * (a - 4);
+  const uint32_t mag = (uint32_t)(0x1E1C1A1814100800ull >> (8 * a)) & 0xFFu;
   return mag | (x < 0.f ? 0x20u : 0u);
 }
 
 // Store the 8 codes of channels 8 cq .. 8 cq + 7 of one row (row points at its d code bytes).
 // FP6: the four threads of a 32-channel slot are consecutive lanes (cq & 3 = 0..3); they swap
 // their 48-bit packs so that each writes one aligned 8-byte word of the slot.
-__device__ inline void store_codes(int8_t* row, int cq, const float (&x)[8], bool fp6) {
-  if (!fp6) {
+template <bool FP6>
+__device__ inline void store_codes(int8_t* row, int cq, const float (&x)[8]) {
+  if (!FP6) {
     union { int8_t c[8]; uint2 u; } out;
 #pragma unroll
     for (int e = 0; e < 8; ++e) out.c[e] = (int8_t)(int)x[e];
@@ -75,11 +78,9 @@ __device__ inline void store_codes(int8_t* row, int cq, const float (&x)[8], boo
   const int j = cq & 3;
   // slot bits [48 t, 48 t + 48) hold thread t's pack; word j covers bits [64 j, 64 j + 64)
   const unsigned long long nxt = __shfl_down(mine, 1, 4);   // pack of thread j + 1 (same slot)
-  unsigned long long word;
-  if (j == 0) word = mine | (nxt << 48);
-  else if (j == 1) word = (mine >> 16) | (nxt << 32);
-  else if (j == 2) word = (mine >> 32) | (nxt << 16);
-  else word = 0;                                            // bytes 24..31: padding
+  // j = 0, 1, 2: bits [16 j, 64) of this pack and the first 16 (j + 1) bits of the next one;
+  // j = 3: bytes 24..31 of the slot, padding
+  const unsigned long long word = j < 3 ? (mine >> (16 * j)) | (nxt << (48 - 16 * j)) : 0ull;
   *reinterpret_cast<uint2*>(row + 32 * (cq >> 2) + 8 * j) = make_uint2((uint32_t)word, (uint32_t)(word >> 32));
 }
 
@@ -301,7 +302,7 @@ __device__ inline void store_v16(const T* __restrict__ vbase, long long tstride,
 // V codes are written transposed per 64-key group in the FP8 MFMA k-slot order; with PV16
 // V itself (fp16) is written transposed per 16-key group in the fp16 MFMA k-slot order.
 // ---------------------------------------------------------------------------------------
-template <int D, bool PV16, typename T>
+template <int D, bool PV16, typename T, bool QK4>
 __global__ __launch_bounds__(256) void kv_quant(const T* __restrict__ k, const T* __restrict__ v,
                                                 const unsigned long long* __restrict__ ksum,
                                                 const unsigned int* __restrict__ vamax,
@@ -396,7 +397,7 @@ __global__ __launch_bounds__(256) void kv_quant(const T* __restrict__ k, const T
     float x[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] = fminf(fmaxf(rintf(gk[p][e] * inv), -R), R);
-    store_codes(kcodes + (rows + row) * D, cq, x, R < 8.f);
+    store_codes<QK4>(kcodes + (rows + row) * D, cq, x);
   }
 
   if (PV16) {
@@ -447,7 +448,7 @@ __global__ __launch_bounds__(256) void kv_quant(const T* __restrict__ k, const T
 // Q smoothing (per 128-row block mean) + per-row quantization.
 // grid (blocks of the longest sequence, B*H), 256 threads.
 // ---------------------------------------------------------------------------------------
-template <int D, typename T>
+template <int D, typename T, bool QK4>
 __global__ __launch_bounds__(256) void q_quant(const T* __restrict__ q, int8_t* __restrict__ qcodes,
                                                float* __restrict__ qscale, float* __restrict__ muq,
                                                uint16_t* __restrict__ muqs, Geo g, float R) {
@@ -541,7 +542,7 @@ __global__ __launch_bounds__(256) void q_quant(const T* __restrict__ q, int8_t* 
     float y[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) y[e] = fminf(fmaxf(rintf(x[p][e] * inv), -R), R);
-    store_codes(qcodes + (rows + row) * D, cq, y, R < 8.f);
+    store_codes<QK4>(qcodes + (rows + row) * D, cq, y);
     if (cq == 0) qscale[rows + row] = am / R;
   }
 }
@@ -889,16 +890,24 @@ hipError_t launch_prologue_d(const Dims& Dm, const Ptrs& P, hipStream_t s) {
   const int nkv = Dm.B * Dm.Hkv * D;
   init_stats<<<(nkv + 255) / 256, 256, 0, s>>>(P.ksum, P.vamax, nkv, Dm.bf16 ? kLimbs : 1);
   const dim3 gs((Dm.N + 255) / 256, Dm.B * Dm.Hkv), gq(Dm.nkb, Dm.B * Dm.Hkv);
+  // INT4-range codes (R = 7) are stored as FP6: a compile-time switch of the code store
+  auto kvq = [&](auto pv16, auto qk4) {
+    kv_quant<D, decltype(pv16)::value, T, decltype(qk4)::value><<<gq, 256, 0, s>>>(
+        k, v, P.ksum, P.vamax, P.kcodes, P.vcodes, P.kscale, P.muk, P.vscale, g, R);
+  };
+  const bool qk4 = Dm.qk_bits == 4;
   if (Dm.pv_bits == 16) {
     kv_stats<D, false, T><<<gs, 256, 0, s>>>(k, v, P.ksum, P.vamax, g);
-    kv_quant<D, true, T><<<gq, 256, 0, s>>>(k, v, P.ksum, P.vamax, P.kcodes, P.vcodes, P.kscale, P.muk,
-                                            P.vscale, g, R);
+    if (qk4) kvq(std::true_type{}, std::true_type{});
+    else kvq(std::true_type{}, std::false_type{});
   } else {
     kv_stats<D, true, T><<<gs, 256, 0, s>>>(k, v, P.ksum, P.vamax, g);
-    kv_quant<D, false, T><<<gq, 256, 0, s>>>(k, v, P.ksum, P.vamax, P.kcodes, P.vcodes, P.kscale, P.muk,
-                                             P.vscale, g, R);
+    if (qk4) kvq(std::false_type{}, std::true_type{});
+    else kvq(std::false_type{}, std::false_type{});
   }
-  q_quant<D, T><<<dim3(Dm.nqb, Dm.B * Dm.H), 256, 0, s>>>(q, P.qcodes, P.qscale, P.muq, P.muqs, g, R);
+  const dim3 gqq(Dm.nqb, Dm.B * Dm.H);
+  if (qk4) q_quant<D, T, true><<<gqq, 256, 0, s>>>(q, P.qcodes, P.qscale, P.muq, P.muqs, g, R);
+  else q_quant<D, T, false><<<gqq, 256, 0, s>>>(q, P.qcodes, P.qscale, P.muq, P.muqs, g, R);
   const float k2 = (float)(1.4426950408889634 / sqrt((double)D));
   // the K-block form pays off when each key block serves many Q blocks
   if ((size_t)(Dm.H / Dm.Hkv) * Dm.nqb >= 1024) {

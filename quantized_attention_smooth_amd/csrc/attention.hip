@@ -131,43 +131,80 @@ typedef __attribute__((address_space(3))) void lds_void;
 template <int D>
 constexpr int kTileInstrs = BK * D / 16 / 64 / WAVES;
 
-// K codes of one block (ktile: its first row) and its Delta_S row slice (wave 0) into stage st.
-// The Delta_S load goes first, so a wait for "all but the last kTileInstrs" loads of wave 0
-// leaves only K chunks outstanding.
-template <int D, bool PV16>
-__device__ inline void issue_k(const int8_t* ktile, const float* dsrc, Smem<D, PV16>& sm, int st, int w, int lane) {
-  constexpr int CPR = D / 16;                 // 16-byte chunks per K row
-  if (w == 0 && lane < BK / 4)
-    __builtin_amdgcn_global_load_lds(dsrc + (uint32_t)(lane * 4), (lds_void*)sm.ds[st], 16, 0, 0);
-  // wave-uniform tile base (scalar registers) plus 32-bit per-lane byte offsets
-  const int8_t* kbase = ktile;
-#pragma unroll
-  for (int m = 0; m < kTileInstrs<D>; ++m) {
-    const int blk = m * WAVES + w;            // which 1 KB of the tile this wave writes
-    const int p = blk * 64 + lane;            // 16-byte chunk index in LDS
-    const int row = p / CPR, pc = p % CPR;
-    const uint32_t off = (uint32_t)(row * D + ((pc ^ kswz<D>(row)) * 16));
-    __builtin_amdgcn_global_load_lds(kbase + off, (lds_void*)(sm.k[st] + blk * 1024), 16, 0, 0);
-  }
+// Tile loads: buffer loads straight to LDS (buffer_load_dwordx4 ... lds).  Each operand stream
+// has a buffer resource over this (sequence, head)'s data; a lane's byte offset inside a tile is
+// the same for every block, so it is computed once, and the block moves only the scalar
+// offset.  (Per-lane 64-bit pointers advanced every block cost ~20 VALU instructions per block.)
+// Loads past a resource's end return zeros (range-checked).
+// The buffer builtins exist only for the GPU target: their code is compiled in the device pass
+// (in the host pass, kernels using them otherwise lost their launch stubs without a diagnostic).
+#if defined(__HIP_DEVICE_COMPILE__)
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
+#endif
 
-// V of block kb into stage st: FP8 codes (64-byte rows) or fp16 V (32-byte rows, twice the
-// instructions).
 template <int D, bool PV16>
-__device__ inline void issue_v(const uint8_t* vtile, Smem<D, PV16>& sm, int st, int w, int lane) {
-  constexpr int RB = PV16 ? 32 : VGROUP;      // bytes per LDS row (group, channel)
-  constexpr int CR = RB / 16;                 // 16-byte chunks per row
-  const uint8_t* vbase = vtile;
+struct TileLoader {
+  static constexpr int NK = kTileInstrs<D>;                 // K (and FP8 V) instructions per wave
+  static constexpr int NV = kTileInstrs<D> * (PV16 ? 2 : 1);
+  static constexpr int VB = PV16 ? 2 : 1;                   // V bytes per element
+  const void *kp, *vp, *dp;
+  uint32_t kbytes, vbytes, dbytes;
+  uint32_t koff[NK], voff[NV];
+
+  // kc, vc: the head's K codes / V rows; dsrow: the Q block's Delta_S row of ds_len floats
+  __device__ TileLoader(const int8_t* kc, const uint8_t* vc, const float* dsrow, int nkb, int ds_len, int w,
+                        int lane) {
+    kp = kc; kbytes = (uint32_t)nkb * BK * D;
+    vp = vc; vbytes = (uint32_t)nkb * BK * D * VB;
+    dp = dsrow; dbytes = (uint32_t)ds_len * 4;
+    constexpr int CPR = D / 16;                             // 16-byte chunks per K row
 #pragma unroll
-  for (int m = 0; m < kTileInstrs<D> * (PV16 ? 2 : 1); ++m) {
-    const int blk = m * WAVES + w;
-    const int p = blk * 64 + lane;
-    const int row = p / CR, pc = p % CR;      // row = group * D + channel
-    const int sw = PV16 ? v16swz(row % D) : vswz(row % D);
-    const uint32_t off = (uint32_t)(row * RB + ((pc ^ sw) * 16));
-    __builtin_amdgcn_global_load_lds(vbase + off, (lds_void*)(sm.v[st] + blk * 1024), 16, 0, 0);
+    for (int m = 0; m < NK; ++m) {
+      const int p = (m * WAVES + w) * 64 + lane;            // 16-byte chunk index in LDS
+      const int row = p / CPR, pc = p % CPR;
+      koff[m] = (uint32_t)(row * D + ((pc ^ kswz<D>(row)) * 16));
+    }
+    constexpr int RB = PV16 ? 32 : VGROUP;                  // bytes per V LDS row (group, channel)
+    constexpr int CR = RB / 16;
+#pragma unroll
+    for (int m = 0; m < NV; ++m) {
+      const int p = (m * WAVES + w) * 64 + lane;
+      const int row = p / CR, pc = p % CR;                  // row = group * D + channel
+      const int sw = PV16 ? v16swz(row % D) : vswz(row % D);
+      voff[m] = (uint32_t)(row * RB + ((pc ^ sw) * 16));
+    }
   }
-}
+
+  // K codes of block kb and its Delta_S row slice (wave 0) into stage st.  The Delta_S load goes
+  // first, so a wait for "all but the last kTileInstrs" loads of wave 0 leaves only K chunks
+  // outstanding.
+  __device__ void issue_k(Smem<D, PV16>& sm, int st, int kb, int w, int lane) const {
+#if defined(__HIP_DEVICE_COMPILE__)
+    if (w == 0 && lane < BK / 4)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(dp, dbytes), (lds_void*)sm.ds[st], 16, lane * 16,
+                                               kb * BK * 4, 0, 0);
+    const auto kr = make_rsrc(kp, kbytes);
+#pragma unroll
+    for (int m = 0; m < NK; ++m)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(sm.k[st] + (m * WAVES + w) * 1024), 16, koff[m],
+                                               kb * BK * D, 0, 0);
+#endif
+  }
+
+  // V of block kb into stage st: FP8 codes (64-byte rows) or 16-bit V (32-byte rows, twice the
+  // instructions).
+  __device__ void issue_v(Smem<D, PV16>& sm, int st, int kb, int w) const {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const auto vr = make_rsrc(vp, vbytes);
+#pragma unroll
+    for (int m = 0; m < NV; ++m)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(sm.v[st] + (m * WAVES + w) * 1024), 16, voff[m],
+                                               kb * BK * D * VB, 0, 0);
+#endif
+  }
+};
 
 __device__ inline void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
@@ -228,7 +265,8 @@ template <int D, bool CAUSAL, bool DUMP, bool QK4, bool PV16, bool BF>
 __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
   typedef PV16T<BF> PT;
   __shared__ Smem<D, PV16> sm;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, col = lane & 31, half = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, col = lane & 31, half = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform: kept in a scalar
 
   const int H = a.g.H, Hkv = a.g.Hkv;
   int b, h, qb;
@@ -257,8 +295,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
   const uint8_t* vc = a.vcodes + krows * D * (PV16 ? 2 : 1);
   const float* kscl = a.kscale + blocks_off(sq, Hkv, hk) * 2;
   const float* dsrow = a.ds + ds_off(sq, a.g.causal, h) + ds_row_offset(a.g.causal, qb, nkb * BK);
-  auto ktile = [&](int kb) { return kc + (size_t)kb * BK * D; };
-  auto vtile = [&](int kb) { return vc + (size_t)kb * BK * D * (PV16 ? 2 : 1); };
+  const TileLoader<D, PV16> ld(kc, vc, dsrow, nkb, ds_row_len(a.g.causal, qb, nkb * BK), w, lane);
 
   // the wave's 32 query rows as the B operand of S^T = K Q^T (16 bytes per k-step)
   // (INT4 range: 32 bytes per 64-channel step, held as two consecutive v4i)
@@ -271,7 +308,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
   const float qd = a.qscale[qrows + i];
 
   if (DUMP) {
-    issue_k<D, PV16>(ktile(a.dbg_kb), dsrow + (size_t)a.dbg_kb * BK, sm, 0, w, lane);
+    ld.issue_k(sm, 0, a.dbg_kb, w, lane);
     wait_loads();
     __syncthreads();
     v16i sacc[BK / 32];
@@ -292,8 +329,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
 #pragma unroll
   for (int ct = 0; ct < D / 32; ++ct) og[ct] = (v16f){};
 
-  issue_v<D, PV16>(vtile(0), sm, 0, w, lane);
-  issue_k<D, PV16>(ktile(0), dsrow, sm, 0, w, lane);
+  ld.issue_v(sm, 0, 0, w);
+  ld.issue_k(sm, 0, 0, w, lane);
   wait_loads();
   __syncthreads();
 
@@ -305,8 +342,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
     const int st = kb & 1;
     const bool more = kb + 1 < nblk;
     if (more) {
-      if (!PV16) issue_v<D, PV16>(vtile(kb + 1), sm, st ^ 1, w, lane);
-      issue_k<D, PV16>(ktile(kb + 1), dsrow + (size_t)(kb + 1) * BK, sm, st ^ 1, w, lane);
+      if (!PV16) ld.issue_v(sm, st ^ 1, kb + 1, w);
+      ld.issue_k(sm, st ^ 1, kb + 1, w, lane);
     }
 
     v16i sacc[BK / 32];
@@ -404,7 +441,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
 
       wait_loads();
       __syncthreads();
-      if (more) issue_v<D, PV16>(vtile(kb + 1), sm, 0, w, lane);
+      if (more) ld.issue_v(sm, 0, kb + 1, w);
       return;
     }
 

@@ -80,8 +80,8 @@ def attend_block_fp16acc(pro: sage.Prologue, b: int, h: int, qb: int) -> np.ndar
         finite = np.isfinite(m_new)
         alpha = np.where(np.isfinite(m), np.exp(m - np.where(finite, m_new, 0.0)), 0.0)
         p = np.where(finite[:, None], np.exp(zb - np.where(finite, m_new, 0.0)[:, None]), 0.0)
-        l = l * alpha + p.sum(axis=1)
         pt = fp8.round_sat((p * p_r).astype(np.float32))
+        l = l * alpha + pt.sum(axis=1) / p_r         # the weights that multiply V, as attend_block
         acc = acc * alpha[:, None] + pv_local_fp16(pt, vq[c0:c1])
         m = m_new
     np.seterr(**np_err)

@@ -36,11 +36,10 @@ What is computed, per (batch b, query head h); kv(h) = h div (H / Hkv):
       V_q = E4M3sat(RN32(V * RN32(V_r / amax))) [SA2pp key_machinery].
   O9  online softmax over KV blocks of bk keys (FlashAttention tiling with the online
       normalizer [SA2pp supporting_citations]): m' = max(m, blockmax z); alpha = e^(m - m');
-      p = e^(z - m'); l = l * alpha + sum p (unquantized p);
-      P~_q = E4M3sat(RN32(p * P_r)) (static range: within a block max p <= 1, so
-      delta_P = 1 / P_r [SA2pp key_machinery]); two-level accumulation [SA2 abstract;
-      SA2c on Sec. 3.4]: local = sum_j P~_q * V_q over the block (exact), acc = acc * alpha +
-      local.
+      p = e^(z - m'); P~_q = E4M3sat(RN32(p * P_r)) (static range: within a block max p <= 1,
+      so delta_P = 1 / P_r [SA2pp key_machinery]); l = l * alpha + sum P~_q / P_r (the
+      weights that multiply V; see attend_block); two-level accumulation [SA2 abstract; SA2c
+      on Sec. 3.4]: local = sum_j P~_q * V_q over the block (exact), acc = acc * alpha + local.
   O10 O = acc * delta_V[c] / (P_r * l).
 
 Readings where the pages are silent are listed with each function.
@@ -336,8 +335,11 @@ def logits(pro: Prologue, b: int, h: int, qb: int) -> np.ndarray:
 def attend_block(pro: Prologue, b: int, h: int, qb: int, return_state: bool = False):
     """O9-O10 for the rows of Q block qb: output fp64 [rows, d].
 
-    Reading (pages silent): the row sum l accumulates the unquantized p; only the PV
-    operand is quantized.  Blocks are visited in ascending key order.
+    Reading (pages silent on the row sum): l accumulates the weights that multiply V -- the
+    quantized P~_q / P_r in the FP8 mode, p itself when P V is not quantized -- so the output
+    is a weighted mean whose weights sum to exactly 1.  (Against exact attention this is as
+    accurate as summing the unquantized p, slightly more on most inputs.)  Blocks are visited
+    in ascending key order.
     """
     g = pro.geom
     hk = pro.kv_head(h)
@@ -362,11 +364,11 @@ def attend_block(pro: Prologue, b: int, h: int, qb: int, return_state: bool = Fa
         finite = np.isfinite(m_new)
         alpha = np.where(np.isfinite(m), np.exp(m - np.where(finite, m_new, 0.0)), 0.0)
         p = np.where(finite[:, None], np.exp(zb - np.where(finite, m_new, 0.0)[:, None]), 0.0)
-        l = l * alpha + p.sum(axis=1)
         if pro.quant_pv:
             pt = fp8.round_sat((p * p_r).astype(F32))     # P~_q = E4M3sat(RN32(p * P_r))
         else:
             pt = p
+        l = l * alpha + pt.sum(axis=1) / p_r               # the weights that multiply V
         local = pt @ vq[c0:c1]                             # block-local accumulation
         acc = acc * alpha[:, None] + local                 # global accumulation
         m = m_new
@@ -383,9 +385,10 @@ def fp8_midpoint_slack(pro: Prologue, b: int, h: int, qb: int, rel: float = 2.0 
     Reading: a P~ element whose p * P_r lies within `rel` (relative) of the midpoint between two
     E4M3 values has two correct codes -- a computation of the logits in fp32 (any faithful one,
     as on the GPU) may land on either side.  Both results are outputs of the method, so a parity
-    check accepts either: each such element may change its row's output in channel c by at most
-    (the gap between the two codes) * |V_q[j, c]| * delta_V[c] / (P_r * l), later rescalings being
-    factors <= 1.  Zero where no decision is ambiguous (almost everywhere).
+    check accepts either.  O = N / L with N = sum P~ V_q delta_V and L = sum P~ (in P~ units);
+    codes moving by gaps g_j give O' - O = sum g_j (v_j - O) / (L + sum g_j), so
+    |O' - O| <= sum g_j (|V_q[j] delta_V| + |O|) / (L - sum g_j); later rescalings scale the g_j
+    of an earlier block by factors <= 1.  Zero where no decision is ambiguous (almost everywhere).
     """
     g = pro.geom
     hk = pro.kv_head(h)
@@ -398,28 +401,28 @@ def fp8_midpoint_slack(pro: Prologue, b: int, h: int, qb: int, rel: float = 2.0 
     vmag = np.abs(fp8.decode(pro.v_codes[b, hk])) * pro.v_delta[b, hk].astype(F64)[None, :]
     p_r = F64(g.p_range)
     m = np.full(rows, -np.inf)
-    l = np.zeros(rows)
-    slack = np.zeros((rows, pro.d))
+    gv = np.zeros((rows, pro.d))                       # sum g_j |V_q[j] delta_V|
+    gs = np.zeros(rows)                                # sum g_j
     for kb in range(pro.nkb):
         c0, c1 = kb * g.bk, min(pro.N, (kb + 1) * g.bk)
         zb = z[:, c0:c1]
         m_new = np.maximum(m, zb.max(axis=1))
         finite = np.isfinite(m_new)
-        alpha = np.where(np.isfinite(m), np.exp(m - np.where(finite, m_new, 0.0)), 0.0)
         p = np.where(finite[:, None], np.exp(zb - np.where(finite, m_new, 0.0)[:, None]), 0.0)
-        l = l * alpha + p.sum(axis=1)
         x = p * p_r
         i = np.clip(np.searchsorted(mids, x), 0, len(mids) - 1)
-        near = np.zeros(x.shape, bool)
         gap = np.zeros(x.shape)
         for j in (i - 1, i):                            # the two closest midpoints
             jj = np.clip(j, 0, len(mids) - 1)
             hit = np.abs(x - mids[jj]) <= rel * np.maximum(x, mids[jj])
             gap = np.where(hit, np.maximum(gap, gaps[jj]), gap)
-            near |= hit
-        slack += (np.where(near, gap, 0.0)) @ vmag[c0:c1]
+        gv += gap @ vmag[c0:c1]
+        gs += gap.sum(axis=1)
         m = m_new
-    return slack / (p_r * np.where(l > 0, l, 1.0))[:, None]
+    out, _, l = attend_block(pro, b, h, qb, return_state=True)
+    big_l = p_r * l                                    # L in P~ units
+    denom = np.where(big_l - gs > 0, big_l - gs, np.inf)
+    return (gv + gs[:, None] * np.abs(out)) / denom[:, None]
 
 
 def sage_attention(q, k, v, causal: bool = False, qk_bits: int = 8, geom: Geometry = DEFAULT,

@@ -66,6 +66,8 @@ template <> struct PV16T<true> {
 };
 
 constexpr float kLog2Pr = 8.807354922057604f;   // log2(448)
+// FP8 E4M3 1.0 in all 32 bytes of an MFMA operand
+#define kOnesFp8 ((v8i){0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838})
 
 struct AttnArgs {
   const int8_t* qcodes;
@@ -447,7 +449,6 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
 
     // P~ = E4M3(p * P_r), packed straight into the FP8 MFMA B operand
     v8i pb[BK / 64];
-    float lsum = 0.f;
 #pragma unroll
     for (int t = 0; t < BK / 32; ++t) {
 #pragma unroll
@@ -456,13 +457,21 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
         const float p1 = __builtin_amdgcn_exp2f(z[t][4 * qq + 1] - mo);
         const float p2 = __builtin_amdgcn_exp2f(z[t][4 * qq + 2] - mo);
         const float p3 = __builtin_amdgcn_exp2f(z[t][4 * qq + 3] - mo);
-        lsum += (p0 + p1) + (p2 + p3);
         int word = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
         word = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, word, true);
         pb[t >> 1][(t & 1) * 4 + qq] = word;
       }
     }
-    l_part = fmaf(l_part, alpha, lsum);
+    // the row sum of the weights that multiply V: P~ against an all-ones A operand on the FP8
+    // MFMA (every output row is the column sum, both lane halves included) -- two matrix
+    // instructions instead of 64 vector adds per lane
+    {
+      v16f ls = {};
+#pragma unroll
+      for (int u = 0; u < BK / 64; ++u)
+        ls = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kOnesFp8, pb[u], ls, 0, 0, 0, 0, 0, 0);
+      l_part = fmaf(l_part, alpha, ls[0]);
+    }
 
     // P~ V: block-local accumulation from zero, then the fp32 global accumulator
 #pragma unroll
@@ -492,9 +501,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
   for (int kb = 0; kb < nfull; ++kb) block(kb, std::false_type{});
   if (mask_last) block(nblk - 1, std::true_type{});
 
-  // epilogue: O = acc * delta_V / l   (FP8: l counts p * P_r, so it carries the 1/P_r;
-  // fp16: no V scale)
-  const float l = xhalf_sum(l_part);
+  // epilogue: O = acc * delta_V / l   (FP8: l sums P~, so it carries the 1/P_r, and the MFMA
+  // has already added both lane halves; fp16: no V scale, per-lane partial sums)
+  const float l = PV16 ? xhalf_sum(l_part) : l_part;
   const float inv_l = l > 0.f ? 1.f / l : 0.f;
   if (i < N) {
     __half* orow = a.o + b * a.g.st.qb + (long long)(sq.tok0 + i) * a.g.st.qt + h * a.g.st.qh;

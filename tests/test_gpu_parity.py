@@ -56,6 +56,10 @@ def _check_o(o_gpu, o_ref, what, slack=None):
     diff = np.abs(o_gpu - o_ref)
     err = diff.max()
     scale = np.abs(o_ref).max()
+    if scale == 0:                       # an all-zero reference (zero V): zeros, exactly
+        _say(f"  {what}: reference is all zero; max|O_gpu| = {np.abs(o_gpu).max()}")
+        assert np.all(o_gpu == 0), f"{what}: nonzero output for an all-zero reference"
+        return
     cos = (o_gpu * o_ref).sum() / math.sqrt((o_gpu ** 2).sum() * (o_ref ** 2).sum())
     allowed = O_REL_TOL * scale + (0.0 if slack is None else slack)
     beyond = diff > O_REL_TOL * scale
@@ -137,35 +141,78 @@ SMALL16 = [
 CASES = [(n, w, 8) for n, w in SMALL] + [(n, w, 16) for n, w in SMALL16]
 
 
-@pytest.mark.parametrize("name,w,pv_bits", CASES, ids=[c[0] for c in CASES])
-def test_small_case_full_parity(sa, name, w, pv_bits):
-    _say(f"[case {name}] B{w.B} H{w.H} Hkv{w.Hkv} N{w.N} d{w.d} causal={w.causal} bits={w.qk_bits} pv={pv_bits}")
-    q, k, v = make_inputs(w, seed=0)
+def _full_parity(sa, name, q, k, v, causal, bits, pv_bits):
+    """Every prologue tensor of every head, every output element, and the raw int32 tiles of the
+    last head, against the oracle."""
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
     qpv = pv_bits == 8
-    dev, o_gpu, dbg = _run(sa, q, k, v, w.causal, w.qk_bits, pv_bits=pv_bits)
-    pro = osage.prologue(q, k, v, w.causal, w.qk_bits, quant_pv=qpv)
-    o_ref = np.zeros((w.B, w.H, w.N, w.d))
+    dev, o_gpu, dbg = _run(sa, q, k, v, causal, bits, pv_bits=pv_bits)
+    pro = osage.prologue(q, k, v, causal, bits, quant_pv=qpv)
+    o_ref = np.zeros((B, H, N, d))
     slack = np.zeros_like(o_ref)
-    for b in range(w.B):
-        for h in range(w.H):
-            hk = h // (w.H // w.Hkv)
-            ph = osage.prologue(*_head_slice(q, k, v, b, h, w.H, w.Hkv), w.causal, w.qk_bits, quant_pv=qpv)
+    for b in range(B):
+        for h in range(H):
+            hk = h // (H // Hkv)
+            ph = osage.prologue(*_head_slice(q, k, v, b, h, H, Hkv), causal, bits, quant_pv=qpv)
             _check_prologue(dbg, ph, b, h, hk, f"{name} b{b} h{h}")
             for qb in range(pro.nqb):
-                r0, r1 = qb * 128, min(w.N, qb * 128 + 128)
+                r0, r1 = qb * 128, min(N, qb * 128 + 128)
                 o_ref[b, h, r0:r1] = osage.attend_block(pro, b, h, qb)
                 if qpv:
                     slack[b, h, r0:r1] = osage.fp8_midpoint_slack(pro, b, h, qb)
     _check_o(o_gpu, o_ref, name, slack)
     # raw int32 tiles of (b=last, h=last) for every (qb, kb)
-    b, h = w.B - 1, w.H - 1
+    b, h = B - 1, H - 1
     for qb in range(pro.nqb):
         for kb in range(pro.nkb):
-            tile = sa.qk_tile_debug(*dev, b, h, qb, kb, w.causal, w.qk_bits, pv_bits).cpu().numpy()
-            r0, r1 = qb * 128, min(w.N, qb * 128 + 128)
-            c0, c1 = kb * 128, min(w.N, kb * 128 + 128)
+            tile = sa.qk_tile_debug(*dev, b, h, qb, kb, causal, bits, pv_bits).cpu().numpy()
+            r0, r1 = qb * 128, min(N, qb * 128 + 128)
+            c0, c1 = kb * 128, min(N, kb * 128 + 128)
             ref = osage.scores_int(pro, b, h, slice(r0, r1), slice(c0, c1))
             np.testing.assert_array_equal(tile[:r1 - r0, :c1 - c0], ref, err_msg=f"{name} tile {qb},{kb}")
+
+
+@pytest.mark.parametrize("name,w,pv_bits", CASES, ids=[c[0] for c in CASES])
+def test_small_case_full_parity(sa, name, w, pv_bits):
+    _say(f"[case {name}] B{w.B} H{w.H} Hkv{w.Hkv} N{w.N} d{w.d} causal={w.causal} bits={w.qk_bits} pv={pv_bits}")
+    q, k, v = make_inputs(w, seed=0)
+    _full_parity(sa, name, q, k, v, w.causal, w.qk_bits, pv_bits)
+
+
+def _degenerate(name):
+    """Inputs for the method's degenerate cases (seed 11): all zero; zero V; every key equal (so
+    gamma_K = 0: zero K groups, scales and Delta_S) with one Q block of equal rows (zero Q
+    groups) and a zero and a constant V channel."""
+    rng = np.random.default_rng(11)
+    f16 = lambda *s: rng.standard_normal(s).astype(np.float16)
+    if name == "zero-qkv":
+        z = np.zeros((1, 2, 200, 64), np.float16)
+        return z, z[:, :1].copy(), z[:, :1].copy()
+    if name == "zero-v":
+        k = f16(1, 1, 200, 64)
+        return f16(1, 2, 200, 64), k, np.zeros_like(k)
+    q = f16(1, 2, 300, 128)
+    q[:, :, :128] = q[:, :, :1]
+    k = np.repeat(f16(1, 2, 1, 128), 300, axis=2)
+    v = f16(1, 2, 300, 128)
+    v[..., 0] = 0
+    v[..., 1] = 2.5
+    return q, k, v
+
+
+DEGENERATE = [("zero-qkv", False, 8, 8), ("zero-v", True, 4, 8), ("equal-keys", True, 4, 8),
+              ("equal-keys", False, 8, 8), ("equal-keys", False, 8, 16)]
+
+
+@pytest.mark.parametrize("name,causal,bits,pv_bits", DEGENERATE,
+                         ids=[f"{c[0]}-{'causal' if c[1] else 'full'}-int{c[2]}-pv{c[3]}" for c in DEGENERATE])
+def test_degenerate_inputs_full_parity(sa, name, causal, bits, pv_bits):
+    """Zero groups take a zero scale and zero codes on both sides (no 0/0), a zero V gives an
+    exactly zero output, and equal keys give equal weights (every P~ code is P_r exactly)."""
+    q, k, v = _degenerate(name)
+    _say(f"[degenerate {name}] {q.shape} Hkv{k.shape[1]} causal={causal} bits={bits} pv={pv_bits}")
+    _full_parity(sa, name, q, k, v, causal, bits, pv_bits)
 
 
 def test_deterministic(sa):

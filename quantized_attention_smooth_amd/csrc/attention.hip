@@ -95,12 +95,18 @@ struct Smem {
   __attribute__((aligned(16))) float ds[2][BK];
 };
 
-// The int32 S^T accumulators start from the bit pattern of the float 1.5 * 2^23.  |S| <= 127^2 * 128
-// < 2^21, so after the integer MFMA adds S the bits read as the float 1.5 * 2^23 + S exactly (same
-// binade, unit spacing); one exact fp32 subtraction then yields S as a float.  This replaces the
-// int->float conversion, which issues at a quarter of the fp32 add rate on gfx950.
-constexpr int kAccBias = 0x4B400000;
+// int32 S^T accumulators to floats, exactly (|S| <= 127^2 * 128 < 2^21).  At d = 128 they start
+// from the bit pattern of the float 1.5 * 2^23, so after the MFMA adds S the bits read as the
+// float 1.5 * 2^23 + S (same binade, unit spacing) and one fp32 subtraction yields S.  At d = 64
+// they start from zero and v_cvt_f32_i32 converts them: it issues at about a third of the add rate
+// but beside the matrix unit, which measured 2 % faster there and about 1 % slower at d = 128.
+template <int D> constexpr bool kCvtS = D == 64;
+template <int D> constexpr int kAccInit = kCvtS<D> ? 0 : 0x4B400000;
 constexpr float kAccBiasF = 12582912.0f;   // 1.5 * 2^23
+template <int D>
+__device__ inline float s_to_float(int acc) {
+  return kCvtS<D> ? (float)acc : __int_as_float(acc) - kAccBiasF;
+}
 
 // XOR swizzles of the 16-byte chunk index inside an LDS row.  Each operand read has 32 lanes
 // fetch 16 bytes from 32 consecutive rows at one logical chunk; the swizzles spread those rows
@@ -219,7 +225,7 @@ __device__ inline void wait_all_but_k_tile() {
 }
 
 // S^T tiles (32 keys each) x the wave's 32 queries, exact.  INT8 codes: v_mfma_i32_32x32x32_i8
-// from the biased accumulator (see kAccBias), 16 code bytes per lane per k-step.  INT4-range codes
+// from kAccInit, 16 code bytes per lane per k-step.  INT4-range codes
 // (stored as FP6 E2M3, 24 bytes of each 32-byte slot): v_mfma_f32_32x32x64_f8f6f4 in FP6 mode from
 // zero, one slot per lane per k-step, at twice the INT8 rate; the products and sums of integers
 // this small are exact in its accumulator, so S arrives as fp32.
@@ -244,8 +250,8 @@ __device__ inline void qk_tiles(const Smem<D, PV16>& sm, int st, const v4i (&qre
 #pragma unroll
       for (int e = 0; e < 16; ++e) sacc[t][e] = __float_as_int(acc[e]);
     } else {
-      v16i acc = {kAccBias, kAccBias, kAccBias, kAccBias, kAccBias, kAccBias, kAccBias, kAccBias,
-                  kAccBias, kAccBias, kAccBias, kAccBias, kAccBias, kAccBias, kAccBias, kAccBias};
+      constexpr int a0 = kAccInit<D>;
+      v16i acc = {a0, a0, a0, a0, a0, a0, a0, a0, a0, a0, a0, a0, a0, a0, a0, a0};
 #pragma unroll
       for (int s = 0; s < D / 32; ++s) {
         const int pc = (2 * s + half) ^ kswz<D>(row);
@@ -320,7 +326,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int jl = 32 * t + 8 * (e >> 2) + 4 * half + (e & 3);
-        a.dbg_out[il * BK + jl] = QK4 ? (int32_t)__int_as_float(sacc[t][e]) : sacc[t][e] - kAccBias;
+        a.dbg_out[il * BK + jl] = QK4 ? (int32_t)__int_as_float(sacc[t][e]) : (int32_t)s_to_float<D>(sacc[t][e]);
       }
     return;
   }
@@ -372,7 +378,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const float sf = QK4 ? __int_as_float(sacc[t][4 * qq + r])                // exact S
-                               : __int_as_float(sacc[t][4 * qq + r]) - kAccBiasF;
+                               : s_to_float<D>(sacc[t][4 * qq + r]);      // exact
           float x = fmaf(sf, cmul, dsa[r]);
           if (MASK) {
             const int j = kb * BK + j0 + r;
@@ -457,7 +463,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
         const float p1 = __builtin_amdgcn_exp2f(z[t][4 * qq + 1] - mo);
         const float p2 = __builtin_amdgcn_exp2f(z[t][4 * qq + 2] - mo);
         const float p3 = __builtin_amdgcn_exp2f(z[t][4 * qq + 3] - mo);
-        int word = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+        // the first convert writes the low half; passing p0's (dead) bits as the untouched high
+        // half saves materialising a zero register per word
+        int word = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, __float_as_int(p0), false);
         word = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, word, true);
         pb[t >> 1][(t & 1) * 4 + qq] = word;
       }

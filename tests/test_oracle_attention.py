@@ -35,6 +35,19 @@ def test_unquantized_reduces_to_exact_attention(causal, H, Hkv):
     assert np.abs(o - e).max() < 1e-12
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_exact_attention_matches_torch_sdpa(causal):
+    """The fp64 reference itself, against PyTorch's scaled_dot_product_attention on the CPU in
+    float64 (an independent implementation; GQA by repeating each kv head H / Hkv times)."""
+    torch = pytest.importorskip("torch")
+    q, k, v = make_inputs(custom(2, 4, 2, 77, 32, q_bias_std=1.0), seed=21)
+    e = sage.exact_attention(q, k, v, causal)
+    tq, tk, tv = (torch.from_numpy(x.astype(np.float64)) for x in (q, k, v))
+    tk, tv = tk.repeat_interleave(2, dim=1), tv.repeat_interleave(2, dim=1)
+    t = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal).numpy()
+    assert np.abs(e - t).max() < 1e-12
+
+
 def test_unquantized_ragged_close_to_exact():
     q, k, v = make_inputs(custom(2, 2, 1, 301, 64, q_bias_std=1.0), seed=11)
     for causal in (False, True):

@@ -23,7 +23,9 @@
 //     sums its products with reduced internal precision, so the block-local step bounds that
 //     error to one block, as on the hardware the pages target.
 //   * K/V code tiles stream HBM -> LDS with direct-to-LDS loads (global_load_lds_dwordx4),
-//     double buffered, 16-byte chunks XOR-swizzled against LDS bank conflicts.
+//     in a ring of two stages (three at d = 64 in the FP8 mode, where a block's arithmetic is
+//     too short to cover a tile issued only one block ahead), 16-byte chunks XOR-swizzled
+//     against LDS bank conflicts.
 //   * Workgroup ids are remapped so each XCD (own L2) works through whole heads (of every
 //     sequence of the batch); causal grids start with each sequence's longest (diagonal-most)
 //     query blocks.
@@ -85,14 +87,17 @@ struct AttnArgs {
   int32_t* dbg_out;
 };
 
-// V stages: FP8 codes [64-key group][channel][64 slots], double buffered; or fp16 V
+// V stages: FP8 codes [64-key group][channel][64 slots], one per K stage; or fp16 V
 // [16-key group][channel][16 slots], one stage.  16-byte chunks swizzled in both.
 template <int D, bool PV16>
 struct Smem {
-  static constexpr int VST = PV16 ? 1 : 2;
-  __attribute__((aligned(16))) int8_t k[2][BK * D];    // K tile rows, 16-byte chunks swizzled
+  // K (and FP8 V, Delta_S) stages: a ring of three at d = 64 in the FP8 mode, where a block's
+  // arithmetic is short enough that a tile issued one block ahead can still be in flight
+  static constexpr int NST = (!PV16 && D == 64) ? 3 : 2;
+  static constexpr int VST = PV16 ? 1 : NST;
+  __attribute__((aligned(16))) int8_t k[NST][BK * D];  // K tile rows, 16-byte chunks swizzled
   __attribute__((aligned(16))) uint8_t v[VST][BK * D * (PV16 ? 2 : 1)];
-  __attribute__((aligned(16))) float ds[2][BK];
+  __attribute__((aligned(16))) float ds[NST][BK];
 };
 
 // int32 S^T accumulators to floats, exactly (|S| <= 127^2 * 128 < 2^21).  At d = 128 they start
@@ -185,14 +190,14 @@ struct TileLoader {
     }
   }
 
-  // K codes of block kb and its Delta_S row slice (wave 0) into stage st.  The Delta_S load goes
-  // first, so a wait for "all but the last kTileInstrs" loads of wave 0 leaves only K chunks
-  // outstanding.
+  // K codes of block kb and its Delta_S row slice into stage st (each wave a quarter of the
+  // slice, so every wave issues the same number of loads per block).  The Delta_S load goes
+  // first, so a wait for "all but the last kTileInstrs" loads leaves only K chunks outstanding.
   __device__ void issue_k(Smem<D, PV16>& sm, int st, int kb, int w, int lane) const {
 #if defined(__HIP_DEVICE_COMPILE__)
-    if (w == 0 && lane < BK / 4)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(dp, dbytes), (lds_void*)sm.ds[st], 16, lane * 16,
-                                               kb * BK * 4, 0, 0);
+    if (lane < BK / 4 / WAVES)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(dp, dbytes), (lds_void*)(sm.ds[st] + w * (BK / WAVES)), 16,
+                                               lane * 16 + w * (BK / WAVES) * 4, kb * BK * 4, 0, 0);
     const auto kr = make_rsrc(kp, kbytes);
 #pragma unroll
     for (int m = 0; m < NK; ++m)
@@ -215,6 +220,13 @@ struct TileLoader {
 };
 
 __device__ inline void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// wait until at most the loads of one block (its Delta_S slice, K and V tiles) are outstanding
+template <int D>
+__device__ inline void wait_all_but_one_block() {
+  static_assert(2 * kTileInstrs<D> + 1 == 5, "vmcnt immediate");
+  asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+}
 
 // wait until at most the last kTileInstrs<D> vector loads of this wave are outstanding
 template <int D>
@@ -337,21 +349,33 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
 #pragma unroll
   for (int ct = 0; ct < D / 32; ++ct) og[ct] = (v16f){};
 
-  ld.issue_v(sm, 0, 0, w);
-  ld.issue_k(sm, 0, 0, w, lane);
-  wait_loads();
+  constexpr int NST = Smem<D, PV16>::NST;
+  // blocks 0 .. NST - 2 into stages 0 .. NST - 2; wait for block 0
+  for (int i = 0; i < NST - 1 && i < nblk; ++i) {
+    ld.issue_v(sm, i, i, w);
+    ld.issue_k(sm, i, i, w, lane);
+  }
+  if constexpr (NST == 3) {
+    if (nblk > 1) wait_all_but_one_block<D>();
+    else wait_loads();
+  } else {
+    wait_loads();
+  }
   __syncthreads();
+  int st = 0;                                   // stage of block kb: kb % NST
 
   // One KV block: S^T on the int8 MFMA, dequantize + bias (+ mask), online softmax, P~ V on the
   // FP8 MFMA (or P V on the fp16 MFMA).  MASK is set only for the last block of a row range
   // (causal diagonal or ragged tail).
   auto block = [&](const int kb, auto mask_tag) {
     constexpr bool MASK = decltype(mask_tag)::value;
-    const int st = kb & 1;
     const bool more = kb + 1 < nblk;
-    if (more) {
-      if (!PV16) ld.issue_v(sm, st ^ 1, kb + 1, w);
-      ld.issue_k(sm, st ^ 1, kb + 1, w, lane);
+    // block kb + NST - 1 into the stage block kb - 1 used (every wave is past its barrier)
+    const int stn = st == 0 ? NST - 1 : st - 1;
+    const bool issue = kb + NST - 1 < nblk;
+    if (issue) {
+      if (!PV16) ld.issue_v(sm, stn, kb + NST - 1, w);
+      ld.issue_k(sm, stn, kb + NST - 1, w, lane);
     }
 
     v16i sacc[BK / 32];
@@ -450,6 +474,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
       wait_loads();
       __syncthreads();
       if (more) ld.issue_v(sm, 0, kb + 1, w);
+      st = st + 1 == NST ? 0 : st + 1;
       return;
     }
 
@@ -499,8 +524,15 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
       for (int e = 0; e < 16; ++e) og[ct][e] = fmaf(og[ct][e], alpha, loc[e]);
     }
 
-    wait_loads();
+    // block kb + 1 has landed (the loads issued above, for block kb + NST - 1, may still fly)
+    if constexpr (NST == 3) {
+      if (issue) wait_all_but_one_block<D>();
+      else wait_loads();
+    } else {
+      wait_loads();
+    }
     __syncthreads();
+    st = st + 1 == NST ? 0 : st + 1;
   };
 
   // the last block needs masking when causal (diagonal block) or when N is not a multiple of BK

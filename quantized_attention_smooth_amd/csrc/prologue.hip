@@ -167,23 +167,33 @@ __global__ void init_stats(unsigned long long* ksum, unsigned int* vamax, int n,
 // 16-bit floats) skips V entirely.
 // grid (ceil(longest / 256), B*Hkv), 256 threads; thread = (row slot, 8-channel chunk).
 // ---------------------------------------------------------------------------------------
+template <int D, typename T>
+struct KvStatsSmem {
+  static constexpr int RPP = 256 / (D / 8);
+  static constexpr bool BF = std::is_same<T, __bf16>::value;
+  double ls[BF ? 1 : RPP][D];
+  float lm[RPP][D];
+  unsigned long long acc[BF ? D * kLimbs : 1];
+};
+
+// (bx, by): the workgroup's token tile and (sequence, kv head)
 template <int D, bool VSTATS, typename T>
-__global__ __launch_bounds__(256) void kv_stats(const T* __restrict__ k, const T* __restrict__ v,
-                                                unsigned long long* __restrict__ ksum,
-                                                unsigned int* __restrict__ vamax, Geo g) {
+__device__ inline void kv_stats_body(const T* __restrict__ k, const T* __restrict__ v,
+                                     unsigned long long* __restrict__ ksum, unsigned int* __restrict__ vamax,
+                                     const Geo& g, int bx, int by, KvStatsSmem<D, T>& sm) {
   constexpr int TPR = D / 8;      // threads per row
   constexpr int RPP = 256 / TPR;  // rows per pass
   constexpr int TOK = 256;        // tokens per workgroup
   constexpr bool BF = std::is_same<T, __bf16>::value;
-  __shared__ double ls[BF ? 1 : RPP][D];
-  __shared__ float lm[RPP][D];
-  __shared__ unsigned long long acc[BF ? D * kLimbs : 1];
+  auto& ls = sm.ls;
+  auto& lm = sm.lm;
+  auto& acc = sm.acc;
   const int tid = threadIdx.x, cq = tid % TPR, r0 = tid / TPR;
-  const size_t bh = blockIdx.y;                 // (sequence, kv head)
+  const size_t bh = by;                         // (sequence, kv head)
   const int sidx = (int)bh / g.Hkv, hk = (int)bh % g.Hkv;
   const Seq sq = g.seq(sidx);
   const int N = sq.n;
-  if ((int)blockIdx.x * TOK >= N) return;
+  if (bx * TOK >= N) return;
   const long long base = sidx * g.st.kb + (long long)sq.tok0 * g.st.kt + hk * g.st.kh;
   const T* kb = k + base;
   const T* vb = v + base;
@@ -198,7 +208,7 @@ __global__ __launch_bounds__(256) void kv_stats(const T* __restrict__ k, const T
     for (int i = tid; i < D * kLimbs; i += 256) acc[i] = 0ull;
     __syncthreads();
   }
-  const int tok0 = blockIdx.x * TOK;
+  const int tok0 = bx * TOK;
   // 4 passes at a time, loads issued before use: rows past N read row N - 1 (in bounds) and are
   // skipped afterwards, so no load waits behind its own branch
   constexpr int CH = 4;
@@ -448,18 +458,29 @@ __global__ __launch_bounds__(256) void kv_quant(const T* __restrict__ k, const T
 // Q smoothing (per 128-row block mean) + per-row quantization.
 // grid (blocks of the longest sequence, B*H), 256 threads.
 // ---------------------------------------------------------------------------------------
+template <int D, typename T>
+struct QQuantSmem {
+  static constexpr int RPP = 256 / (D / 8);
+  static constexpr bool BF = std::is_same<T, __bf16>::value;
+  double ls[BF ? 1 : RPP][D];
+  float lmu[D];
+  unsigned long long acc[BF ? D * kLimbs : 1];
+};
+
+// (bx, by): the workgroup's Q block and (sequence, head)
 template <int D, typename T, bool QK4>
-__global__ __launch_bounds__(256) void q_quant(const T* __restrict__ q, int8_t* __restrict__ qcodes,
-                                               float* __restrict__ qscale, float* __restrict__ muq,
-                                               uint16_t* __restrict__ muqs, Geo g, float R) {
+__device__ inline void q_quant_body(const T* __restrict__ q, int8_t* __restrict__ qcodes,
+                                    float* __restrict__ qscale, float* __restrict__ muq,
+                                    uint16_t* __restrict__ muqs, const Geo& g, float R, int bx, int by,
+                                    QQuantSmem<D, T>& sm) {
   constexpr int TPR = D / 8, RPP = 256 / TPR, PASSES = BQ / RPP;
   constexpr bool BF = std::is_same<T, __bf16>::value;
-  __shared__ double ls[BF ? 1 : RPP][D];
-  __shared__ float lmu[D];
-  __shared__ unsigned long long acc[BF ? D * kLimbs : 1];
+  auto& ls = sm.ls;
+  auto& lmu = sm.lmu;
+  auto& acc = sm.acc;
   const int tid = threadIdx.x, cq = tid % TPR, r0 = tid / TPR;
-  const int qb = blockIdx.x;
-  const int sidx = (int)blockIdx.y / g.H, h = (int)blockIdx.y % g.H;
+  const int qb = bx;
+  const int sidx = by / g.H, h = by % g.H;
   const Seq sq = g.seq(sidx);
   if (qb >= seq_blocks(sq)) return;
   const int N = sq.n;
@@ -545,6 +566,28 @@ __global__ __launch_bounds__(256) void q_quant(const T* __restrict__ q, int8_t* 
     store_codes<QK4>(qcodes + (rows + row) * D, cq, y);
     if (cq == 0) qscale[rows + row] = am / R;
   }
+}
+
+// ---------------------------------------------------------------------------------------
+// K/V channel statistics and the Q prologue in one launch (they are independent): workgroups
+// 0 .. nks - 1 take the statistics tiles, the rest the Q blocks, so the Q blocks' load and
+// reduction latency overlaps the statistics stream and one launch (and its tail) is saved.
+// grid (nks + nqb * B*H), 256 threads.
+// ---------------------------------------------------------------------------------------
+template <int D, bool VSTATS, typename T, bool QK4>
+__global__ __launch_bounds__(256) void stats_and_q(const T* __restrict__ k, const T* __restrict__ v,
+                                                   unsigned long long* __restrict__ ksum,
+                                                   unsigned int* __restrict__ vamax, const T* __restrict__ q,
+                                                   int8_t* __restrict__ qcodes, float* __restrict__ qscale,
+                                                   float* __restrict__ muq, uint16_t* __restrict__ muqs, Geo g,
+                                                   float R, int stx, int nks, int nqb) {
+  __shared__ union U {
+    KvStatsSmem<D, T> ks;
+    QQuantSmem<D, T> qq;
+  } sm;
+  const int i = blockIdx.x;
+  if (i < nks) kv_stats_body<D, VSTATS, T>(k, v, ksum, vamax, g, i % stx, i / stx, sm.ks);
+  else q_quant_body<D, T, QK4>(q, qcodes, qscale, muq, muqs, g, R, (i - nks) % nqb, (i - nks) / nqb, sm.qq);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -896,18 +939,27 @@ hipError_t launch_prologue_d(const Dims& Dm, const Ptrs& P, hipStream_t s) {
         k, v, P.ksum, P.vamax, P.kcodes, P.vcodes, P.kscale, P.muk, P.vscale, g, R);
   };
   const bool qk4 = Dm.qk_bits == 4;
+  // statistics (K, and V unless it stays 16-bit) and the Q prologue: one launch
+  const int nks = (int)(gs.x * gs.y), nsq = nks + Dm.nqb * Dm.B * Dm.H;
+  auto sq = [&](auto vstats, auto q4) {
+    stats_and_q<D, decltype(vstats)::value, T, decltype(q4)::value><<<nsq, 256, 0, s>>>(
+        k, v, P.ksum, P.vamax, q, P.qcodes, P.qscale, P.muq, P.muqs, g, R, (int)gs.x, nks, Dm.nqb);
+  };
+  const bool vstats = Dm.pv_bits != 16;
+  if (vstats) {
+    if (qk4) sq(std::true_type{}, std::true_type{});
+    else sq(std::true_type{}, std::false_type{});
+  } else {
+    if (qk4) sq(std::false_type{}, std::true_type{});
+    else sq(std::false_type{}, std::false_type{});
+  }
   if (Dm.pv_bits == 16) {
-    kv_stats<D, false, T><<<gs, 256, 0, s>>>(k, v, P.ksum, P.vamax, g);
     if (qk4) kvq(std::true_type{}, std::true_type{});
     else kvq(std::true_type{}, std::false_type{});
   } else {
-    kv_stats<D, true, T><<<gs, 256, 0, s>>>(k, v, P.ksum, P.vamax, g);
     if (qk4) kvq(std::false_type{}, std::true_type{});
     else kvq(std::false_type{}, std::false_type{});
   }
-  const dim3 gqq(Dm.nqb, Dm.B * Dm.H);
-  if (qk4) q_quant<D, T, true><<<gqq, 256, 0, s>>>(q, P.qcodes, P.qscale, P.muq, P.muqs, g, R);
-  else q_quant<D, T, false><<<gqq, 256, 0, s>>>(q, P.qcodes, P.qscale, P.muq, P.muqs, g, R);
   const float k2 = (float)(1.4426950408889634 / sqrt((double)D));
   // the K-block form pays off when each key block serves many Q blocks
   if ((size_t)(Dm.H / Dm.Hkv) * Dm.nqb >= 1024) {

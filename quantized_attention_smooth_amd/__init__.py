@@ -237,10 +237,10 @@ def sageattn(q, k, v, attn_mask=None, dropout_p: float = 0.0, is_causal: bool = 
     """Quantized drop-in for F.scaled_dot_product_attention(q, k, v, is_causal=...).
 
     tensor_layout "HND": q [B, H, N, d], k/v [B, Hkv, N, d]; "NHD": q [B, N, H, d],
-    k/v [B, N, Hkv, d].  fp16, contiguous; d in {64, 128}; qk_bits 8 (INT8 codes) or 4
-    (INT4-range codes); pv_bits 8 (FP8 P~ and V, the fast mode) or 16 (fp16 P and V, the
-    high-fidelity mode).  Grouped-query attention maps head h to kv head h // (H // Hkv).
-    Returns o shaped and laid out like q.
+    k/v [B, N, Hkv, d].  fp16 or bf16 (all three alike), contiguous; d in {64, 128}; qk_bits 8
+    (INT8 codes) or 4 (INT4-range codes); pv_bits 8 (FP8 P~ and V, the fast mode) or 16 (16-bit
+    P and V, the high-fidelity mode).  Grouped-query attention maps head h to kv head
+    h // (H // Hkv).  Returns o shaped, laid out and typed like q.
     """
     if attn_mask is not None or dropout_p != 0.0 or scale is not None:
         raise NotImplementedError("attn_mask, dropout and custom scale are not supported")
@@ -272,7 +272,7 @@ def sageattn_varlen(q, k, v, cu_seqlens, is_causal: bool = False, qk_bits: int =
     """Variable-length batch: q [T, H, d], k/v [T, Hkv, d] hold the sequences back to back;
     sequence s is tokens cu_seqlens[s] .. cu_seqlens[s + 1] - 1 (cu_seqlens: a host list or CPU
     tensor of B + 1 increasing ints from 0 to T).  Each sequence is attended, smoothed and
-    quantized on its own.  Returns o [T, H, d]."""
+    quantized on its own.  fp16 or bf16.  Returns o [T, H, d]."""
     _check_qkv(q, k, v, 3)
     T, H, d = q.shape
     Hkv = k.shape[1]

@@ -22,7 +22,7 @@
 //     into the fp32 output accumulator: O = O * alpha + local.  On gfx950 the FP8 MFMA also
 //     sums its products with reduced internal precision, so the block-local step bounds that
 //     error to one block, as on the hardware the pages target.
-//   * K/V code tiles stream HBM -> LDS with direct-to-LDS loads (global_load_lds_dwordx4),
+//   * K/V code tiles stream HBM -> LDS with direct-to-LDS buffer loads (buffer_load_dwordx4 lds),
 //     in a ring of two stages (three at d = 64 in the FP8 mode, where a block's arithmetic is
 //     too short to cover a tile issued only one block ahead), 16-byte chunks XOR-swizzled
 //     against LDS bank conflicts.

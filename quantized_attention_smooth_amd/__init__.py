@@ -10,6 +10,8 @@ library is missing or fails to load, importing this package raises ImportError.
     o = sageattn(q, k, v, is_causal=True, qk_bits=8, pv_bits=8)   # like F.scaled_dot_product_attention
     o = sageattn(q, k, v, tensor_layout="NHD")                     # q [B, N, H, d]
     o = sageattn_varlen(q, k, v, cu_seqlens, is_causal=True)       # packed q [T, H, d]
+    attn = SageAttention(head_dim=128, is_causal=True, quant_mode="qk_int8_pv_fp16")
+    o = attn(q, k, v)                                              # module-style, reuses its workspace
 """
 from __future__ import annotations
 
@@ -18,7 +20,7 @@ import os
 
 import torch
 
-__all__ = ["sageattn", "sageattn_varlen", "fwd", "prologue", "attend", "workspace_bytes", "get_config",
+__all__ = ["sageattn", "sageattn_varlen", "SageAttention", "QUANT_MODES", "fwd", "prologue", "attend", "workspace_bytes", "get_config",
            "quant_debug", "qk_tile_debug", "Problem", "LIB_PATH", "SageError"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsage_mi355x.so")
@@ -36,6 +38,10 @@ EXPORTS = ("sage_get_config", "sage_attn_workspace_bytes", "sage_attn_fwd", "sag
            "sage_attn_attend_ex", "sage_quant_debug_ex")
 
 LAYOUTS = {"HND": 0, "NHD": 1}
+#: quant_mode names of the blog page's precision-control section (INT8 QK with FP8 or fp16 PV),
+#: plus their INT4-range QK counterparts, as (qk_bits, pv_bits)
+QUANT_MODES = {"qk_int8_pv_fp8": (8, 8), "qk_int8_pv_fp16": (8, 16),
+               "qk_int4_pv_fp8": (4, 8), "qk_int4_pv_fp16": (4, 16)}
 DTYPES = {torch.float16: 0, torch.bfloat16: 1}
 
 
@@ -244,6 +250,17 @@ def sageattn(q, k, v, attn_mask=None, dropout_p: float = 0.0, is_causal: bool = 
     """
     if attn_mask is not None or dropout_p != 0.0 or scale is not None:
         raise NotImplementedError("attn_mask, dropout and custom scale are not supported")
+    pb = _dense_problem(q, k, v, is_causal, qk_bits, pv_bits, tensor_layout)
+    nbytes = problem_ws_bytes(pb)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = alloc_workspace(nbytes, q.device)
+    o = torch.empty_like(q)
+    fwd_ex(pb, q, k, v, o, workspace)
+    return o
+
+
+def _dense_problem(q, k, v, is_causal, qk_bits, pv_bits, tensor_layout) -> Problem:
+    """The problem descriptor of a fixed-length batch, after checking the tensors."""
     if tensor_layout == "HND" and q.dtype == torch.float16:
         B, H, Hkv, N, d = _shapes(q, k, v)
     else:
@@ -258,13 +275,46 @@ def sageattn(q, k, v, attn_mask=None, dropout_p: float = 0.0, is_causal: bool = 
             raise ValueError(f"tensor_layout must be one of {sorted(LAYOUTS)}")
         if not ok:
             raise ValueError(f"k/v shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
-    pb = Problem(B, H, Hkv, N, d, is_causal, qk_bits, pv_bits, tensor_layout, q.dtype)
-    nbytes = problem_ws_bytes(pb)
-    if workspace is None or workspace.numel() < nbytes:
-        workspace = alloc_workspace(nbytes, q.device)
-    o = torch.empty_like(q)
-    fwd_ex(pb, q, k, v, o, workspace)
-    return o
+    return Problem(B, H, Hkv, N, d, is_causal, qk_bits, pv_bits, tensor_layout, q.dtype)
+
+
+class SageAttention:
+    """Module-style front end (the blog page's core-API call: an attention object built from
+    head_dim, is_causal and quant_mode that replaces a model's attention function).
+
+    quant_mode: one of QUANT_MODES -- "qk_int8_pv_fp8" (fast), "qk_int8_pv_fp16" (high
+    fidelity: V and P stay 16-bit), or the INT4-range QK forms.  Calling it on q, k, v (laid out
+    as tensor_layout, fp16 or bf16) returns o; the workspace is kept and reused while it is
+    large enough, so repeated calls of one shape allocate only the output.  Calls share that
+    workspace: calls of one object that may overlap (on different streams) race."""
+
+    def __init__(self, head_dim: int, is_causal: bool = False, quant_mode: str = "qk_int8_pv_fp8",
+                 tensor_layout: str = "HND"):
+        if head_dim not in (64, 128):
+            raise ValueError(f"head_dim must be 64 or 128, got {head_dim}")
+        if quant_mode not in QUANT_MODES:
+            raise ValueError(f"quant_mode must be one of {sorted(QUANT_MODES)}, got {quant_mode!r}")
+        if tensor_layout not in LAYOUTS:
+            raise ValueError(f"tensor_layout must be one of {sorted(LAYOUTS)}")
+        self.head_dim, self.is_causal, self.quant_mode, self.tensor_layout = head_dim, bool(is_causal), quant_mode, tensor_layout
+        self.qk_bits, self.pv_bits = QUANT_MODES[quant_mode]
+        self._workspace = None
+
+    def __call__(self, q, k, v):
+        if q.shape[-1] != self.head_dim:
+            raise ValueError(f"head dim {q.shape[-1]} differs from this module's head_dim {self.head_dim}")
+        pb = _dense_problem(q, k, v, self.is_causal, self.qk_bits, self.pv_bits, self.tensor_layout)
+        nbytes = problem_ws_bytes(pb)
+        ws = self._workspace
+        if ws is None or ws.numel() < nbytes or ws.device != q.device:
+            ws = self._workspace = alloc_workspace(nbytes, q.device)
+        o = torch.empty_like(q)
+        fwd_ex(pb, q, k, v, o, ws)
+        return o
+
+    def __repr__(self):
+        return (f"SageAttention(head_dim={self.head_dim}, is_causal={self.is_causal}, "
+                f"quant_mode={self.quant_mode!r}, tensor_layout={self.tensor_layout!r})")
 
 
 def sageattn_varlen(q, k, v, cu_seqlens, is_causal: bool = False, qk_bits: int = 8, pv_bits: int = 8,

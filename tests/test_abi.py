@@ -130,6 +130,25 @@ def test_python_wrapper_rejects_unsupported(pkg):
         pkg.sageattn(q.float(), q, q)
 
 
+def test_module_front_end_modes_and_checks(pkg):
+    """SageAttention maps the quant_mode names onto (qk_bits, pv_bits) and checks its arguments
+    (host side only: nothing here touches a GPU)."""
+    import torch
+    assert pkg.QUANT_MODES == {"qk_int8_pv_fp8": (8, 8), "qk_int8_pv_fp16": (8, 16),
+                               "qk_int4_pv_fp8": (4, 8), "qk_int4_pv_fp16": (4, 16)}
+    a = pkg.SageAttention(head_dim=128, is_causal=True, quant_mode="qk_int8_pv_fp16")
+    assert (a.qk_bits, a.pv_bits, a.is_causal) == (8, 16, True)
+    for bad in (dict(head_dim=96), dict(head_dim=64, quant_mode="qk_fp8_pv_fp8"),
+                dict(head_dim=64, tensor_layout="BSHD")):
+        with pytest.raises(ValueError):
+            pkg.SageAttention(**bad)
+    q = torch.zeros(1, 2, 16, 64, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        a(q, q, q)                                # head_dim mismatch
+    with pytest.raises(ValueError):
+        pkg.SageAttention(head_dim=64)(q, q, q)   # CPU tensors
+
+
 def test_problem_descriptor_validation(pkg):
     lib = pkg._lib
     n = ctypes.c_size_t(0)

@@ -238,6 +238,25 @@ def test_k_shift_invariance_on_gpu(sa):
     assert torch.equal(o1, o2)
 
 
+@pytest.mark.parametrize("mode", ["qk_int8_pv_fp8", "qk_int4_pv_fp16"])
+def test_module_front_end_matches_sageattn(sa, mode):
+    """SageAttention(head_dim, is_causal, quant_mode) gives sageattn's output bit for bit, and a
+    second call of a smaller problem reuses its workspace."""
+    qk, pv = sa.QUANT_MODES[mode]
+    w = custom(1, 4, 2, 300, 64, True, qk, q_bias_std=1.0)
+    q, k, v = _to_dev(*make_inputs(w, seed=6))
+    attn = sa.SageAttention(head_dim=64, is_causal=True, quant_mode=mode)
+    o1 = attn(q, k, v)
+    ws = attn._workspace
+    o2 = attn(q[:, :, :200].contiguous(), k[:, :, :200].contiguous(), v[:, :, :200].contiguous())
+    ref1 = sa.sageattn(q, k, v, is_causal=True, qk_bits=qk, pv_bits=pv)
+    ref2 = sa.sageattn(q[:, :, :200].contiguous(), k[:, :, :200].contiguous(), v[:, :, :200].contiguous(),
+                       is_causal=True, qk_bits=qk, pv_bits=pv)
+    torch.cuda.synchronize()
+    assert attn._workspace is ws
+    assert torch.equal(o1, ref1) and torch.equal(o2, ref2)
+
+
 def test_accuracy_vs_exact_reported(sa):
     """O against exact fp64 attention (reported beside the pages' CosSim/RMSE figures); the
     fp16 P V mode, which skips the FP8 rounding of P and V, must be the closer of the two."""

@@ -65,7 +65,10 @@ int check_problem(const sage_problem_t* p, sage::Dims* D, std::vector<sage::Seq>
     if ((double)tot_pad * H * d > 9.0e18 || (double)tot_ds * 4.0 > 9.0e18) return SAGE_ERR_INVALID_ARG;
   }
   const long long npad = (nmax + 127) / 128 * 128;
-  if ((double)B * H * (double)(npad / 128) > 2147483647.0) return SAGE_ERR_INVALID_ARG;   // 1-D grid
+  // 1-D grids: the attention kernel (Q blocks of every head) and the statistics + Q prologue
+  // launch (256-token tiles of every kv head, then the Q blocks)
+  if ((double)B * H * (double)(npad / 128) + (double)B * Hkv * (double)((nmax + 255) / 256) > 2147483647.0)
+    return SAGE_ERR_INVALID_ARG;
   D->B = B; D->H = H; D->Hkv = Hkv; D->N = (int)nmax; D->d = d; D->causal = p->causal;
   D->qk_bits = p->qk_bits; D->pv_bits = p->pv_bits;
   D->Npad = (int)npad;

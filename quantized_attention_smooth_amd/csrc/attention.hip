@@ -26,9 +26,9 @@
 //     in a ring of two stages (three at d = 64 in the FP8 mode, where a block's arithmetic is
 //     too short to cover a tile issued only one block ahead), 16-byte chunks XOR-swizzled
 //     against LDS bank conflicts.
-//   * Workgroup ids are remapped so each XCD (own L2) works through whole heads (of every
-//     sequence of the batch); causal grids start with each sequence's longest (diagonal-most)
-//     query blocks.
+//   * Workgroup ids are remapped so each XCD (own L2) works through whole kv heads (of every
+//     sequence of the batch), with the query heads that share a kv head side by side for each
+//     Q block; causal grids start with each sequence's longest (diagonal-most) query blocks.
 //   * fp16 P V (PV16; the high-fidelity "qk_int8_pv_fp16" mode of the blog page "SageAttention：
 //     大模型量化注意力加速实践指南", section on precision control): V stays fp16 and P = e^(z - m)
 //     is rounded to fp16 into the B operand of v_mfma_f32_32x32x16_f16 (8 k-slots per lane: a
@@ -295,12 +295,16 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
     b = a.dbg_b; h = a.dbg_h; qb = a.dbg_qb;
     sq = a.g.seq(b);
   } else {
-    // head-major order: each XCD's contiguous share holds whole heads of every sequence, so
-    // varlen batches split evenly and a kv head's codes stay in one XCD's L2
-    const int total = a.B * H * a.nqb;
+    // kv-head-major order: each XCD's contiguous share holds whole kv heads of every sequence,
+    // so varlen batches split evenly and a kv head's codes stay in one XCD's L2; within it the
+    // query heads sharing the kv head come together for each Q block, so they stream the same
+    // K/V tiles at the same time
+    const int total = a.B * H * a.nqb, G = H / Hkv;
     const int L = xcd_remap(blockIdx.x, total);
-    const int hbi = L / a.nqb, qi = L % a.nqb;
-    h = hbi / a.B; b = hbi % a.B;
+    const int g = L % G, r = L / G;
+    const int qi = r % a.nqb, kbi = r / a.nqb;
+    b = kbi % a.B;
+    h = (kbi / a.B) * G + g;
     sq = a.g.seq(b);
     if (qi >= seq_blocks(sq)) return;           // beyond this sequence (varlen)
     qb = CAUSAL ? seq_blocks(sq) - 1 - qi : qi;

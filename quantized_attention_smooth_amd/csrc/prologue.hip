@@ -165,7 +165,8 @@ __global__ void init_stats(unsigned long long* ksum, unsigned int* vamax, int n,
 // inputs in fp64 within a workgroup and int64 fixed point across; bf16 inputs in the limb
 // accumulator above (LDS within a workgroup, int64 atomics across).  VSTATS = false (V kept in
 // 16-bit floats) skips V entirely.
-// grid (ceil(longest / 256), B*Hkv), 256 threads; thread = (row slot, 8-channel chunk).
+// Workgroup (bx, by) of a (ceil(longest / 256), B*Hkv) tiling, 256 threads; thread = (row slot,
+// 8-channel chunk).  Runs inside stats_and_q.
 // ---------------------------------------------------------------------------------------
 template <int D, typename T>
 struct KvStatsSmem {
@@ -456,7 +457,8 @@ __global__ __launch_bounds__(256) void kv_quant(const T* __restrict__ k, const T
 
 // ---------------------------------------------------------------------------------------
 // Q smoothing (per 128-row block mean) + per-row quantization.
-// grid (blocks of the longest sequence, B*H), 256 threads.
+// Workgroup (bx, by) of a (blocks of the longest sequence, B*H) tiling, 256 threads.  Runs
+// inside stats_and_q.
 // ---------------------------------------------------------------------------------------
 template <int D, typename T>
 struct QQuantSmem {

@@ -488,6 +488,34 @@ def test_bf16_parity(sa, name, w, pv):
     _check_o(o, o_ref, name, allow)
 
 
+@pytest.mark.parametrize("name,pv", [("llm", 8), ("dit", 16)])
+def test_bf16_full_size_sampled(sa, name, pv):
+    """bf16 inputs at a full workload size: the prologue tensors of the first and last head and
+    the outputs of their first, middle and last Q blocks against the oracle (same bars as the
+    small bf16 cases)."""
+    w = WORKLOADS[name]
+    _say(f"[case bf16 {name}] B{w.B} H{w.H} Hkv{w.Hkv} N{w.N} d{w.d} causal={w.causal} bits={w.qk_bits} pv={pv}")
+    q, k, v = make_inputs(w, seed=0, dtype="bf16")
+    qd, kd, vd = _bf16_dev(q, k, v)
+    o = sa.sageattn(qd, kd, vd, is_causal=w.causal, qk_bits=w.qk_bits, pv_bits=pv)
+    torch.cuda.synchronize()
+    nqb = -(-w.N // 128)
+    dbg = {n: t for n, t in sa.quant_debug(qd, kd, vd, w.causal, w.qk_bits, pv).items() if t is not None}
+    for b, h in sorted({(0, 0), (w.B - 1, w.H - 1)}):
+        hk = h // (w.H // w.Hkv)
+        qs, ks, vs = _head_slice(q, k, v, b, h, w.H, w.Hkv)
+        ph = osage.prologue(qs, ks, vs, w.causal, w.qk_bits, quant_pv=pv == 8)
+        sub = {n: t[b:b + 1, (hk if n in ("mu_k", "k_codes", "k_scales", "v_codes", "v_scales") else h):][:, :1].cpu().numpy()
+               for n, t in dbg.items()}
+        _check_prologue(sub, ph, 0, 0, 0, f"bf16 {name} b{b} h{h}")
+        for qb in sorted({0, nqb // 2, nqb - 1}):
+            r0, r1 = qb * 128, min(w.N, qb * 128 + 128)
+            ref, allow = _bf16_allowance(qs, ks, vs, w.causal, w.qk_bits, pv, ph, 0, 0, qb)
+            _check_o(o[b, h, r0:r1].float().cpu().numpy(), ref, f"bf16 {name} b{b} h{h} qb{qb}", allow)
+    del dbg
+    torch.cuda.empty_cache()
+
+
 def test_bf16_extreme_range_means_exact(sa):
     """bf16 keys and queries spread over 2^-133 .. 2^126, with a column whose +-4e37 entries
     cancel exactly around 2^-100: the GPU's limb accumulator must give the oracle's means, codes

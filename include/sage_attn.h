@@ -67,7 +67,7 @@ extern "C" {
 #define SAGE_ERR_HIP (-4)         /* a HIP runtime call or kernel launch failed          */
 
 /*
- * Compile-time constants of this build.  The CPU oracle takes its geometry from here.
+ * Compile-time constants of the library.  The CPU oracle takes its geometry from here.
  *   bq      : query rows per workgroup and per Q-smoothing block (mu_Q is per bq rows)
  *   bk      : keys per KV block: online-softmax block, block-local PV accumulation span,
  *             and the slice of K sharing quantization scales

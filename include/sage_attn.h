@@ -67,7 +67,9 @@ extern "C" {
 #define SAGE_ERR_HIP (-4)         /* a HIP runtime call or kernel launch failed          */
 
 /*
- * Compile-time constants of the library.  The CPU oracle takes its geometry from here.
+ * Compile-time constants of the library: the block sizes and quantization-group geometry that
+ * fix the codes and scales, readable by callers (and by tests that check a reference against
+ * them).
  *   bq      : query rows per workgroup and per Q-smoothing block (mu_Q is per bq rows)
  *   bk      : keys per KV block: online-softmax block, block-local PV accumulation span,
  *             and the slice of K sharing quantization scales

@@ -9,6 +9,7 @@ Modules:
   sage  -- the method step by step (exact means, smoothing, grouped quantization, Delta_S,
            integer QK^T, online softmax with FP8 P~ and V, two-level accumulation) and
            exact fp64 attention for accuracy reporting.
+  range_study -- the (P_r, V_r) narrowing study of an fp16 P~V accumulator (oracle only).
 """
 from . import fp8, sage  # noqa: F401
 from .sage import (DEFAULT, Geometry, Prologue, attend_block, delta_s, exact_attention,  # noqa: F401

@@ -124,6 +124,8 @@ SMALL = [
     ("n17-causal", custom(1, 1, 1, 17, 128, True, 8)),
     ("n127", custom(1, 1, 1, 127, 64, False, 4)),
     ("n129-causal", custom(1, 2, 1, 129, 128, True, 8, q_bias_std=1.0)),
+    ("d128-int4", custom(1, 2, 2, 520, 128, False, 4, q_bias_std=1.0)),
+    ("d64-causal-int8", custom(1, 2, 1, 520, 64, True, 8, q_bias_std=1.0)),
 ]
 
 
@@ -443,6 +445,8 @@ BF16_CASES = [
     ("bf16-d64-int4", custom(1, 2, 1, 333, 64, False, 4, q_bias_std=1.0), 8),
     ("bf16-d128-pv16", custom(1, 2, 2, 384, 128, False, 8), 16),
     ("bf16-d64-causal-int4-pv16", custom(1, 2, 1, 200, 64, True, 4), 16),
+    ("bf16-d128-int8", custom(1, 2, 2, 300, 128, False, 8), 8),
+    ("bf16-d64-causal-int8", custom(1, 2, 2, 300, 64, True, 8), 8),
 ]
 
 

@@ -447,6 +447,7 @@ BF16_CASES = [
     ("bf16-d64-causal-int4-pv16", custom(1, 2, 1, 200, 64, True, 4), 16),
     ("bf16-d128-int8", custom(1, 2, 2, 300, 128, False, 8), 8),
     ("bf16-d64-causal-int8", custom(1, 2, 2, 300, 64, True, 8), 8),
+    ("bf16-d128-causal-int4-pv16", custom(1, 2, 1, 300, 128, True, 4, q_bias_std=1.0), 16),
 ]
 
 

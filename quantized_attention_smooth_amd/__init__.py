@@ -151,6 +151,13 @@ def _stream(device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+def _on(device):
+    """Make the tensors' GPU current for a library call: its kernels launch on torch's current
+    stream of that GPU, and torch's default stream is the null stream, which HIP resolves
+    against the current device."""
+    return torch.cuda.device(device)
+
+
 def _ptr(t) -> ctypes.c_void_p:
     return ctypes.c_void_p(0 if t is None else t.data_ptr())
 
@@ -182,15 +189,17 @@ def fwd(q, k, v, o, workspace, is_causal: bool = False, qk_bits: int = 8, pv_bit
     B, H, Hkv, N, d = _shapes(q, k, v)
     if o.shape != q.shape or o.dtype != torch.float16 or not o.is_contiguous() or o.device != q.device:
         raise ValueError("o must be a contiguous float16 tensor shaped like q on q's device")
-    _check(_lib.sage_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, Hkv, N, d, int(is_causal), qk_bits,
-                              pv_bits, _ptr(workspace), workspace.numel(), _stream(q.device)))
+    with _on(q.device):
+        _check(_lib.sage_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, Hkv, N, d, int(is_causal), qk_bits,
+                                  pv_bits, _ptr(workspace), workspace.numel(), _stream(q.device)))
 
 
 def prologue(q, k, v, workspace, is_causal: bool = False, qk_bits: int = 8, pv_bits: int = 8) -> None:
     """sage_attn_prologue: fill `workspace` with the quantized/smoothed operands."""
     B, H, Hkv, N, d = _shapes(q, k, v)
-    _check(_lib.sage_attn_prologue(_ptr(q), _ptr(k), _ptr(v), B, H, Hkv, N, d, int(is_causal), qk_bits,
-                                   pv_bits, _ptr(workspace), workspace.numel(), _stream(q.device)))
+    with _on(q.device):
+        _check(_lib.sage_attn_prologue(_ptr(q), _ptr(k), _ptr(v), B, H, Hkv, N, d, int(is_causal), qk_bits,
+                                       pv_bits, _ptr(workspace), workspace.numel(), _stream(q.device)))
 
 
 def attend(o, workspace, shape, Hkv: int, is_causal: bool = False, qk_bits: int = 8, pv_bits: int = 8) -> None:
@@ -200,8 +209,9 @@ def attend(o, workspace, shape, Hkv: int, is_causal: bool = False, qk_bits: int 
     B, H, N, d = shape
     if tuple(o.shape) != (B, H, N, d) or o.dtype != torch.float16 or not o.is_contiguous() or not o.is_cuda:
         raise ValueError("o must be a contiguous float16 CUDA tensor of shape (B, H, N, d)")
-    _check(_lib.sage_attn_attend(_ptr(o), B, H, Hkv, N, d, int(is_causal), qk_bits, pv_bits, _ptr(workspace),
-                                 workspace.numel(), _stream(o.device)))
+    with _on(o.device):
+        _check(_lib.sage_attn_attend(_ptr(o), B, H, Hkv, N, d, int(is_causal), qk_bits, pv_bits, _ptr(workspace),
+                                     workspace.numel(), _stream(o.device)))
 
 
 def problem_ws_bytes(pb: Problem) -> int:
@@ -225,17 +235,20 @@ def _check_qkv(q, k, v, ndim: int):
 
 def fwd_ex(pb: Problem, q, k, v, o, workspace) -> None:
     """sage_attn_fwd_ex on caller-provided tensors (o and workspace are written)."""
-    _check(_lib.sage_attn_fwd_ex(pb.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(workspace), workspace.numel(),
-                                 _stream(q.device)))
+    with _on(q.device):
+        _check(_lib.sage_attn_fwd_ex(pb.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(workspace), workspace.numel(),
+                                     _stream(q.device)))
 
 
 def prologue_ex(pb: Problem, q, k, v, workspace) -> None:
-    _check(_lib.sage_attn_prologue_ex(pb.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(workspace), workspace.numel(),
-                                      _stream(q.device)))
+    with _on(q.device):
+        _check(_lib.sage_attn_prologue_ex(pb.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(workspace), workspace.numel(),
+                                          _stream(q.device)))
 
 
 def attend_ex(pb: Problem, o, workspace) -> None:
-    _check(_lib.sage_attn_attend_ex(pb.ref, _ptr(o), _ptr(workspace), workspace.numel(), _stream(o.device)))
+    with _on(o.device):
+        _check(_lib.sage_attn_attend_ex(pb.ref, _ptr(o), _ptr(workspace), workspace.numel(), _stream(o.device)))
 
 
 def sageattn(q, k, v, attn_mask=None, dropout_p: float = 0.0, is_causal: bool = False, scale=None,
@@ -368,8 +381,9 @@ def quant_debug(q, k, v, is_causal: bool = False, qk_bits: int = 8, pv_bits: int
     pb = Problem(B, H, Hkv, N, d, is_causal, qk_bits, pv_bits, "HND", q.dtype)
     ws = alloc_workspace(problem_ws_bytes(pb), dev)
     names = ("mu_k", "k_codes", "k_scales", "v_codes", "v_scales", "mu_q", "q_codes", "q_scales", "delta_s")
-    _check(_lib.sage_quant_debug_ex(pb.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(ws), ws.numel(), _stream(dev),
-                                    *[_ptr(out[n]) for n in names]))
+    with _on(dev):
+        _check(_lib.sage_quant_debug_ex(pb.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(ws), ws.numel(), _stream(dev),
+                                        *[_ptr(out[n]) for n in names]))
     return out
 
 
@@ -380,6 +394,7 @@ def qk_tile_debug(q, k, v, b: int, h: int, qb: int, kb: int, is_causal: bool = F
     cfg = get_config()
     tile = torch.empty(cfg["bq"], cfg["bk"], dtype=torch.int32, device=q.device)
     ws = alloc_workspace(workspace_bytes(B, H, Hkv, N, d, is_causal, qk_bits, pv_bits), q.device)
-    _check(_lib.sage_qk_tile_debug(_ptr(q), _ptr(k), _ptr(v), B, H, Hkv, N, d, int(is_causal), qk_bits, pv_bits,
-                                   _ptr(ws), ws.numel(), _stream(q.device), b, h, qb, kb, _ptr(tile)))
+    with _on(q.device):
+        _check(_lib.sage_qk_tile_debug(_ptr(q), _ptr(k), _ptr(v), B, H, Hkv, N, d, int(is_causal), qk_bits, pv_bits,
+                                       _ptr(ws), ws.numel(), _stream(q.device), b, h, qb, kb, _ptr(tile)))
     return tile

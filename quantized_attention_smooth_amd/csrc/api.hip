@@ -69,6 +69,9 @@ int check_problem(const sage_problem_t* p, sage::Dims* D, std::vector<sage::Seq>
   // launch (256-token tiles of every kv head, then the Q blocks)
   if ((double)B * H * (double)(npad / 128) + (double)B * Hkv * (double)((nmax + 255) / 256) > 2147483647.0)
     return SAGE_ERR_INVALID_ARG;
+  // the Delta_S launch: (32 or 64 Q blocks, 256 keys) tiles of every head
+  if ((double)B * H * (double)((npad / 128 + 31) / 32) * (double)((npad + 255) / 256) > 2147483647.0)
+    return SAGE_ERR_INVALID_ARG;
   D->B = B; D->H = H; D->Hkv = Hkv; D->N = (int)nmax; D->d = d; D->causal = p->causal;
   D->qk_bits = p->qk_bits; D->pv_bits = p->pv_bits;
   D->Npad = (int)npad;

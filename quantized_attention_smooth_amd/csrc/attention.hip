@@ -151,11 +151,6 @@ constexpr int kTileInstrs = BK * D / 16 / 64 / WAVES;
 // Loads past a resource's end return zeros (range-checked).
 // The buffer builtins exist only for the GPU target: their code is compiled in the device pass
 // (in the host pass, kernels using them otherwise lost their launch stubs without a diagnostic).
-#if defined(__HIP_DEVICE_COMPILE__)
-__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-#endif
 
 template <int D, bool PV16>
 struct TileLoader {
@@ -273,12 +268,6 @@ __device__ inline void qk_tiles(const Smem<D, PV16>& sm, int st, const v4i (&qre
       sacc[t] = acc;
     }
   }
-}
-
-__device__ inline int xcd_remap(int bid, int total) {
-  const int q = total / 8, r = total % 8;
-  const int x = bid % 8, k = bid / 8;
-  return x * q + min(x, r) + k;
 }
 
 template <int D, bool CAUSAL, bool DUMP, bool QK4, bool PV16, bool BF>

@@ -601,255 +601,215 @@ __global__ __launch_bounds__(256) void stats_and_q(const T* __restrict__ k, cons
 // are accumulated, smallest first (x3y1 + x2y2 + x1y3 + x2y1 + x1y2 + x1y1); the dropped
 // terms are below 2^-24 of it.  The bf16 MFMA accumulates in fp32 (unlike the FP8 one).
 //
-// One workgroup per (KV head, 128-key block): it reads the block's fp16 keys once, forms
-// gamma_K = RN32(K - mu_K), splits it and keeps the three parts in LDS in the MFMA operand
-// layout, then sweeps the Q blocks of every query head that shares the KV head (the mu_Q parts
-// come split from the Q prologue).  Causal: only Q blocks qb >= kb see these keys.
-// 256 threads: wave w owns keys 64 (w & 1) .. +63 of the block (two 32x32 accumulators) and
-// every other 32-Q-block tile (parity w >> 1); the next tile's mu_Q parts are loaded while the
-// current tile is stored.
+// One workgroup per (64 Q blocks of one query head, 256 keys), 256 threads.  The 64 Q blocks'
+// mu_Q parts (split by the Q prologue) are copied to LDS once and read there by all four
+// waves; wave w owns keys 64 w .. 64 w + 63 of the tile, loads their rows up front (one
+// memory round trip), forms gamma_K = RN32(K - mu_K) and its split one 16-channel k-step at a
+// time, and accumulates 2 x 2 MFMA tiles of 32 Q blocks x 32 keys.  Workgroup ids run over
+// (Q-block tile, query head of the group, key tile, sequence, kv head), fastest first, split into
+// one contiguous share per XCD (own L2): the workgroups that read one key tile are adjacent
+// and on one XCD, so the keys come from HBM about once however many Q blocks and query heads
+// use them, and each XCD's share holds whole kv heads of every sequence (even varlen shares).
+// Causal: Q block qb stores keys j < (qb + 1) * 128; tiles above the diagonal are skipped.
 // ---------------------------------------------------------------------------------------
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-template <int D>
+constexpr int DS_KT = 256;    // keys per workgroup: 64 per wave, two 32-column MFMA tiles
+
+// QT Q blocks per workgroup (NU = QT / 32 MFMA row tiles)
+template <int D, int QT>
 struct DsSmem {
-  __attribute__((aligned(16))) uint16_t g[3][D / 16][BK][16];   // [part][k-step][key][16 ch], swizzled halves
+  // one Q block's three bf16 parts of D channels, plus 16 bytes: the 32 lanes of an operand
+  // read (32 consecutive Q blocks, one 16-byte chunk each) then fall on distinct banks
+  static constexpr int ROW = 3 * D * 2 + 16;
+  __attribute__((aligned(16))) uint8_t a[QT * ROW];
+  __attribute__((aligned(16))) float muk[D];
 };
-
-// 16-byte half (8 channels) of a key's k-step row, XOR-swizzled by key bit 3 against bank conflicts
-__device__ inline int ds_half(int key, int hl) { return hl ^ ((key >> 3) & 1); }
 
 struct Split3 {
   bf16x8 p[3];
 };
 
+// x = x1 + x2 + x3 exactly, in pairs: the packed fp32 -> bf16 convert rounds two elements to
+// nearest even at once, and a bf16 pair widens back to fp32 by a shift (low) and a mask (high).
+// Each residual x - x1 and x - x1 - x2 is exact in fp32 (the rounding error of a narrower format).
+__device__ inline uint32_t bf16_pair(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
+}
+__device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
 __device__ inline Split3 split3(const float (&x)[8]) {
+  uint32_t w[3][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float a = x[2 * i], b = x[2 * i + 1];
+    const uint32_t w1 = bf16_pair(a, b);
+    const float ra = a - bf16_lo(w1), rb = b - bf16_hi(w1);
+    const uint32_t w2 = bf16_pair(ra, rb);
+    w[0][i] = w1;
+    w[1][i] = w2;
+    w[2][i] = bf16_pair(ra - bf16_lo(w2), rb - bf16_hi(w2));   // at most 8 significant bits remain: exact
+  }
   Split3 s;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const __bf16 b1 = (__bf16)x[e];
-    const float r1 = x[e] - (float)b1;       // exact: b1 is x rounded to 8 significant bits
-    const __bf16 b2 = (__bf16)r1;
-    const float r2 = r1 - (float)b2;         // exact
-    s.p[0][e] = b1;
-    s.p[1][e] = b2;
-    s.p[2][e] = (__bf16)r2;                  // r2 has at most 8 significant bits left: exact
-  }
+  for (int p = 0; p < 3; ++p) s.p[p] = __builtin_bit_cast(bf16x8, (uint4){w[p][0], w[p][1], w[p][2], w[p][3]});
   return s;
 }
 
-// Q-tile form, for few Q blocks per key: grid (Npad/256 key tiles, ceil(nqb/32) Q-block tiles of
-// the longest sequence, B*H), 256 threads; each wave owns 32 Q blocks x 64 keys (two 32x32 MFMA tiles) and splits
-// both operands itself.  Causal rows stop at key (qb + 1) * 128.
-template <int D, bool CAUSAL, typename T>
-__global__ __launch_bounds__(256) void delta_s_qtile(const T* __restrict__ k, const float* __restrict__ muk,
-                                               const float* __restrict__ muq, float* __restrict__ ds,
-                                               Geo g, float k2) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, r = lane & 31, hl = lane >> 5;
-  const int H = g.H, Hkv = g.Hkv;
-  const int bh = blockIdx.z, b = bh / H, h = bh % H, hk = h / (H / Hkv);
-  const size_t bkv = (size_t)b * Hkv + hk;
+// Store v at byte offset off of [base, base + bytes) through a buffer resource: a store at or past
+// the end is dropped by the hardware's range check, so masked elements cost no branch.
+__device__ inline void store_or_drop(float* base, uint32_t bytes, uint32_t off, float v) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), make_rsrc(base, bytes), (int)off, 0, 0);
+#endif
+}
+constexpr uint32_t kDropOffset = 0xFFFFFF00u;   // past any resource here (all are below 2^31 bytes)
+
+// grid (nqt * H * nkt * B), nqt = Q-block tiles and nkt = key tiles of the longest sequence
+template <int D, bool CAUSAL, typename T, int NU>
+__global__ __launch_bounds__(256) void delta_s(const T* __restrict__ k, const float* __restrict__ muk,
+                                               const uint16_t* __restrict__ muqs, float* __restrict__ ds,
+                                               Geo g, int B, int nqt, int nkt, float k2) {
+  constexpr int QT = 32 * NU;                          // Q blocks of the tile
+  __shared__ DsSmem<D, QT> sm;
+  constexpr int KS = D / 16;                            // 16-channel MFMA k-steps
+  constexpr int ROW = DsSmem<D, QT>::ROW;
+  const int tid = threadIdx.x, lane = tid & 63, r = lane & 31, hl = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int H = g.H, Hkv = g.Hkv, G = H / Hkv;
+  const int L = xcd_remap(blockIdx.x, nqt * H * nkt * B);
+  int rest = L;
+  const int qt = rest % nqt; rest /= nqt;
+  const int gq = rest % G; rest /= G;
+  const int kt = rest % nkt; rest /= nkt;
+  const int b = rest % B, hk = rest / B;
+  const int h = hk * G + gq;
   const Seq sq = g.seq(b);
   const int N = sq.n, nqb = seq_blocks(sq), Npad = nqb * BQ;
-  const int q0 = blockIdx.y * 32;                      // first Q block of this tile
-  const int j0 = blockIdx.x * 256 + w * 64;            // first key of this wave
-  if (q0 >= nqb || j0 >= Npad) return;                 // beyond this sequence
-  const int qlast = min(q0 + 31, nqb - 1);
-  if (CAUSAL && j0 >= (qlast + 1) * BQ) return;        // every row of the tile stops earlier
-  const int qb = q0 + r;                               // A row (operand) of this lane
-  const bool qvalid = qb < nqb;
-  const long long ts = g.st.kt;
-  const T* kb = k + b * g.st.kb + (long long)sq.tok0 * ts + hk * g.st.kh;
-  const float* muqh = muq + blocks_off(sq, H, h) * D;
-  f32x16 acc[2] = {};
-#pragma unroll 2
-  for (int ks = 0; ks < D / 16; ++ks) {
-    const int c0 = 16 * ks + 8 * hl;
-    float xa[8];
-    {
-      float4 m0 = make_float4(0.f, 0.f, 0.f, 0.f), m1 = m0;
-      if (qvalid) {
-        const float* src = muqh + (size_t)qb * D + c0;
-        m0 = *reinterpret_cast<const float4*>(src);
-        m1 = *reinterpret_cast<const float4*>(src + 4);
-      }
-      xa[0] = m0.x; xa[1] = m0.y; xa[2] = m0.z; xa[3] = m0.w;
-      xa[4] = m1.x; xa[5] = m1.y; xa[6] = m1.z; xa[7] = m1.w;
-    }
-    const Split3 A = split3(xa);
-    const float4 mk0 = *reinterpret_cast<const float4*>(muk + bkv * D + c0);
-    const float4 mk1 = *reinterpret_cast<const float4*>(muk + bkv * D + c0 + 4);
-    const float mkv[8] = {mk0.x, mk0.y, mk0.z, mk0.w, mk1.x, mk1.y, mk1.z, mk1.w};
+  const int q0 = qt * QT, k0 = kt * DS_KT;
+  if (q0 >= nqb || k0 >= Npad) return;                 // beyond this sequence
+  const int qlast = min(q0 + QT, nqb) - 1;
+  if (CAUSAL && k0 >= (qlast + 1) * BQ) return;        // every row of the tile stops earlier
+
+  // the tile's Q blocks' mu_Q parts (rows past the sequence repeat its last block and are never
+  // stored) and mu_K -> LDS.  Their loads go out first, so the LDS fill waits for them alone
+  // while this wave's key rows are still arriving.
+  constexpr int CPQ = 3 * D / 8;                       // 16-byte chunks per Q block
+  const uint16_t* aq = muqs + blocks_off(sq, H, h) * 3 * D;
+  uint4 av[QT * CPQ / 256];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int j = j0 + 32 * t + r;                   // B column (key) of this lane
-      float xb[8];
-      if (j < N) {
-        const auto kk = load8(kb + j * ts + c0);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) xb[e] = kk.f(e) - mkv[e];   // gamma_K, RN32
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) xb[e] = 0.f;
-      }
-      const Split3 Bv = split3(xb);
-      f32x16 c = acc[t];
-      c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A.p[2], Bv.p[0], c, 0, 0, 0);
-      c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A.p[1], Bv.p[1], c, 0, 0, 0);
-      c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A.p[0], Bv.p[2], c, 0, 0, 0);
-      c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A.p[1], Bv.p[0], c, 0, 0, 0);
-      c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A.p[0], Bv.p[1], c, 0, 0, 0);
-      c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A.p[0], Bv.p[0], c, 0, 0, 0);
-      acc[t] = c;
-    }
+  for (int it = 0; it < QT * CPQ / 256; ++it) {
+    const int c = it * 256 + tid;
+    av[it] = *reinterpret_cast<const uint4*>(aq + (size_t)min(q0 + c / CPQ, nqb - 1) * 3 * D + (c % CPQ) * 8);
   }
-  // lane holds rows q0 + 8a + 4hl + e (e < 4) of key column j0 + 32t + r
-  float* dsh = ds + ds_off(sq, CAUSAL, h);
+  float4 mk = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (tid < D / 4) mk = *reinterpret_cast<const float4*>(muk + ((size_t)b * Hkv + hk) * D + 4 * tid);
+  __builtin_amdgcn_sched_barrier(0);                   // keep these loads ahead of the key rows
+
+  // this wave's key rows, all k-steps (rows past the sequence read its last row and count as
+  // zero)
+  const long long ts = g.st.kt;
+  const T* kbase = k + b * g.st.kb + (long long)sq.tok0 * ts + hk * g.st.kh;
+  const int j0 = k0 + 64 * w;                          // this wave's first key
+  In8<T> kr[2][KS];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int j = j0 + 32 * t + r;
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      kr[t][ks] = load8(kbase + (long long)min(j0 + 32 * t + r, N - 1) * ts + 16 * ks + 8 * hl);
+
+#pragma unroll
+  for (int it = 0; it < QT * CPQ / 256; ++it) {
+    const int c = it * 256 + tid;
+    *reinterpret_cast<uint4*>(sm.a + (c / CPQ) * ROW + (c % CPQ) * 16) = av[it];
+  }
+  if (tid < D / 4) *reinterpret_cast<float4*>(&sm.muk[4 * tid]) = mk;
+  __syncthreads();
+  if (j0 >= Npad || (CAUSAL && j0 >= (qlast + 1) * BQ)) return;   // no key of this wave is stored
+
+  // A tile u (Q blocks q0 + 32 u ..) is live if it has a Q block that stores key j0.  Both tiles
+  // are multiplied either way (a branch per tile would split the MFMA schedule); a dead one is
+  // just not stored.
+  bool live[NU];
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const int qa = q0 + 32 * u;
+    live[u] = qa < nqb && (!CAUSAL || j0 < (min(qa + 31, nqb - 1) + 1) * BQ);
+  }
+
+  // the 2 x 2 tile products, one k-step at a time; TAIL: the wave holds keys j >= N, which
+  // count as zero (only the last wave of a sequence takes that path)
+  f32x16 acc[NU][2] = {};
+  auto gemm = [&](auto tail_tag) {
+    constexpr bool TAIL = decltype(tail_tag)::value;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int c0 = 16 * ks + 8 * hl;                 // this lane's 8 channels of the k-step
+      const float4 m0 = *reinterpret_cast<const float4*>(&sm.muk[c0]);
+      const float4 m1 = *reinterpret_cast<const float4*>(&sm.muk[c0 + 4]);
+      const float mm[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+      bf16x8 A[NU][3];
+#pragma unroll
+      for (int u = 0; u < NU; ++u)
+#pragma unroll
+        for (int p = 0; p < 3; ++p)
+          A[u][p] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const s16x8*>(sm.a + (32 * u + r) * ROW + (p * D + c0) * 2));
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        float xb[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = kr[t][ks].f(e) - mm[e];      // gamma_K, RN32
+          xb[e] = TAIL && j0 + 32 * t + r >= N ? 0.f : x;
+        }
+        const Split3 Bv = split3(xb);
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+          f32x16 c = acc[u][t];
+          c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[u][2], Bv.p[0], c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[u][1], Bv.p[1], c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[u][0], Bv.p[2], c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[u][1], Bv.p[0], c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[u][0], Bv.p[1], c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[u][0], Bv.p[0], c, 0, 0, 0);
+          acc[u][t] = c;
+        }
+      }
+    }
+  };
+  if (j0 + 64 > N) gemm(std::true_type{});
+  else gemm(std::false_type{});
+
+  // lane holds Q blocks q0 + 32 u + 8 a + 4 hl + e (a, e < 4) of key column j0 + 32 t + r.  The
+  // stores go through one buffer resource over rows q0 .. qlast of this head: fewer than 2^31
+  // bytes (at most 64 rows of at most 2^23 keys), so 32-bit offsets reach every element and
+  // an element that is not stored (Q block past the sequence, key past a causal row) takes
+  // an offset past the end.
+  const size_t row0 = ds_row_offset(CAUSAL, q0, Npad);
+  float* const dsr = ds + ds_off(sq, CAUSAL, h) + row0;
+  const uint32_t span = (uint32_t)((ds_row_offset(CAUSAL, qlast + 1, Npad) - row0) * 4);
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    if (!live[u]) continue;
 #pragma unroll
     for (int a4 = 0; a4 < 4; ++a4)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int q = q0 + 8 * a4 + 4 * hl + e;
-        if (q < nqb && j < ds_row_len(CAUSAL, q, Npad)) dsh[ds_row_offset(CAUSAL, q, Npad) + j] = acc[t][4 * a4 + e] * k2;
-      }
-  }
-}
-
-// K-block form, for many Q blocks per key (grouped query heads, long sequences): see above.
-template <int D>
-struct AParts {                                  // one lane's mu_Q parts for a 32-Q-block tile
-  bf16x8 a[D / 16][3];
-};
-
-template <int D>
-__device__ inline void load_aparts(AParts<D>& A, const uint16_t* __restrict__ head, int nqb, int qa, int hl) {
-  const uint16_t* ap = head + (size_t)min(qa, nqb - 1) * 3 * D;   // head: this query head's parts
+        const int qb = q0 + 32 * u + 8 * a4 + 4 * hl + e;
+        // row qb's first element relative to row q0's (causal rows hold (qb + 1) * 128 keys)
+        const uint32_t rel = CAUSAL ? 64u * (uint32_t)((qb - q0) * (qb + q0 + 1)) : (uint32_t)(qb - q0) * (uint32_t)Npad;
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks)
-#pragma unroll
-    for (int p = 0; p < 3; ++p) {
-      const s16x8 av = qa < nqb ? *reinterpret_cast<const s16x8*>(ap + p * D + 16 * ks + 8 * hl) : (s16x8){};
-      A.a[ks][p] = __builtin_bit_cast(bf16x8, av);
-    }
-}
-
-template <int D, bool CAUSAL, typename T>
-__global__ __launch_bounds__(256) void delta_s_kblock(const T* __restrict__ k, const float* __restrict__ muk,
-                                               const uint16_t* __restrict__ muqs, float* __restrict__ ds,
-                                               Geo g, float k2) {
-  __shared__ DsSmem<D> sm;
-  constexpr int KS = D / 16;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 31, hl = lane >> 5;
-  const int H = g.H, Hkv = g.Hkv;
-  const int kb = blockIdx.x;
-  const int bkv = blockIdx.y, b = bkv / Hkv, hk = bkv % Hkv, G = H / Hkv;
-  const Seq sq = g.seq(b);
-  const int N = sq.n, nqb = seq_blocks(sq), Npad = nqb * BQ;
-  if (kb >= nqb) return;                                      // beyond this sequence
-  const long long ts = g.st.kt;
-  const T* kbase = k + b * g.st.kb + (long long)sq.tok0 * ts + hk * g.st.kh;
-  auto muq_head = [&](int hq) { return muqs + blocks_off(sq, H, hk * G + hq) * 3 * D; };
-
-  // gamma_K parts of the block's 128 keys -> LDS
-  constexpr int CH = D / 8;                                   // 8-channel chunks per key
-  In8<T> kr[BK * CH / 256];                                   // loads first (clamped, masked later)
-#pragma unroll
-  for (int it = 0; it < BK * CH / 256; ++it) {
-    const int idx = it * 256 + tid;
-    kr[it] = load8(kbase + min(kb * BK + idx / CH, N - 1) * ts + (idx % CH) * 8);
-  }
-#pragma unroll
-  for (int it = 0; it < BK * CH / 256; ++it) {
-    const int idx = it * 256 + tid, key = idx / CH, c8 = idx % CH;
-    const int j = kb * BK + key;
-    float x[8];
-    {
-      const float4 m0 = *reinterpret_cast<const float4*>(muk + (size_t)bkv * D + c8 * 8);
-      const float4 m1 = *reinterpret_cast<const float4*>(muk + (size_t)bkv * D + c8 * 8 + 4);
-      const float mm[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = j < N ? kr[it].f(e) - mm[e] : 0.f;   // gamma_K, RN32
-    }
-    union { __bf16 b[8]; uint4 u; } p0, p1, p2;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const __bf16 b1 = (__bf16)x[e];
-      const float r1 = x[e] - (float)b1;       // exact: b1 is x rounded to 8 significant bits
-      const __bf16 b2 = (__bf16)r1;
-      p0.b[e] = b1;
-      p1.b[e] = b2;
-      p2.b[e] = (__bf16)(r1 - (float)b2);      // at most 8 significant bits remain: exact
-    }
-    const int ks = c8 >> 1, h = ds_half(key, c8 & 1);
-    *reinterpret_cast<uint4*>(&sm.g[0][ks][key][8 * h]) = p0.u;
-    *reinterpret_cast<uint4*>(&sm.g[1][ks][key][8 * h]) = p1.u;
-    *reinterpret_cast<uint4*>(&sm.g[2][ks][key][8 * h]) = p2.u;
-  }
-  __syncthreads();
-
-  // wave w: keys 64 (w & 1) .. +63 (two 32-key accumulators), Q tiles of parity w >> 1
-  const int qlo = CAUSAL ? kb & ~31 : 0;                     // first 32-aligned Q tile that sees the keys
-  const int ntile = (nqb - qlo + 31) / 32;
-  const int my0 = w >> 1;                                    // this wave's tiles: my0, my0 + 2, ...
-  const int total = G * ((ntile - my0 + 1) / 2);             // (q head, tile) pairs of this wave
-  auto pair = [&](int n, int& hq, int& q0) {
-    const int per = (ntile - my0 + 1) / 2;
-    hq = n / per;
-    q0 = qlo + 32 * (my0 + 2 * (n % per));
-  };
-  AParts<D> A;
-  if (total > 0) {
-    int hq, q0;
-    pair(0, hq, q0);
-    load_aparts<D>(A, muq_head(hq), nqb, q0 + r, hl);
-  }
-  for (int n = 0; n < total; ++n) {
-    int hq, q0;
-    pair(n, hq, q0);
-    f32x16 acc[2] = {};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int key = 64 * (w & 1) + 32 * t + r;
-        bf16x8 Bv[3];
-#pragma unroll
-        for (int p = 0; p < 3; ++p)
-          Bv[p] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const s16x8*>(&sm.g[p][ks][key][8 * ds_half(key, hl)]));
-        f32x16 c = acc[t];
-        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A.a[ks][2], Bv[0], c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A.a[ks][1], Bv[1], c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A.a[ks][0], Bv[2], c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A.a[ks][1], Bv[0], c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A.a[ks][0], Bv[1], c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A.a[ks][0], Bv[0], c, 0, 0, 0);
-        acc[t] = c;
-      }
-    }
-    // next pair's mu_Q parts load while this pair's results are stored
-    if (n + 1 < total) {
-      int hq2, q02;
-      pair(n + 1, hq2, q02);
-      load_aparts<D>(A, muq_head(hq2), nqb, q02 + r, hl);
-    }
-    float* dsh = ds + ds_off(sq, CAUSAL, hk * G + hq);
-    // lane holds Q blocks q0 + 8a + 4hl + e (e < 4) of key column j
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int j = kb * BK + 64 * (w & 1) + 32 * t + r;
-#pragma unroll
-      for (int a4 = 0; a4 < 4; ++a4)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int qb = q0 + 8 * a4 + 4 * hl + e;
-          if (qb < nqb && (!CAUSAL || qb >= kb)) dsh[ds_row_offset(CAUSAL, qb, Npad) + j] = acc[t][4 * a4 + e] * k2;
+        for (int t = 0; t < 2; ++t) {
+          const int j = j0 + 32 * t + r;
+          const bool ok = qb < nqb && (!CAUSAL || (j >> 7) <= qb);
+          store_or_drop(dsr, span, ok ? (rel + (uint32_t)j) * 4u : kDropOffset, acc[u][t][4 * a4 + e] * k2);
         }
-    }
+      }
   }
 }
 
@@ -963,20 +923,19 @@ hipError_t launch_prologue_d(const Dims& Dm, const Ptrs& P, hipStream_t s) {
     else kvq(std::false_type{}, std::false_type{});
   }
   const float k2 = (float)(1.4426950408889634 / sqrt((double)D));
-  // the K-block form pays off when each key block serves many Q blocks
-  if ((size_t)(Dm.H / Dm.Hkv) * Dm.nqb >= 1024) {
-    const dim3 gr(Dm.nkb, Dm.B * Dm.Hkv);
+  // 64 Q blocks per workgroup when sequences are long (the key split is shared by more MFMAs),
+  // 32 when they are short on average (varlen prefill batches: less work on rows past the end)
+  auto dsl = [&](auto nu) {
+    constexpr int NU = decltype(nu)::value;
+    const int nqt = (Dm.nqb + 32 * NU - 1) / (32 * NU), nkt = (Dm.Npad + DS_KT - 1) / DS_KT;
+    const int gds = nqt * Dm.H * nkt * Dm.B;
     if (Dm.causal)
-      delta_s_kblock<D, true, T><<<gr, 256, 0, s>>>(k, P.muk, P.muqs, P.ds, g, k2);
+      delta_s<D, true, T, NU><<<gds, 256, 0, s>>>(k, P.muk, P.muqs, P.ds, g, Dm.B, nqt, nkt, k2);
     else
-      delta_s_kblock<D, false, T><<<gr, 256, 0, s>>>(k, P.muk, P.muqs, P.ds, g, k2);
-  } else {
-    const dim3 gr((Dm.Npad + 255) / 256, (Dm.nqb + 31) / 32, Dm.B * Dm.H);
-    if (Dm.causal)
-      delta_s_qtile<D, true, T><<<gr, 256, 0, s>>>(k, P.muk, P.muq, P.ds, g, k2);
-    else
-      delta_s_qtile<D, false, T><<<gr, 256, 0, s>>>(k, P.muk, P.muq, P.ds, g, k2);
-  }
+      delta_s<D, false, T, NU><<<gds, 256, 0, s>>>(k, P.muk, P.muqs, P.ds, g, Dm.B, nqt, nkt, k2);
+  };
+  if (Dm.tot_pad >= 48LL * BQ * Dm.B) dsl(std::integral_constant<int, 2>{});
+  else dsl(std::integral_constant<int, 1>{});
   return hipGetLastError();
 }
 

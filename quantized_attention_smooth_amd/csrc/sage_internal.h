@@ -198,6 +198,22 @@ inline Ptrs carve(void* ws, const Layout& L, const void* q, const void* k, const
   return p;
 }
 
+// Workgroup ids are dealt to the 8 XCDs (each with its own L2) round-robin: id i runs on XCD
+// i % 8.  xcd_remap(i, total) renumbers them so that XCD x works through one contiguous share
+// of [0, total), shares differing in size by at most one.
+__device__ inline int xcd_remap(int bid, int total) {
+  const int q = total / 8, r = total % 8;
+  const int x = bid % 8, k = bid / 8;
+  return x * q + min(x, r) + k;
+}
+// A raw buffer resource over [base, base + bytes): loads past the end return zero and stores
+// past it are dropped.  Buffer builtins exist only for the GPU target, so every use sits in
+// device-pass code (#if defined(__HIP_DEVICE_COMPILE__)).
+#if defined(__HIP_DEVICE_COMPILE__)
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+#endif
 // ---- launchers (return the hipError_t of the launch) ----
 // varlen: copy the host-built sequence table into the workspace (kernel arguments, no host
 // buffer outlives the call)

@@ -342,8 +342,8 @@ def test_int4_extreme_codes_exact(sa):
 
 @pytest.mark.parametrize("causal", [True, False])
 def test_many_q_blocks_per_key_block(sa, causal):
-    """64 query heads on one KV head: each key block serves 64 x 16 Q blocks, so Delta_S takes the
-    key-block form of its GEMM.  Sampled heads: full prologue tensors and every output block."""
+    """64 query heads on one KV head: each key block serves 64 x 16 Q blocks, and the Delta_S tiles
+    of all 64 heads read one key tile.  Sampled heads: full prologue tensors and every output block."""
     w = custom(1, 64, 1, 2048, 64, causal, 8, q_bias_std=1.0)
     _say(f"[case many-q-blocks causal={causal}] B{w.B} H{w.H} Hkv{w.Hkv} N{w.N} d{w.d}")
     q, k, v = make_inputs(w, seed=11)
@@ -435,6 +435,31 @@ def test_varlen_full_size_sampled(sa):
                 r0, r1 = qb * 128, min(ph.N, qb * 128 + 128)
                 ref = osage.attend_block(ph, 0, 0, qb)
                 _check_o(o[a + r0:a + r1, h].cpu().numpy(), ref, f"varlen seq {s} h{h} qb{qb}", _slack(ph, 0, 0, qb))
+
+
+def test_varlen_long_and_short_sequences(sa):
+    """Mostly long sequences (the Delta_S launch takes 64-Q-block tiles) next to a short one:
+    every sequence bit-identical to its fixed-length call (whose launch may tile differently),
+    sampled Q blocks of both heads against the oracle."""
+    from workloads import VarlenWorkload, make_varlen_inputs
+    w = VarlenWorkload("varlen-long", (13000, 5000, 200), 2, 1, 64, True, 8, q_bias_std=1.0)
+    _say(f"[case varlen-long] lens {w.lens} H{w.H} Hkv{w.Hkv} d{w.d} causal={w.causal}")
+    q, k, v = make_varlen_inputs(w, seed=9)
+    cu = w.cu_seqlens
+    qd, kd, vd = _to_dev(q, k, v)
+    o = sa.sageattn_varlen(qd, kd, vd, cu, is_causal=True, qk_bits=8)
+    torch.cuda.synchronize()
+    for s in range(w.B):
+        a, b = cu[s], cu[s + 1]
+        fixed = sa.sageattn(*(x[a:b].transpose(0, 1).contiguous()[None] for x in (qd, kd, vd)), is_causal=True, qk_bits=8)
+        assert torch.equal(fixed[0].transpose(0, 1), o[a:b]), f"seq {s}: varlen != fixed-length"
+        for h in range(w.H):
+            sl = lambda x, hh: np.ascontiguousarray(x[a:b, hh:hh + 1].transpose(1, 0, 2))[None]
+            ph = osage.prologue(sl(q, h), sl(k, 0), sl(v, 0), True, 8)
+            for qb in sorted({0, ph.nqb // 2, ph.nqb - 1}):
+                r0, r1 = qb * 128, min(ph.N, qb * 128 + 128)
+                _check_o(o[a + r0:a + r1, h].cpu().numpy(), osage.attend_block(ph, 0, 0, qb),
+                         f"varlen-long seq {s} h{h} qb{qb}", _slack(ph, 0, 0, qb))
 
 
 # ------------------------------------------------------------------------------------------

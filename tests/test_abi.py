@@ -78,6 +78,7 @@ def test_workspace_bytes(pkg):
     ((1, 2, 2, 256, 64, 0, 8, 4), -2),    # pv_bits
     ((1, 2, 2, 256, 64, 0, 8, 32), -2),   # pv_bits
     ((1, 2, 2, (1 << 23) + 1, 64, 0, 8, 8), -2),   # N beyond the exact-sum bound
+    ((1, 64, 64, 1 << 23, 64, 0, 8, 8), -1),      # Delta_S launch beyond 2^31 - 1 workgroups
 ])
 def test_validation_errors(pkg, args, status):
     lib = pkg._lib

@@ -6,8 +6,9 @@
 // pith.science verdict on arXiv 2505.21136, key "key_machinery": per-channel V scale
 // max|V| / V_r.
 //
-// All kernels are HBM-streaming codec work: each reads its fp16 input once (K and V twice:
-// statistics, then quantization) and writes 1-byte codes plus a few scales.
+// The codec kernels stream HBM: each reads its fp16 input once (K and V twice: statistics, then
+// quantization) and writes 1-byte codes plus a few scales.  Delta_S (the Q-smoothing bias,
+// mu_Q . gamma_K per Q block and key) reads K a third time and writes 4 bytes per (Q block, key).
 //
 // Bit-exactness: the channel means are exact sums.  Every fp16 value is an integer multiple of
 // 2^-24 below 2^16, so a sum of up to 256 of them is exact in fp64 (below 2^24, 48 bits of

@@ -389,7 +389,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
     const float kd = half ? kd1 : kd0;
     const float cmul = qd * kd * a.k2;
     float z[BK / 32][16];
-    float mloc = -INFINITY;
+    // the row max in two chains of three-input maxima (v_max3_f32: two new elements per
+    // instruction); a max is exact in any order
+    float mloc = -INFINITY, mloc2 = -INFINITY;
 #pragma unroll
     for (int t = 0; t < BK / 32; ++t) {
 #pragma unroll
@@ -409,11 +411,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
           }
           z[t][4 * qq + r] = x;
         }
-        mloc = fmaxf(mloc, fmaxf(fmaxf(z[t][4 * qq], z[t][4 * qq + 1]), fmaxf(z[t][4 * qq + 2], z[t][4 * qq + 3])));
+        mloc = fmaxf(fmaxf(mloc, z[t][4 * qq]), z[t][4 * qq + 1]);
+        mloc2 = fmaxf(fmaxf(mloc2, z[t][4 * qq + 2]), z[t][4 * qq + 3]);
       }
     }
     // row max across the two lane halves holding the same query
-    mloc = xhalf_max(mloc);
+    mloc = xhalf_max(fmaxf(mloc, mloc2));
     const float m_new = fmaxf(m_run, mloc);
     // a row has a finite max from its first block on (key 0 is never masked); the guards only
     // keep -inf - -inf out of the arithmetic

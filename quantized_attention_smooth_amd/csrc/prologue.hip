@@ -602,16 +602,17 @@ __global__ __launch_bounds__(256) void stats_and_q(const T* __restrict__ k, cons
 // are accumulated, smallest first (x3y1 + x2y2 + x1y3 + x2y1 + x1y2 + x1y1); the dropped
 // terms are below 2^-24 of it.  The bf16 MFMA accumulates in fp32 (unlike the FP8 one).
 //
-// One workgroup per (64 Q blocks of one query head, 256 keys), 256 threads.  The 64 Q blocks'
-// mu_Q parts (split by the Q prologue) are copied to LDS once and read there by all four
-// waves; wave w owns keys 64 w .. 64 w + 63 of the tile, loads their rows up front (one
-// memory round trip), forms gamma_K = RN32(K - mu_K) and its split one 16-channel k-step at a
-// time, and accumulates 2 x 2 MFMA tiles of 32 Q blocks x 32 keys.  Workgroup ids run over
+// One workgroup per (32 NU Q blocks of one query head, 256 keys), 256 threads, NU = 1 or 2.
+// The Q blocks' mu_Q parts (split by the Q prologue) are copied to LDS once and read there by
+// all four waves; wave w owns keys 64 w .. 64 w + 63 of the tile, loads their rows up front
+// (one memory round trip), forms gamma_K = RN32(K - mu_K) and its split one 16-channel k-step
+// at a time, and accumulates NU x 2 MFMA tiles of 32 Q blocks x 32 keys.  Workgroup ids run over
 // (Q-block tile, query head of the group, key tile, sequence, kv head), fastest first, split into
 // one contiguous share per XCD (own L2): the workgroups that read one key tile are adjacent
 // and on one XCD, so the keys come from HBM about once however many Q blocks and query heads
 // use them, and each XCD's share holds whole kv heads of every sequence (even varlen shares).
-// Causal: Q block qb stores keys j < (qb + 1) * 128; tiles above the diagonal are skipped.
+// Causal: Q block qb stores keys j < (qb + 1) * 128; workgroups and waves whose keys no row of
+// theirs stores exit early, and a 32-row tile with no such row is multiplied but not stored.
 // ---------------------------------------------------------------------------------------
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));

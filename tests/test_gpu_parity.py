@@ -358,6 +358,27 @@ def test_many_q_blocks_per_key_block(sa, causal):
         _check_o(o[0, h], ref, f"many-q-blocks h{h}", slack)
 
 
+@pytest.mark.parametrize("causal", [True, False])
+def test_delta_s_64_block_tiles_ragged_batch(sa, causal):
+    """Sequences averaging over 48 Q blocks take the 64-Q-block Delta_S tiles: a ragged length
+    (not a multiple of the 256-key tile), two sequences, two query heads on one kv head.  Every
+    prologue tensor of every head, and sampled output blocks, against the oracle."""
+    w = custom(2, 2, 1, 48 * 128 + 56, 64, causal, 8, q_bias_std=1.0)
+    _say(f"[case delta-s-64 causal={causal}] B{w.B} H{w.H} Hkv{w.Hkv} N{w.N} d{w.d}")
+    q, k, v = make_inputs(w, seed=13)
+    qd, kd, vd = _to_dev(q, k, v)
+    o = sa.sageattn(qd, kd, vd, is_causal=causal, qk_bits=8).cpu().numpy()
+    dbg = {n: t.cpu().numpy() for n, t in sa.quant_debug(qd, kd, vd, causal, 8).items()}
+    for b in range(w.B):
+        for h in range(w.H):
+            ph = osage.prologue(*_head_slice(q, k, v, b, h, w.H, w.Hkv), causal, 8)
+            _check_prologue(dbg, ph, b, h, 0, f"delta-s-64 b{b} h{h}")
+            for qb in (0, ph.nqb // 2, ph.nqb - 1):
+                r0, r1 = qb * 128, min(w.N, qb * 128 + 128)
+                _check_o(o[b, h, r0:r1], osage.attend_block(ph, 0, 0, qb), f"delta-s-64 b{b} h{h} qb{qb}",
+                         _slack(ph, 0, 0, qb))
+
+
 # ------------------------------------------------------------------------------------------
 # variable-length batches and the NHD layout
 # ------------------------------------------------------------------------------------------

@@ -36,13 +36,21 @@ What is computed, per (batch b, query head h); kv(h) = h div (H / Hkv):
       V_q = E4M3sat(RN32(V * RN32(V_r / amax))) [SA2pp key_machinery].
   O9  online softmax over KV blocks of bk keys (FlashAttention tiling with the online
       normalizer [SA2pp supporting_citations]): m' = max(m, blockmax z); alpha = e^(m - m');
-      p = e^(z - m'); P~_q = E4M3sat(RN32(p * P_r)) (static range: within a block max p <= 1,
-      so delta_P = 1 / P_r [SA2pp key_machinery]); l = l * alpha + sum P~_q / P_r (the
+      p = e^(z - m'); P~_q = E4M3sat(RN32(p * P_r)) with the static range delta_P = 1 / P_r,
+      valid because p <= 1 everywhere (reading: [SA2pp key_machinery] describes a per-block
+      scale max(P~) / P_r instead, which equals 1 / P_r only in the block holding the running
+      maximum; p_quant_stats measures the difference); l = l * alpha + sum P~_q / P_r (the
       weights that multiply V; see attend_block); two-level accumulation [SA2 abstract; SA2c
       on Sec. 3.4]: local = sum_j P~_q * V_q over the block (exact), acc = acc * alpha + local.
   O10 O = acc * delta_V[c] / (P_r * l).
 
 Readings where the pages are silent are listed with each function.
+
+Parity unpinned: the default quantization-group geometry (Geometry's defaults: one scale per
+query row, one per (KV block, lane half) of keys) beyond its special cases (per token, per
+block), which are pinned against textbook quantization.  The pages fix only "thread-level
+granularity" on NVIDIA's layout; which gfx950 lanes share a scale is a contract with the GPU
+library (its configuration call exports the same numbers), not something a pin can derive.
 """
 
 from __future__ import annotations
@@ -208,6 +216,7 @@ class Prologue:
     quant_pv: bool
     smooth_q: bool
     smooth_k: bool
+    row_sum: str               # "weights" (default) or "unquantized": see attend_block
     # per (b, kv head)
     mu_k: np.ndarray = field(repr=False)       # f32 [B, Hkv, d]
     gamma_k: np.ndarray = field(repr=False)    # f32 [B, Hkv, N, d]
@@ -237,13 +246,17 @@ class Prologue:
 
 def prologue(q, k, v, causal: bool = False, qk_bits: int = 8, geom: Geometry = DEFAULT, *,
              quant_qk: bool = True, quant_pv: bool = True, smooth_q: bool = True,
-             smooth_k: bool = True) -> Prologue:
+             smooth_k: bool = True, row_sum: str = "weights") -> Prologue:
     """Steps O1-O4 and O8 on fp16 inputs q [B,H,N,d], k/v [B,Hkv,N,d] (numpy float16), or on
     bf16 inputs (float32 arrays of bf16 values, see is_bf16).
 
     The switches turn parts of the method off; they exist so that tests can reduce the
-    oracle to textbook attention (all off) and check each part against it.
+    oracle to textbook attention (all off) and check each part against it.  row_sum selects
+    the reading of the softmax row sum (see attend_block); only tests comparing the two
+    readings change it.
     """
+    if row_sum not in ("weights", "unquantized"):
+        raise ValueError("row_sum must be 'weights' or 'unquantized'")
     q = np.asarray(q)
     k = np.asarray(k)
     v = np.asarray(v)
@@ -287,7 +300,7 @@ def prologue(q, k, v, causal: bool = False, qk_bits: int = 8, geom: Geometry = D
             q_codes[b, h], q_delta[b, h], _ = quantize_groups(gamma_q[b, h], qgid, R)
 
     return Prologue(B, H, Hkv, N, d, bool(causal), qk_bits, g, quant_qk, quant_pv, smooth_q,
-                    smooth_k, mu_k, gamma_k, k_codes, k_delta, v_codes, v_delta, v_amax, v,
+                    smooth_k, row_sum, mu_k, gamma_k, k_codes, k_delta, v_codes, v_delta, v_amax, v,
                     mu_q, gamma_q, q_codes, q_delta)
 
 
@@ -337,8 +350,9 @@ def attend_block(pro: Prologue, b: int, h: int, qb: int, return_state: bool = Fa
 
     Reading (pages silent on the row sum): l accumulates the weights that multiply V -- the
     quantized P~_q / P_r in the FP8 mode, p itself when P V is not quantized -- so the output
-    is a weighted mean whose weights sum to exactly 1.  (Against exact attention this is as
-    accurate as summing the unquantized p, slightly more on most inputs.)  Blocks are visited
+    is a weighted mean whose weights sum to exactly 1.  The other plain reading, l summing the
+    unquantized p as a FlashAttention-style normaliser, is kept as pro.row_sum ==
+    "unquantized" so that tests can hold the two against exact attention.  Blocks are visited
     in ascending key order.
     """
     g = pro.geom
@@ -368,7 +382,10 @@ def attend_block(pro: Prologue, b: int, h: int, qb: int, return_state: bool = Fa
             pt = fp8.round_sat((p * p_r).astype(F32))     # P~_q = E4M3sat(RN32(p * P_r))
         else:
             pt = p
-        l = l * alpha + pt.sum(axis=1) / p_r               # the weights that multiply V
+        if pro.row_sum == "weights":
+            l = l * alpha + pt.sum(axis=1) / p_r           # the weights that multiply V
+        else:
+            l = l * alpha + p.sum(axis=1)                  # the unquantized probabilities
         local = pt @ vq[c0:c1]                             # block-local accumulation
         acc = acc * alpha[:, None] + local                 # global accumulation
         m = m_new
@@ -423,6 +440,71 @@ def fp8_midpoint_slack(pro: Prologue, b: int, h: int, qb: int, rel: float = 2.0 
     big_l = p_r * l                                    # L in P~ units
     denom = np.where(big_l - gs > 0, big_l - gs, np.inf)
     return (gv + gs[:, None] * np.abs(out)) / denom[:, None]
+
+
+def p_quant_stats(pro: Prologue, b: int, h: int, qb: int) -> dict:
+    """How the static range treats the probabilities of Q block qb (FP8 mode).
+
+    Static range: P~ = E4M3sat(RN32(p * P_r)) with the fixed scale delta_P = 1 / P_r, because
+    0 < p <= 1 everywhere (p = e^(z - m) with m the running maximum).  Only a block that holds
+    its row's running maximum has max p = 1; in later blocks max p < 1, and an entry with
+    p * P_r below half the smallest E4M3 subnormal (2^-10) is coded as zero.  The per-block
+    form of the scale, delta_P = max(P~) / P_r, would code each block's entries relative to
+    the block's own maximum instead; `zero_block_scale` counts the zeros that form would give
+    on the same p (for comparison only: the method here uses the static range).
+
+    Returns counts over the unmasked (row, key) entries: n, zero_static (p > 0 but P~ = 0),
+    subnormal_static (0 < P~ < 2^-6, the E4M3 subnormal range), zero_block_scale, and the
+    number of (row, block) pairs whose block maximum p is below 1 (rows_blocks_below_one) out
+    of rows_blocks.
+    """
+    g = pro.geom
+    z = logits(pro, b, h, qb)
+    rows = z.shape[0]
+    m = np.full(rows, -np.inf)
+    out = dict(n=0, zero_static=0, subnormal_static=0, zero_block_scale=0, rows_blocks=0,
+               rows_blocks_below_one=0)
+    for kb in range(pro.nkb):
+        c0, c1 = kb * g.bk, min(pro.N, (kb + 1) * g.bk)
+        zb = z[:, c0:c1]
+        m_new = np.maximum(m, zb.max(axis=1))
+        live = np.isfinite(zb)
+        p = np.where(live, np.exp(zb - np.where(np.isfinite(m_new), m_new, 0.0)[:, None]), 0.0)
+        pt = fp8.round_sat((p * g.p_range).astype(F32))
+        bmax = p.max(axis=1)
+        has = live.any(axis=1)
+        scale = np.where(bmax > 0, g.p_range / np.where(bmax > 0, bmax, 1.0), 0.0)
+        pt_blk = fp8.round_sat((p * scale[:, None]).astype(F32))
+        out["n"] += int(live.sum())
+        out["zero_static"] += int(np.count_nonzero(live & (p > 0) & (pt == 0)))
+        out["subnormal_static"] += int(np.count_nonzero(live & (pt > 0) & (pt < 2.0 ** -6)))
+        out["zero_block_scale"] += int(np.count_nonzero(live & (p > 0) & (pt_blk == 0)))
+        out["rows_blocks"] += int(has.sum())
+        out["rows_blocks_below_one"] += int(np.count_nonzero(has & (bmax < 1.0)))
+        m = m_new
+    return out
+
+
+def p_flushed_mass(pro: Prologue, b: int, h: int, qb: int) -> np.ndarray:
+    """Per row of Q block qb: the share of its exact softmax weight e^(z - max z) / sum that
+    falls on entries the static range codes as zero (p * P_r at or below 2^-10, p taken against
+    the running maximum of its block, as in the online softmax).  fp64 [rows]."""
+    g = pro.geom
+    z = logits(pro, b, h, qb)
+    top = z.max(axis=1)
+    w = np.exp(z - top[:, None])
+    total = w.sum(axis=1)
+    m = np.full(z.shape[0], -np.inf)
+    flushed = np.zeros(z.shape[0])
+    for kb in range(pro.nkb):
+        c0, c1 = kb * g.bk, min(pro.N, (kb + 1) * g.bk)
+        zb = z[:, c0:c1]
+        m = np.maximum(m, zb.max(axis=1))
+        live = np.isfinite(zb)
+        p = np.where(live, np.exp(zb - m[:, None]), 0.0)
+        pt = fp8.round_sat((p * g.p_range).astype(F32))
+        flushed += np.where(live & (p > 0) & (pt == 0), w[:, c0:c1], 0.0).sum(axis=1)
+    return flushed / total
 
 
 def sage_attention(q, k, v, causal: bool = False, qk_bits: int = 8, geom: Geometry = DEFAULT,

@@ -18,10 +18,11 @@
 //   * The S^T accumulators already sit in the B-operand layout of v_mfma_f32_32x32x64_f8f6f4
 //     (lane l: column l % 32, 32 consecutive k-slots): P~ goes from registers to the FP8 MFMA
 //     with no LDS round trip; V^T is pre-permuted by the prologue into the same k-slot order.
-//   * Each 128-key block's P~V accumulates from zero (two 64-deep MFMAs), then is folded
-//     into the fp32 output accumulator: O = O * alpha + local.  On gfx950 the FP8 MFMA also
-//     sums its products with reduced internal precision, so the block-local step bounds that
-//     error to one block, as on the hardware the pages target.
+//   * Two-level P~V accumulation: on gfx950 each FP8 MFMA sums its 64 products inside the
+//     matrix unit with reduced precision (the block-local level, 64 keys), and adds that sum to
+//     its C operand at fp32 precision (the global level).  So the fp32 output accumulator O is
+//     itself the C operand: O <- O * alpha (skipped when the wave's running maxima did not
+//     move), then O += P~ V per 64-key half.  The narrow sum never spans more than 64 products.
 //   * K/V code tiles stream HBM -> LDS with direct-to-LDS buffer loads (buffer_load_dwordx4 lds),
 //     in a ring of two stages (three at d = 64 in the FP8 mode, where a block's arithmetic is
 //     too short to cover a tile issued only one block ahead), 16-byte chunks XOR-swizzled
@@ -48,6 +49,7 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
@@ -68,8 +70,36 @@ template <> struct PV16T<true> {
 };
 
 constexpr float kLog2Pr = 8.807354922057604f;   // log2(448)
-// FP8 E4M3 1.0 in all 32 bytes of an MFMA operand
-#define kOnesFp8 ((v8i){0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838})
+
+// The row sum of P~ on v_mfma_f32_16x16x128_f8f6f4, with P~ as its B operand exactly as packed
+// for the 32x32x64 P~V instruction.  Each group g = l / 16 of 16 lanes supplies one quarter of the
+// k range for columns l % 16; in the 32x32x64 layout lane l holds query l % 32 and 32 keys, so
+// groups 0 and 2 hold queries 0-15 (two key ranges each), groups 1 and 3 queries 16-31.  The A
+// operand selects: its row r (lane r % 16 of group g supplies A[r][k] for that group's k range)
+// is FP8 1.0 where r % 4 == 0 and (r / 4) % 2 == g % 2, else zero.  Then output row 4G of column
+// n sums the lanes 16g + n with g = G (mod 2), i.e. all keys of query 16 (G % 2) + n, and that
+// row is element 0 of the accumulator of lane 16 G + n -- the lane holding that query.  One
+// 16x16x128 instruction per 64 keys (half the matrix time of a 32x32x64 against all-ones).
+__device__ inline v8i rowsum_selector(int lane) {
+  const int r = lane & 15, g = lane >> 4;
+  const int x = ((r & 3) == 0 && ((r >> 2) & 1) == (g & 1)) ? 0x38383838 : 0;
+  return (v8i){x, x, x, x, x, x, x, x};
+}
+__device__ inline v4f rowsum_mfma(const v8i& sel, const v8i& pb, v4f acc) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(sel, pb, acc, 0, 0, 0, 0, 0, 0);
+}
+
+// O <- O * alpha before a block's P~V (or P V) matrix instructions accumulate into O.  alpha is
+// per query (lane column); when no query of the wave raised its running maximum, every alpha is
+// exactly 1 and the whole wave skips the multiplications (a wave-uniform branch).
+template <int NT>
+__device__ inline void rescale_o(v16f (&og)[NT], float alpha) {
+  if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) == 0) return;
+#pragma unroll
+  for (int ct = 0; ct < NT; ++ct)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) og[ct][e] *= alpha;
+}
 
 struct AttnArgs {
   const int8_t* qcodes;
@@ -347,6 +377,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
   v16f og[D / 32];
 #pragma unroll
   for (int ct = 0; ct < D / 32; ++ct) og[ct] = (v16f){};
+  const v8i rsel = rowsum_selector(lane);     // A operand of the P~ row-sum instruction
 
   constexpr int NST = Smem<D, PV16>::NST;
   // blocks 0 .. NST - 2 into stages 0 .. NST - 2; wait for block 0
@@ -431,10 +462,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
       if (more) wait_all_but_k_tile<D>();
       else wait_loads();
       __syncthreads();
-#pragma unroll
-      for (int ct = 0; ct < D / 32; ++ct)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) og[ct][e] *= alpha;
+      rescale_o(og, alpha);
 
       // per 32-key tile: P = RN16(p) packed straight into two fp16 MFMA B operands (operand m
       // takes the lane's keys of accumulator quads 2m and 2m + 1), then P V into the fp32
@@ -480,15 +508,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
       return;
     }
 
+    // O * alpha first: the P~V matrix instructions below accumulate into O
+    rescale_o(og, alpha);
     if constexpr (kSplitPV<D>) {
       // P~ = E4M3(p * P_r), packed straight into the FP8 MFMA B operand, one 64-key half (u) at a
-      // time: the matrix instructions of half u -- its row sum, and its P~ V into the block-local
-      // accumulators -- do not depend on the exponentials of the next half, so the two interleave.
-      // Each accumulator still sums u = 0 then u = 1 from zero, as before the split.
-      v16f ls = {};
-      v16f loc[D / 32];
-#pragma unroll
-      for (int ct = 0; ct < D / 32; ++ct) loc[ct] = (v16f){};
+      // time: the matrix instructions of half u -- its row sum, and its P~ V into O -- do not
+      // depend on the exponentials of the next half, so the two interleave.
+      v4f ls = {};
 #pragma unroll
       for (int u = 0; u < BK / 64; ++u) {
         v8i pb;
@@ -508,11 +534,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
             pb[tt * 4 + qq] = word;
           }
         }
-        // the row sum of the weights that multiply V: P~ against an all-ones A operand on the FP8
-        // MFMA (every output row is the column sum, both lane halves included) -- one matrix
-        // instruction per half instead of 32 vector adds per lane
-        ls = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kOnesFp8, pb, ls, 0, 0, 0, 0, 0, 0);
-        // P~ V, block-local: half u of every channel tile
+        // the row sum of the weights that multiply V (P~ in FP8 units)
+        ls = rowsum_mfma(rsel, pb, ls);
+        // O += P~ V over this half's 64 keys, every channel tile
 #pragma unroll
         for (int ct = 0; ct < D / 32; ++ct) {
           const int c = 32 * ct + col;
@@ -521,15 +545,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
           const v4i lo = *reinterpret_cast<const v4i*>(row + ((2 * half) ^ sw) * 16);
           const v4i hi = *reinterpret_cast<const v4i*>(row + ((2 * half + 1) ^ sw) * 16);
           const v8i va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          loc[ct] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, loc[ct], 0, 0, 0, 0, 0, 0);
+          og[ct] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, og[ct], 0, 0, 0, 0, 0, 0);
         }
       }
       l_part = fmaf(l_part, alpha, ls[0]);
-      // the fp32 global accumulator
-#pragma unroll
-      for (int ct = 0; ct < D / 32; ++ct)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) og[ct][e] = fmaf(og[ct][e], alpha, loc[ct][e]);
     } else {
       // P~ = E4M3(p * P_r), packed straight into the FP8 MFMA B operand
       v8i pb[BK / 64];
@@ -548,21 +567,17 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
           pb[t >> 1][(t & 1) * 4 + qq] = word;
         }
       }
-      // the row sum of the weights that multiply V: P~ against an all-ones A operand on the FP8
-      // MFMA (every output row is the column sum, both lane halves included) -- two matrix
-      // instructions instead of 64 vector adds per lane
+      // the row sum of the weights that multiply V (P~ in FP8 units)
       {
-        v16f ls = {};
+        v4f ls = {};
 #pragma unroll
-        for (int u = 0; u < BK / 64; ++u)
-          ls = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kOnesFp8, pb[u], ls, 0, 0, 0, 0, 0, 0);
+        for (int u = 0; u < BK / 64; ++u) ls = rowsum_mfma(rsel, pb[u], ls);
         l_part = fmaf(l_part, alpha, ls[0]);
       }
 
-      // P~ V: block-local accumulation from zero, then the fp32 global accumulator
+      // O += P~ V, 64 keys per matrix instruction
 #pragma unroll
       for (int ct = 0; ct < D / 32; ++ct) {
-        v16f loc = {};
         const int c = 32 * ct + col;
 #pragma unroll
         for (int u = 0; u < BK / 64; ++u) {
@@ -571,10 +586,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
           const v4i lo = *reinterpret_cast<const v4i*>(row + ((2 * half) ^ sw) * 16);
           const v4i hi = *reinterpret_cast<const v4i*>(row + ((2 * half + 1) ^ sw) * 16);
           const v8i va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          loc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb[u], loc, 0, 0, 0, 0, 0, 0);
+          og[ct] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb[u], og[ct], 0, 0, 0, 0, 0, 0);
         }
-#pragma unroll
-        for (int e = 0; e < 16; ++e) og[ct][e] = fmaf(og[ct][e], alpha, loc[e]);
       }
     }
 
@@ -595,8 +608,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
   for (int kb = 0; kb < nfull; ++kb) block(kb, std::false_type{});
   if (mask_last) block(nblk - 1, std::true_type{});
 
-  // epilogue: O = acc * delta_V / l   (FP8: l sums P~, so it carries the 1/P_r, and the MFMA
-  // has already added both lane halves; fp16: no V scale, per-lane partial sums)
+  // epilogue: O = acc * delta_V / l   (FP8: l sums P~, so it carries the 1/P_r, and the row-sum
+  // instruction has already added both lane halves; fp16: no V scale, per-lane partial sums)
   const float l = PV16 ? xhalf_sum(l_part) : l_part;
   const float inv_l = l > 0.f ? 1.f / l : 0.f;
   if (i < N) {
@@ -644,11 +657,8 @@ AttnArgs make_args(const Dims& D, const Ptrs& P) {
 template <int DD, bool QK4, bool PV16, bool BF>
 hipError_t launch_d(const Dims& D, const AttnArgs& a, hipStream_t s) {
   const int grid = D.B * D.H * D.nqb;
-  if (D.causal)
-    attn_fwd<DD, true, false, QK4, PV16, BF><<<grid, 256, 0, s>>>(a);
-  else
-    attn_fwd<DD, false, false, QK4, PV16, BF><<<grid, 256, 0, s>>>(a);
-  return hipGetLastError();
+  if (D.causal) return launch(attn_fwd<DD, true, false, QK4, PV16, BF>, dim3(grid), dim3(256), s, a);
+  return launch(attn_fwd<DD, false, false, QK4, PV16, BF>, dim3(grid), dim3(256), s, a);
 }
 
 template <bool QK4, bool PV16>
@@ -668,14 +678,12 @@ hipError_t launch_attention(const Dims& D, const Ptrs& P, hipStream_t s) {
 hipError_t launch_qk_tile(const Dims& D, const Ptrs& P, int b, int h, int qb, int kb, int32_t* out, hipStream_t s) {
   AttnArgs a = make_args(D, P);
   a.dbg_b = b; a.dbg_h = h; a.dbg_qb = qb; a.dbg_kb = kb; a.dbg_out = out;
-  if (D.qk_bits == 4) {
-    if (D.d == 128) attn_fwd<128, false, true, true, false, false><<<1, 256, 0, s>>>(a);
-    else attn_fwd<64, false, true, true, false, false><<<1, 256, 0, s>>>(a);
-  } else {
-    if (D.d == 128) attn_fwd<128, false, true, false, false, false><<<1, 256, 0, s>>>(a);
-    else attn_fwd<64, false, true, false, false, false><<<1, 256, 0, s>>>(a);
-  }
-  return hipGetLastError();
+  const dim3 one(1), blk(256);
+  if (D.qk_bits == 4)
+    return D.d == 128 ? launch(attn_fwd<128, false, true, true, false, false>, one, blk, s, a)
+                      : launch(attn_fwd<64, false, true, true, false, false>, one, blk, s, a);
+  return D.d == 128 ? launch(attn_fwd<128, false, true, false, false, false>, one, blk, s, a)
+                    : launch(attn_fwd<64, false, true, false, false, false>, one, blk, s, a);
 }
 
 }  // namespace sage

@@ -895,50 +895,41 @@ hipError_t launch_prologue_d(const Dims& Dm, const Ptrs& P, hipStream_t s) {
   const T* k = reinterpret_cast<const T*>(P.k);
   const T* v = reinterpret_cast<const T*>(P.v);
   const int nkv = Dm.B * Dm.Hkv * D;
-  init_stats<<<(nkv + 255) / 256, 256, 0, s>>>(P.ksum, P.vamax, nkv, Dm.bf16 ? kLimbs : 1);
+  const dim3 blk(256);
+  hipError_t e = launch(init_stats, dim3((nkv + 255) / 256), blk, s, P.ksum, P.vamax, nkv, Dm.bf16 ? kLimbs : 1);
+  if (e != hipSuccess) return e;
   const dim3 gs((Dm.N + 255) / 256, Dm.B * Dm.Hkv), gq(Dm.nkb, Dm.B * Dm.Hkv);
   // INT4-range codes (R = 7) are stored as FP6: a compile-time switch of the code store
   auto kvq = [&](auto pv16, auto qk4) {
-    kv_quant<D, decltype(pv16)::value, T, decltype(qk4)::value><<<gq, 256, 0, s>>>(
-        k, v, P.ksum, P.vamax, P.kcodes, P.vcodes, P.kscale, P.muk, P.vscale, g, R);
+    return launch(kv_quant<D, decltype(pv16)::value, T, decltype(qk4)::value>, gq, blk, s,
+                  k, v, P.ksum, P.vamax, P.kcodes, P.vcodes, P.kscale, P.muk, P.vscale, g, R);
   };
   const bool qk4 = Dm.qk_bits == 4;
   // statistics (K, and V unless it stays 16-bit) and the Q prologue: one launch
   const int nks = (int)(gs.x * gs.y), nsq = nks + Dm.nqb * Dm.B * Dm.H;
   auto sq = [&](auto vstats, auto q4) {
-    stats_and_q<D, decltype(vstats)::value, T, decltype(q4)::value><<<nsq, 256, 0, s>>>(
-        k, v, P.ksum, P.vamax, q, P.qcodes, P.qscale, P.muq, P.muqs, g, R, (int)gs.x, nks, Dm.nqb);
+    return launch(stats_and_q<D, decltype(vstats)::value, T, decltype(q4)::value>, dim3(nsq), blk, s,
+                  k, v, P.ksum, P.vamax, q, P.qcodes, P.qscale, P.muq, P.muqs, g, R, (int)gs.x, nks, Dm.nqb);
   };
   const bool vstats = Dm.pv_bits != 16;
-  if (vstats) {
-    if (qk4) sq(std::true_type{}, std::true_type{});
-    else sq(std::true_type{}, std::false_type{});
-  } else {
-    if (qk4) sq(std::false_type{}, std::true_type{});
-    else sq(std::false_type{}, std::false_type{});
-  }
-  if (Dm.pv_bits == 16) {
-    if (qk4) kvq(std::true_type{}, std::true_type{});
-    else kvq(std::true_type{}, std::false_type{});
-  } else {
-    if (qk4) kvq(std::false_type{}, std::true_type{});
-    else kvq(std::false_type{}, std::false_type{});
-  }
+  if (vstats) e = qk4 ? sq(std::true_type{}, std::true_type{}) : sq(std::true_type{}, std::false_type{});
+  else e = qk4 ? sq(std::false_type{}, std::true_type{}) : sq(std::false_type{}, std::false_type{});
+  if (e != hipSuccess) return e;
+  if (Dm.pv_bits == 16) e = qk4 ? kvq(std::true_type{}, std::true_type{}) : kvq(std::true_type{}, std::false_type{});
+  else e = qk4 ? kvq(std::false_type{}, std::true_type{}) : kvq(std::false_type{}, std::false_type{});
+  if (e != hipSuccess) return e;
   const float k2 = (float)(1.4426950408889634 / sqrt((double)D));
   // 64 Q blocks per workgroup when sequences are long (the key split is shared by more MFMAs),
   // 32 when they are short on average (varlen prefill batches: less work on rows past the end)
   auto dsl = [&](auto nu) {
     constexpr int NU = decltype(nu)::value;
     const int nqt = (Dm.nqb + 32 * NU - 1) / (32 * NU), nkt = (Dm.Npad + DS_KT - 1) / DS_KT;
-    const int gds = nqt * Dm.H * nkt * Dm.B;
-    if (Dm.causal)
-      delta_s<D, true, T, NU><<<gds, 256, 0, s>>>(k, P.muk, P.muqs, P.ds, g, Dm.B, nqt, nkt, k2);
-    else
-      delta_s<D, false, T, NU><<<gds, 256, 0, s>>>(k, P.muk, P.muqs, P.ds, g, Dm.B, nqt, nkt, k2);
+    const dim3 gds(nqt * Dm.H * nkt * Dm.B);
+    if (Dm.causal) return launch(delta_s<D, true, T, NU>, gds, blk, s, k, P.muk, P.muqs, P.ds, g, Dm.B, nqt, nkt, k2);
+    return launch(delta_s<D, false, T, NU>, gds, blk, s, k, P.muk, P.muqs, P.ds, g, Dm.B, nqt, nkt, k2);
   };
-  if (Dm.tot_pad >= 48LL * BQ * Dm.B) dsl(std::integral_constant<int, 2>{});
-  else dsl(std::integral_constant<int, 1>{});
-  return hipGetLastError();
+  if (Dm.tot_pad >= 48LL * BQ * Dm.B) return dsl(std::integral_constant<int, 2>{});
+  return dsl(std::integral_constant<int, 1>{});
 }
 
 }  // namespace
@@ -949,9 +940,10 @@ hipError_t launch_seq_table(const Seq* host, int n, Seq* dev, hipStream_t s) {
     c.first = first;
     c.count = n - first < 64 ? n - first : 64;
     for (int i = 0; i < c.count; ++i) c.e[i] = host[first + i];
-    write_seq_table<<<1, 64, 0, s>>>(c, dev);
+    const hipError_t e = launch(write_seq_table, dim3(1), dim3(64), s, c, dev);
+    if (e != hipSuccess) return e;
   }
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 hipError_t launch_prologue(const Dims& D, const Ptrs& P, hipStream_t s) {
@@ -963,7 +955,7 @@ hipError_t launch_debug_copy(const Dims& D, const Ptrs& P, hipStream_t s, float*
                              float* k_scales, uint8_t* v_codes, float* v_scales, float* mu_q, int8_t* q_codes,
                              float* q_scales, float* delta_s_out) {
   const int hkv = D.B * D.Hkv, hq = D.B * D.H;
-  const int grid = 1024, blk = 256;
+  const dim3 grid(1024), blk(256);
   if (mu_k) {
     hipError_t e = hipMemcpyAsync(mu_k, P.muk, (size_t)hkv * D.d * 4, hipMemcpyDeviceToDevice, s);
     if (e != hipSuccess) return e;
@@ -978,16 +970,24 @@ hipError_t launch_debug_copy(const Dims& D, const Ptrs& P, hipStream_t s, float*
     if (e != hipSuccess) return e;
   }
   const bool fp6 = D.qk_bits == 4;    // INT4-range codes are stored as packed FP6 E2M3
-  if (k_codes) copy_rows_i8<<<grid, blk, 0, s>>>(P.kcodes, k_codes, hkv, D.N, D.Npad, D.d, fp6);
-  if (q_codes) copy_rows_i8<<<grid, blk, 0, s>>>(P.qcodes, q_codes, hq, D.N, D.Npad, D.d, fp6);
-  if (k_scales) expand_kscale<<<grid, blk, 0, s>>>(P.kscale, k_scales, hkv, D.N, D.nkb);
-  if (q_scales) copy_rows_f32<<<grid, blk, 0, s>>>(P.qscale, q_scales, (size_t)hq, D.N, D.Npad, 1.f);
-  if (v_codes && pv8) unpermute_v<<<grid, blk, 0, s>>>(P.vcodes, v_codes, hkv, D.N, D.Npad, D.d);
+  hipError_t e = hipSuccess;
+  if (k_codes && (e = launch(copy_rows_i8, grid, blk, s, P.kcodes, k_codes, hkv, D.N, D.Npad, D.d, fp6)) != hipSuccess)
+    return e;
+  if (q_codes && (e = launch(copy_rows_i8, grid, blk, s, P.qcodes, q_codes, hq, D.N, D.Npad, D.d, fp6)) != hipSuccess)
+    return e;
+  if (k_scales && (e = launch(expand_kscale, grid, blk, s, P.kscale, k_scales, hkv, D.N, D.nkb)) != hipSuccess)
+    return e;
+  if (q_scales &&
+      (e = launch(copy_rows_f32, grid, blk, s, P.qscale, q_scales, (size_t)hq, D.N, D.Npad, 1.f)) != hipSuccess)
+    return e;
+  if (v_codes && pv8 &&
+      (e = launch(unpermute_v, grid, blk, s, P.vcodes, v_codes, hkv, D.N, D.Npad, D.d)) != hipSuccess)
+    return e;
   if (delta_s_out) {
     const float inv_k2 = (float)(sqrt((double)D.d) / 1.4426950408889634);
-    copy_ds<<<grid, blk, 0, s>>>(P.ds, delta_s_out, hq, D.nqb, D.N, D.Npad, D.causal != 0, inv_k2);
+    e = launch(copy_ds, grid, blk, s, P.ds, delta_s_out, hq, D.nqb, D.N, D.Npad, D.causal != 0, inv_k2);
   }
-  return hipGetLastError();
+  return e;
 }
 
 }  // namespace sage

@@ -6,6 +6,9 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <tuple>
+#include <utility>
+
 namespace sage {
 
 // ---- compile-time geometry (exported by sage_get_config) ----
@@ -214,6 +217,21 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t by
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 #endif
+// Launch kernel k on stream s and return the status of this launch itself.  (A launch written as
+// k<<<...>>>(...) followed by hipGetLastError() would also report an error left on the thread by
+// an unrelated earlier call.)  The arguments are converted to the kernel's parameter types.
+template <typename... P, typename... A>
+inline hipError_t launch(void (*k)(P...), dim3 grid, dim3 block, hipStream_t s, A&&... args) {
+  static_assert(sizeof...(P) == sizeof...(A) && sizeof...(P) > 0, "kernel argument count");
+  std::tuple<P...> vals(static_cast<P>(std::forward<A>(args))...);
+  return std::apply(
+      [&](auto&... v) {
+        void* ptrs[] = {static_cast<void*>(&v)...};
+        return hipLaunchKernel(reinterpret_cast<const void*>(k), grid, block, ptrs, 0, s);
+      },
+      vals);
+}
+
 // ---- launchers (return the hipError_t of the launch) ----
 // varlen: copy the host-built sequence table into the workspace (kernel arguments, no host
 // buffer outlives the call)

@@ -194,3 +194,57 @@ def test_bf16_workspace_holds_the_limb_sums(pkg):
     assert pkg._lib.sage_attn_workspace_bytes_ex(p16.ref, ctypes.byref(n16)) == 0
     assert pkg._lib.sage_attn_workspace_bytes_ex(pbf.ref, ctypes.byref(nbf)) == 0
     assert nbf.value - n16.value >= 11 * 8 * 2 * 64
+
+
+def _hip_device_count() -> int:
+    """GPUs the HIP runtime sees (0 when none, or when the runtime cannot be loaded)."""
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+    except OSError:
+        return 0
+    n = ctypes.c_int(0)
+    return n.value if hip.hipGetDeviceCount(ctypes.byref(n)) == 0 else 0
+
+
+def test_valid_call_without_a_device_reports_hip_error(pkg):
+    """A call that passes validation reaches its first launch; with no GPU that launch fails and
+    the library returns SAGE_ERR_HIP with the runtime's message for this very launch.  Runs only
+    on a host without a GPU: the pointers are fake and must never reach a kernel."""
+    if _hip_device_count() > 0:
+        pytest.skip("a GPU is present: this check needs a host without one")
+    lib = pkg._lib
+    fake, ws = ctypes.c_void_p(0x10000000), ctypes.c_void_p(0x20000000)
+    dims = (1, 2, 2, 256, 64, 0, 8, 8)
+    assert lib.sage_attn_fwd(fake, fake, fake, fake, *dims, ws, pkg.workspace_bytes(*dims), None) == -4
+    msg = lib.sage_last_error().decode()
+    assert msg.startswith("prologue launch:") and len(msg) > len("prologue launch: ")
+    p = pkg.Problem(2, 4, 2, 0, 64, True, 8, 8, "HND", cu_seqlens=[0, 5, 9])
+    n = ctypes.c_size_t(0)
+    assert lib.sage_attn_workspace_bytes_ex(p.ref, ctypes.byref(n)) == 0
+    assert lib.sage_attn_fwd_ex(p.ref, fake, fake, fake, fake, ws, n.value, None) == -4
+    assert lib.sage_last_error().decode().startswith("sequence table launch:")
+    assert lib.sage_attn_attend(fake, *dims, ws, pkg.workspace_bytes(*dims), None) == -4
+    assert lib.sage_last_error().decode().startswith("attention launch:")
+
+
+def test_host_code_under_address_and_undefined_behavior_sanitizers(tmp_path):
+    """The library's host code (csrc/api.hip: validation, workspace carve-up, varlen table) built
+    with AddressSanitizer and UndefinedBehaviorSanitizer, host side only, and driven by
+    tests/abi_host_check.cpp with stand-in launchers that fill every workspace section and the
+    output in host memory (sections tagged, so overlaps show too)."""
+    import shutil
+    import subprocess
+    hipcc = "/opt/rocm/bin/hipcc" if os.path.exists("/opt/rocm/bin/hipcc") else shutil.which("hipcc")
+    if not hipcc:
+        pytest.skip("hipcc not available")
+    exe = str(tmp_path / "abi_host_check")
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-sanitize-recover=all"]
+    cmd = [hipcc, "-x", "hip", "--offload-host-only", "-std=c++17", "-O1", "-g", *san,
+           os.path.join(ROOT, "quantized_attention_smooth_amd", "csrc", "api.hip"),
+           os.path.join(ROOT, "tests", "abi_host_check.cpp"), "-o", exe]
+    b = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
+    assert b.returncode == 0, b.stdout + b.stderr
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:halt_on_error=1", UBSAN_OPTIONS="halt_on_error=1")
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=600, env=env)
+    assert r.returncode == 0 and r.stdout.strip() == "ok", r.stdout + r.stderr

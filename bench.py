@@ -112,13 +112,105 @@ def cpu_baseline(w, q1, k1, v1, budget_s: float, pv_bits: int = 8, head_ops: flo
     t_head = t_pro + per_unit * sum(cost)
     t_total = t_head * w.ops / head_ops
     value = w.ops / t_total / 1e12
+    cores = len(os.sched_getaffinity(0))
     return {
-        "value": value, "unit": "TOPS", "cores": int(blas), "kind": "oracle",
+        "value": value, "unit": "TOPS", "cores": int(min(cores, blas)), "kind": "oracle",
         "sample": (f"numpy oracle on one head ({pro.N} tokens): full prologue ({t_pro:.1f} s) + {nblk} of {nqb} "
                    f"query blocks ({t_att:.1f} s), extrapolated by block cost to the head and by ops to the "
                    f"workload "
-                   f"(est. {t_total:.0f} s for the workload); BLAS threads {blas}, elementwise 1 thread"),
+                   f"(est. {t_total:.0f} s for the workload); BLAS threads {blas} of {cores} host cores in the "
+                   f"process's affinity set, elementwise 1 thread"),
+        "_blocks": order[:nblk], "_pro": pro,
     }
+
+
+def environment() -> dict:
+    """Host, software and device facts for the record (read outside the timed region)."""
+    import platform
+    import subprocess
+
+    import torch
+    env = {"torch": torch.__version__, "hip": getattr(torch.version, "hip", None), "python": platform.python_version()}
+    try:
+        env["rocm"] = open("/opt/rocm/.info/version").read().strip()
+    except OSError:
+        env["rocm"] = None
+    try:
+        env["gpu"] = torch.cuda.get_device_name(0)
+    except Exception:  # pragma: no cover - reporting only
+        env["gpu"] = None
+    cpu = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    env["cpu_model"] = cpu
+    env["cpu_cores_affinity"] = len(os.sched_getaffinity(0))
+    # the GPU's clock as its management tool reports it right after the timed region (best effort)
+    clocks = None
+    for cmd in (["amd-smi", "metric", "-g", "0", "-c", "--json"], ["rocm-smi", "--showclocks", "--json"]):
+        try:
+            r = subprocess.run(cmd, capture_output=True, text=True, timeout=20)
+        except (OSError, subprocess.TimeoutExpired):
+            continue
+        if r.returncode == 0 and r.stdout.strip():
+            try:
+                clocks = json.loads(r.stdout)
+            except ValueError:
+                clocks = r.stdout.strip()[:2000]
+            break
+    env["clocks_after_run"] = clocks
+    return env
+
+
+def measured_peaks(dev, qk_bits: int, pv_bits: int, iters: int = 6000, reps: int = 3) -> dict:
+    """Sustained dense MFMA rates from the library's rate probe (register operands, two waves per
+    SIMD), for the two instructions the attention kernel uses, and their harmonic mix."""
+    import torch
+
+    import quantized_attention_smooth_amd as sa
+    sink = torch.empty(1 << 18, dtype=torch.float32, device=dev)
+    kinds = {"qk": "int8" if qk_bits == 8 else "fp6", "pv": "fp8" if pv_bits == 8 else "fp16"}
+    out = {}
+    for role, kind in kinds.items():
+        sa.mfma_rate_probe(kind, 100, sink)                 # warm-up
+        best = 0.0
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            ops = sa.mfma_rate_probe(kind, iters, sink)
+            e1.record()
+            torch.cuda.synchronize()
+            best = max(best, ops / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+        out[f"{role}_{kind}_TOPS"] = best
+    out["mix_TOPS"] = 1.0 / (0.5 / out[f"qk_{kinds['qk']}_TOPS"] + 0.5 / out[f"pv_{kinds['pv']}_TOPS"])
+    return out
+
+
+def accuracy(o_gpu, q1, k1, v1, causal: bool, row_blocks, pro) -> dict:
+    """O of the sampled query blocks of one head against exact fp64 attention and against the
+    oracle: cosine similarity, RMSE, relative L1 (sum |o - e| / sum |e|) and the largest error,
+    set beside the pages' figures."""
+    import numpy as np
+    from oracle import sage as osage
+    rows = np.concatenate([np.arange(qb * 128, min(pro.N, qb * 128 + 128)) for qb in row_blocks])
+    e = osage.exact_attention_rows(q1[0, 0], k1[0, 0], v1[0, 0], rows, causal)
+    orc = np.concatenate([osage.attend_block(pro, 0, 0, qb) for qb in row_blocks])
+    g = np.asarray(o_gpu, dtype=np.float64)[rows]
+
+    def cmp(a, b):
+        return {"cos": float((a * b).sum() / np.sqrt((a * a).sum() * (b * b).sum())),
+                "rmse": float(np.sqrt(((a - b) ** 2).mean())),
+                "rel_l1": float(np.abs(a - b).sum() / np.abs(b).sum()),
+                "max_abs": float(np.abs(a - b).max())}
+    return {"rows": int(rows.size), "gpu_vs_exact": cmp(g, e), "oracle_vs_exact": cmp(orc, e),
+            "gpu_vs_oracle": {**cmp(g, orc), "max_abs_over_max_oracle": float(np.abs(g - orc).max() / np.abs(orc).max())},
+            "pages": "CosSim 99.45 % average, 96.72 % worst layer, RMSE 0.0313 (SageAttention2 notes, per-thread "
+                     "INT4, real model layers); CosSim 99.97 %, L1 0.01862 (SageAttention2++ verdict page, "
+                     "CogvideoX layers)"}
 
 
 def calibrate_copy(nbytes: int = 1 << 30, reps: int = 3) -> None:
@@ -209,12 +301,16 @@ def main() -> int:
     wall = time.perf_counter() - t0
 
     ms_step = e_start.elapsed_time(e_end) / K
-    pro_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    att_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    pro_all = [e[0].elapsed_time(e[1]) for e in ev]
+    att_all = [e[1].elapsed_time(e[2]) for e in ev]
+    step_all = [e[0].elapsed_time(e[2]) for e in ev]
+    pro_ms = float(np.mean(pro_all))
+    att_ms = float(np.mean(att_all))
 
     # The prologue alone with the caches emptied first: back to back, the inputs the previous step
     # read can still sit in the 256 MB memory-side cache (MALL).  Writing a 512 MB buffer before
     # each call evicts them, so this time is the HBM-bound one.
+    o_host = o.float().cpu().numpy()                                    # for the accuracy report
     flush = torch.empty(128 << 20, dtype=torch.float32, device=dev)
     cold = []
     for _ in range(min(K, 10)):
@@ -241,6 +337,7 @@ def main() -> int:
     pro_bytes = 2 * (n_q + 2 * n_kv) + (n_q + n_kv) + n_kv * (pv // 8) + 4 * ds_elems
     traffic = _traffic(args.workload, pv)
     peak = attn_peak(w.qk_bits, pv)
+    meas = measured_peaks(dev, w.qk_bits, pv)
     qk_t = "int8" if w.qk_bits == 8 else "fp6 (INT4-range codes)"
     pv_t = "P~V fp8" if pv == 8 else "PV fp16"
 
@@ -254,27 +351,47 @@ def main() -> int:
                    **({"cu_seqlens": w.cu_seqlens} if varlen else {})},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                      "frac": achieved / peak, "traffic": traffic,
+                     "traffic_source": ("HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE "
+                                        "runs of this kernel source (profiles/traffic_counters.txt), not measured "
+                                        "in this run; null when the source changed since"),
+                     "measured_peak": meas["mix_TOPS"], "frac_of_measured_peak": achieved / meas["mix_TOPS"],
+                     "measured_peaks": meas,
                      "kernel": f"attn_fwd (fused QK^T {qk_t} MFMA + softmax + {pv_t} MFMA)",
                      "per_unit": f"4*d = {4 * w.d} int8/fp8 ops per score element; "
                                  f"{ops / (4 * w.d):.4g} score elements per launch"},
         "breakdown": {"prologue_ms": pro_ms, "attention_ms": att_ms,
+                      "step_ms_median": float(np.median(step_all)), "step_ms_min": float(np.min(step_all)),
+                      "attention_ms_median": float(np.median(att_all)), "attention_ms_min": float(np.min(att_all)),
+                      "prologue_ms_median": float(np.median(pro_all)), "prologue_ms_min": float(np.min(pro_all)),
+                      "timing": ("K timed steps between two torch.cuda.synchronize() calls after W warm-up steps; "
+                                 "ms_per_step = the span of all K by HIP events / K; per-kernel times are HIP events "
+                                 "on the stream the kernels run on, mean / median / min over the K steps"),
                       "prologue_GBps_algorithmic": pro_bytes / (pro_ms * 1e-3) / 1e9,
                       "prologue_frac_hbm": pro_bytes / (pro_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
                       "prologue_ms_caches_flushed": pro_cold_ms,
                       "prologue_GBps_algorithmic_caches_flushed": pro_bytes / (pro_cold_ms * 1e-3) / 1e9,
                       "wall_s_timed": wall},
     }
+    line["environment"] = environment()
     if not args.no_cpu_baseline:
         if varlen:                      # one head of the longest sequence
             s = int(np.argmax(w.lens))
             a, b = w.cu_seqlens[s], w.cu_seqlens[s + 1]
             q1, k1, v1 = (np.ascontiguousarray(x[a:b, :1].transpose(1, 0, 2))[None] for x in (q, k, v))
+            o1 = o_host[a:b, 0]
             n = b - a
         else:                           # head (0, 0)
             q1, k1, v1 = (np.ascontiguousarray(x[:1, :1]) for x in (q, k, v))
+            o1 = o_host[0, 0]
             n = w.N
         head_ops = 4.0 * n * n * w.d / (2 if w.causal else 1)
-        line["cpu_baseline"] = cpu_baseline(w, q1, k1, v1, args.cpu_budget, pv, head_ops)
+        cb = cpu_baseline(w, q1, k1, v1, args.cpu_budget, pv, head_ops)
+        blocks, pro = cb.pop("_blocks"), cb.pop("_pro")
+        line["cpu_baseline"] = cb
+        # accuracy of the first, middle and last sampled query blocks of that head
+        pick = sorted({blocks[0], blocks[len(blocks) // 2], blocks[-1]})
+        line["accuracy"] = {"head": "query head 0 of " + ("the longest sequence" if varlen else "sequence 0"),
+                            "query_blocks": pick, **accuracy(o1, q1, k1, v1, w.causal, pick, pro)}
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)

@@ -25,9 +25,10 @@
  * [-7, 7] carried in int8 lanes) with one scale per MFMA lane group; QK^T runs on the
  * integer MFMA with exact int32 accumulation; an online softmax produces P~, which is
  * quantized to FP8 E4M3 with the static range P_r = 448; V is quantized per channel to
- * FP8 E4M3 with V_r = 448 [SA2pp key_machinery]; P~V runs on the FP8 MFMA, each KV block
- * into a zeroed block-local accumulator that is then folded into a global fp32
- * accumulator [SA2], [SA2c].  With pv_bits = 16 (the [BLOG] high-fidelity mode) V is not
+ * FP8 E4M3 with V_r = 448 [SA2pp key_machinery]; P~V runs on the FP8 MFMA with two-level
+ * accumulation [SA2], [SA2c]: each instruction sums its 64 products in the matrix unit (the
+ * narrow, block-local level) and adds them to the fp32 output accumulator it takes as its C
+ * operand (the global level).  With pv_bits = 16 (the [BLOG] high-fidelity mode) V is not
  * quantized: P and V enter the fp16 MFMA (fp32 accumulation) and only QK^T is quantized.
  *
  * Tensors (all device pointers, caller-owned, never freed or retained by the library):
@@ -205,6 +206,20 @@ int sage_qk_tile_debug(const void* q, const void* k, const void* v, int B, int H
                        int d, int causal, int qk_bits, int pv_bits, void* workspace,
                        size_t workspace_bytes, void* stream, int b, int h, int qb, int kb,
                        int32_t* tile_out);
+
+/*
+ * Measurement utility (not part of the method): enqueue a launch that keeps every SIMD's matrix
+ * unit busy with one dense MFMA instruction, register operands only, two waves per SIMD, so that
+ * timing it gives the sustained matrix rate at the clock the chip runs at.
+ *   kind  0: v_mfma_i32_32x32x32_i8 (INT8), 1: v_mfma_f32_32x32x64_f8f6f4 with FP8 E4M3,
+ *         2: the same with FP6 E2M3, 3: v_mfma_f32_32x32x16_f16
+ *   iters rounds of four independent accumulator chains per wave (>= 1)
+ *   sink  device buffer of at least 512 KiB; overwritten with the accumulator sums
+ *   *ops  (host) receives the number of multiply-add operations (x2) the launch performs
+ * Errors: SAGE_ERR_INVALID_ARG (kind, iters, null pointer), SAGE_ERR_WORKSPACE (sink too
+ * small), SAGE_ERR_HIP (launch failed).  Stream ordered; returns after enqueueing.
+ */
+int sage_mfma_rate_probe(int kind, int iters, void* sink, size_t sink_bytes, double* ops, void* stream);
 
 /* Static text for a status code. */
 const char* sage_status_string(int status);

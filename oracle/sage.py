@@ -563,3 +563,18 @@ def exact_attention(q, k, v, causal: bool = False) -> np.ndarray:
             e = np.exp(s)
             out[b, h] = (e / e.sum(axis=1, keepdims=True)) @ v[b, hk]
     return out
+
+
+def exact_attention_rows(q, k, v, rows, causal: bool = False) -> np.ndarray:
+    """softmax(Q K^T / sqrt(d)) V in fp64 for the query rows `rows` of one head: q [N, d], k/v
+    [N, d]; query i sees keys j <= i when causal.  Returns [len(rows), d]."""
+    rows = np.asarray(rows)
+    q = np.asarray(q).astype(F64)[rows]
+    k = np.asarray(k).astype(F64)
+    v = np.asarray(v).astype(F64)
+    s = q @ k.T / math.sqrt(q.shape[1])
+    if causal:
+        s = np.where(np.arange(k.shape[0])[None, :] > rows[:, None], -np.inf, s)
+    s = s - s.max(axis=1, keepdims=True)
+    e = np.exp(s)
+    return (e / e.sum(axis=1, keepdims=True)) @ v

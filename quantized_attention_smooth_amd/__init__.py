@@ -21,7 +21,7 @@ import os
 import torch
 
 __all__ = ["sageattn", "sageattn_varlen", "SageAttention", "QUANT_MODES", "fwd", "prologue", "attend", "workspace_bytes", "get_config",
-           "quant_debug", "qk_tile_debug", "Problem", "LIB_PATH", "SageError"]
+           "quant_debug", "qk_tile_debug", "Problem", "LIB_PATH", "SageError", "mfma_rate_probe", "MFMA_PROBE_KINDS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsage_mi355x.so")
 
@@ -35,7 +35,7 @@ SAGE_ERR_HIP = -4
 EXPORTS = ("sage_get_config", "sage_attn_workspace_bytes", "sage_attn_fwd", "sage_attn_prologue",
            "sage_attn_attend", "sage_quant_debug", "sage_qk_tile_debug", "sage_status_string",
            "sage_last_error", "sage_attn_workspace_bytes_ex", "sage_attn_fwd_ex", "sage_attn_prologue_ex",
-           "sage_attn_attend_ex", "sage_quant_debug_ex")
+           "sage_attn_attend_ex", "sage_quant_debug_ex", "sage_mfma_rate_probe")
 
 LAYOUTS = {"HND": 0, "NHD": 1}
 #: quant_mode names of the blog page's precision-control section (INT8 QK with FP8 or fp16 PV),
@@ -109,13 +109,15 @@ def _load() -> ctypes.CDLL:
     lib.sage_attn_prologue_ex.argtypes = [PP, P, P, P, P, S, P]
     lib.sage_attn_attend_ex.argtypes = [PP, P, P, S, P]
     lib.sage_quant_debug_ex.argtypes = [PP, P, P, P, P, S, P] + [P] * 9
+    lib.sage_mfma_rate_probe.argtypes = [I, I, P, S, ctypes.POINTER(ctypes.c_double), P]
     lib.sage_status_string.argtypes = [I]
     lib.sage_status_string.restype = ctypes.c_char_p
     lib.sage_last_error.argtypes = []
     lib.sage_last_error.restype = ctypes.c_char_p
     for name in ("sage_get_config", "sage_attn_workspace_bytes", "sage_attn_fwd", "sage_attn_prologue",
                  "sage_attn_attend", "sage_quant_debug", "sage_qk_tile_debug", "sage_attn_workspace_bytes_ex",
-                 "sage_attn_fwd_ex", "sage_attn_prologue_ex", "sage_attn_attend_ex", "sage_quant_debug_ex"):
+                 "sage_attn_fwd_ex", "sage_attn_prologue_ex", "sage_attn_attend_ex", "sage_quant_debug_ex",
+                 "sage_mfma_rate_probe"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -398,3 +400,18 @@ def qk_tile_debug(q, k, v, b: int, h: int, qb: int, kb: int, is_causal: bool = F
         _check(_lib.sage_qk_tile_debug(_ptr(q), _ptr(k), _ptr(v), B, H, Hkv, N, d, int(is_causal), qk_bits, pv_bits,
                                        _ptr(ws), ws.numel(), _stream(q.device), b, h, qb, kb, _ptr(tile)))
     return tile
+
+
+#: matrix instructions the rate probe can run (sage_mfma_rate_probe's kind)
+MFMA_PROBE_KINDS = {"int8": 0, "fp8": 1, "fp6": 2, "fp16": 3}
+
+
+def mfma_rate_probe(kind: str, iters: int, sink) -> float:
+    """Enqueue the library's matrix-unit rate probe on the current stream of sink's device (a
+    device tensor of at least 512 KiB, overwritten) and return the ops the launch performs; the
+    caller times it (a measurement utility, not part of the method)."""
+    ops = ctypes.c_double(0.0)
+    with _on(sink.device):
+        _check(_lib.sage_mfma_rate_probe(MFMA_PROBE_KINDS[kind], int(iters), _ptr(sink), sink.numel() * sink.element_size(),
+                                         ctypes.byref(ops), _stream(sink.device)))
+    return ops.value

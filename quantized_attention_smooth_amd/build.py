@@ -14,7 +14,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsage_mi355x.so")
-SOURCES = ["prologue.hip", "attention.hip", "api.hip"]
+SOURCES = ["prologue.hip", "attention.hip", "probe.hip", "api.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

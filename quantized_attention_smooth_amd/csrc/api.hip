@@ -293,4 +293,13 @@ const char* sage_status_string(int status) {
 
 const char* sage_last_error(void) { return g_last_error; }
 
+int sage_mfma_rate_probe(int kind, int iters, void* sink, size_t sink_bytes, double* ops, void* stream) {
+  if (kind < 0 || kind > 3 || iters < 1 || sink == nullptr || ops == nullptr) return SAGE_ERR_INVALID_ARG;
+  if (sink_bytes < sage::mfma_probe_sink_bytes()) return SAGE_ERR_WORKSPACE;
+  *ops = sage::mfma_probe_ops(kind, iters);
+  const hipError_t e = sage::launch_mfma_probe(kind, iters, static_cast<float*>(sink), static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "probe launch");
+  return SAGE_OK;
+}
+
 }  // extern "C"

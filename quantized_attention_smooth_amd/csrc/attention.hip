@@ -119,11 +119,11 @@ struct AttnArgs {
 
 // V stages: FP8 codes [64-key group][channel][64 slots], one per K stage; or fp16 V
 // [16-key group][channel][16 slots], one stage.  16-byte chunks swizzled in both.
-template <int D, bool PV16>
+template <int D, bool PV16, int NSTAGES = (!PV16 && D == 64) ? 3 : 2>
 struct Smem {
   // K (and FP8 V, Delta_S) stages: a ring of three at d = 64 in the FP8 mode, where a block's
   // arithmetic is short enough that a tile issued one block ahead can still be in flight
-  static constexpr int NST = (!PV16 && D == 64) ? 3 : 2;
+  static constexpr int NST = NSTAGES;
   static constexpr int VST = PV16 ? 1 : NST;
   __attribute__((aligned(16))) int8_t k[NST][BK * D];  // K tile rows, 16-byte chunks swizzled
   __attribute__((aligned(16))) uint8_t v[VST][BK * D * (PV16 ? 2 : 1)];
@@ -150,12 +150,15 @@ __device__ inline float s_to_float(int acc) {
 }
 
 // XOR swizzles of the 16-byte chunk index inside an LDS row.  Each operand read has 32 lanes
-// fetch 16 bytes from 32 consecutive rows at one logical chunk; the swizzles spread those rows
-// over distinct bank groups whether the LDS serves 8 lanes per cycle over 32 banks or 16 lanes
-// per cycle over 64 banks (the former swizzle, row & 7, left 2-way conflicts on gfx950).
+// fetch 16 bytes from 32 consecutive rows (an aligned group of 32) at one logical chunk; the
+// swizzles spread those rows over distinct bank groups whether the LDS serves 8 lanes per cycle
+// over 32 banks or 16 lanes per cycle over 64 banks (the plain swizzle row & 7 left 2-way
+// conflicts on gfx950).  None depends on the bits of the row above the 32-row group (row >> 5
+// at d = 128), so the tile-load offsets of one lane differ by exactly 4 KB from one load
+// instruction to the next and need a single register (see TileLoader).
 template <int D>
 __device__ inline int kswz(int row) {       // K rows: 128 bytes (d = 128) or 64 bytes (d = 64)
-  return D == 128 ? ((row ^ (row >> 3)) & 7) : (((row >> 1) ^ (row >> 3)) & 3);
+  return D == 128 ? ((row & 7) ^ ((row >> 3) & 3)) : (((row >> 1) ^ (row >> 3)) & 3);
 }
 __device__ inline int vswz(int c) {         // V^T rows: 64 bytes per channel
   return ((c >> 1) ^ (c >> 3)) & 3;
@@ -193,9 +196,10 @@ struct TileLoader {
   static constexpr int NK = kTileInstrs<D>;                 // K (and FP8 V) instructions per wave
   static constexpr int NV = kTileInstrs<D> * (PV16 ? 2 : 1);
   static constexpr int VB = PV16 ? 2 : 1;                   // V bytes per element
+  static constexpr int STEP = WAVES * 64 * 16;              // bytes per load instruction and workgroup
   const void *kp, *vp, *dp;
   uint32_t kbytes, vbytes, dbytes;
-  uint32_t koff[NK], voff[NV];
+  uint32_t koff, voff;   // this lane's offset for instruction m = 0; instruction m adds m * STEP
 
   // kc, vc: the head's K codes / V rows; dsrow: the Q block's Delta_S row of ds_len floats
   __device__ TileLoader(const int8_t* kc, const uint8_t* vc, const float* dsrow, int nkb, int ds_len, int w,
@@ -203,28 +207,24 @@ struct TileLoader {
     kp = kc; kbytes = (uint32_t)nkb * BK * D;
     vp = vc; vbytes = (uint32_t)nkb * BK * D * VB;
     dp = dsrow; dbytes = (uint32_t)ds_len * 4;
+    // 16-byte chunk p of the tile in LDS (instruction m, wave w, lane) holds the global chunk of
+    // row p / (chunks per row) at swizzled position: the LDS side of a load is linear in the lane
     constexpr int CPR = D / 16;                             // 16-byte chunks per K row
-#pragma unroll
-    for (int m = 0; m < NK; ++m) {
-      const int p = (m * WAVES + w) * 64 + lane;            // 16-byte chunk index in LDS
-      const int row = p / CPR, pc = p % CPR;
-      koff[m] = (uint32_t)(row * D + ((pc ^ kswz<D>(row)) * 16));
-    }
+    const int p = w * 64 + lane;
+    const int row = p / CPR, pc = p % CPR;
+    koff = (uint32_t)(row * D + ((pc ^ kswz<D>(row)) * 16));
     constexpr int RB = PV16 ? 32 : VGROUP;                  // bytes per V LDS row (group, channel)
     constexpr int CR = RB / 16;
-#pragma unroll
-    for (int m = 0; m < NV; ++m) {
-      const int p = (m * WAVES + w) * 64 + lane;
-      const int row = p / CR, pc = p % CR;                  // row = group * D + channel
-      const int sw = PV16 ? v16swz(row % D) : vswz(row % D);
-      voff[m] = (uint32_t)(row * RB + ((pc ^ sw) * 16));
-    }
+    const int vrow = p / CR, vpc = p % CR;                  // vrow = group * D + channel
+    const int sw = PV16 ? v16swz(vrow % D) : vswz(vrow % D);
+    voff = (uint32_t)(vrow * RB + ((vpc ^ sw) * 16));
   }
 
   // K codes of block kb and its Delta_S row slice into stage st (each wave a quarter of the
   // slice, so every wave issues the same number of loads per block).  The Delta_S load goes
   // first, so a wait for "all but the last kTileInstrs" loads leaves only K chunks outstanding.
-  __device__ void issue_k(Smem<D, PV16>& sm, int st, int kb, int w, int lane) const {
+  template <class SM>
+  __device__ void issue_k(SM& sm, int st, int kb, int w, int lane) const {
 #if defined(__HIP_DEVICE_COMPILE__)
     if (lane < BK / 4 / WAVES)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(dp, dbytes), (lds_void*)(sm.ds[st] + w * (BK / WAVES)), 16,
@@ -232,20 +232,21 @@ struct TileLoader {
     const auto kr = make_rsrc(kp, kbytes);
 #pragma unroll
     for (int m = 0; m < NK; ++m)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(sm.k[st] + (m * WAVES + w) * 1024), 16, koff[m],
-                                               kb * BK * D, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(sm.k[st] + (m * WAVES + w) * 1024), 16, koff,
+                                               kb * BK * D + m * STEP, 0, 0);
 #endif
   }
 
   // V of block kb into stage st: FP8 codes (64-byte rows) or 16-bit V (32-byte rows, twice the
   // instructions).
-  __device__ void issue_v(Smem<D, PV16>& sm, int st, int kb, int w) const {
+  template <class SM>
+  __device__ void issue_v(SM& sm, int st, int kb, int w) const {
 #if defined(__HIP_DEVICE_COMPILE__)
     const auto vr = make_rsrc(vp, vbytes);
 #pragma unroll
     for (int m = 0; m < NV; ++m)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(sm.v[st] + (m * WAVES + w) * 1024), 16, voff[m],
-                                               kb * BK * D * VB, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(sm.v[st] + (m * WAVES + w) * 1024), 16, voff,
+                                               kb * BK * D * VB + m * STEP, 0, 0);
 #endif
   }
 };
@@ -272,8 +273,8 @@ __device__ inline void wait_all_but_k_tile() {
 // (stored as FP6 E2M3, 24 bytes of each 32-byte slot): v_mfma_f32_32x32x64_f8f6f4 in FP6 mode from
 // zero, one slot per lane per k-step, at twice the INT8 rate; the products and sums of integers
 // this small are exact in its accumulator, so S arrives as fp32.
-template <int D, bool QK4, bool PV16>
-__device__ inline void qk_tiles(const Smem<D, PV16>& sm, int st, const v4i (&qreg)[D / 32], int col, int half,
+template <int D, bool QK4, class SM>
+__device__ inline void qk_tiles(const SM& sm, int st, const v4i (&qreg)[D / 32], int col, int half,
                                 v16i (&sacc)[BK / 32]) {
 #pragma unroll
   for (int t = 0; t < BK / 32; ++t) {
@@ -361,7 +362,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
     wait_loads();
     __syncthreads();
     v16i sacc[BK / 32];
-    qk_tiles<D, QK4, PV16>(sm, 0, qreg, col, half, sacc);
+    qk_tiles<D, QK4>(sm, 0, qreg, col, half, sacc);
 #pragma unroll
     for (int t = 0; t < BK / 32; ++t)
 #pragma unroll
@@ -409,7 +410,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
     }
 
     v16i sacc[BK / 32];
-    qk_tiles<D, QK4, PV16>(sm, st, qreg, col, half, sacc);
+    qk_tiles<D, QK4>(sm, st, qreg, col, half, sacc);
 
     // dequantize and add the Q-smoothing bias, in the log2 domain
     // both lane halves' delta_K through one wave-uniform (scalar) load, so that waiting for it
@@ -602,8 +603,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
     st = st + 1 == NST ? 0 : st + 1;
   };
 
-  // the last block needs masking when causal (diagonal block) or when N is not a multiple of BK
-  const bool mask_last = CAUSAL || (N % BK) != 0;
+  // the last block needs masking when causal (the diagonal block); keys past N carry a Delta_S
+  // of -inf, so a ragged tail needs none
+  constexpr bool mask_last = CAUSAL;
   const int nfull = mask_last ? nblk - 1 : nblk;
   for (int kb = 0; kb < nfull; ++kb) block(kb, std::false_type{});
   if (mask_last) block(nblk - 1, std::true_type{});

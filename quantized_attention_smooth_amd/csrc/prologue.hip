@@ -809,7 +809,10 @@ __global__ __launch_bounds__(256) void delta_s(const T* __restrict__ k, const fl
         for (int t = 0; t < 2; ++t) {
           const int j = j0 + 32 * t + r;
           const bool ok = qb < nqb && (!CAUSAL || (j >> 7) <= qb);
-          store_or_drop(dsr, span, ok ? (rel + (uint32_t)j) * 4u : kDropOffset, acc[u][t][4 * a4 + e] * k2);
+          // keys past the sequence (the zero-padded tail of its last block) get -inf: the
+          // attention kernel adds Delta_S to the logits, so they drop out without a mask
+          store_or_drop(dsr, span, ok ? (rel + (uint32_t)j) * 4u : kDropOffset,
+                        j < N ? acc[u][t][4 * a4 + e] * k2 : -INFINITY);
         }
       }
   }

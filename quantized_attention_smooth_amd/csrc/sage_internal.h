@@ -80,7 +80,8 @@ struct Dims {
 //  ds     : fp32  per (s, h), from element ds0 of s: the rows of Delta_S * log2(e) / sqrt(d),
 //           one per Q block.  Non-causal: nb_s rows of Npad_s keys.  Causal: row qb holds only
 //           the keys a causal Q block can see, j < (qb + 1) * 128, packed back to back
-//           (ds_row_offset).  Entries past n are zero.
+//           (ds_row_offset).  Entries past n are -inf, so padded keys drop out of the softmax
+//           without a mask.
 //  seqs   : Seq [B]                           varlen only: the sequence table
 // Delta_S storage: elements per (b, h) and the offset of Q block qb's row inside it.
 __host__ __device__ inline size_t ds_head_elems(bool causal, int nqb, int Npad) {
@@ -240,6 +241,10 @@ hipError_t launch_prologue(const Dims& D, const Ptrs& P, hipStream_t s);
 hipError_t launch_attention(const Dims& D, const Ptrs& P, hipStream_t s);
 hipError_t launch_qk_tile(const Dims& D, const Ptrs& P, int b, int h, int qb, int kb, int32_t* out,
                           hipStream_t s);
+// matrix-unit rate probe: ops per launch, sink size, launch (kind 0 INT8, 1 FP8, 2 FP6, 3 fp16)
+double mfma_probe_ops(int kind, int iters);
+size_t mfma_probe_sink_bytes();
+hipError_t launch_mfma_probe(int kind, int iters, float* sink, hipStream_t s);
 hipError_t launch_debug_copy(const Dims& D, const Ptrs& P, hipStream_t s, float* mu_k, int8_t* k_codes,
                              float* k_scales, uint8_t* v_codes, float* v_scales, float* mu_q,
                              int8_t* q_codes, float* q_scales, float* delta_s);

@@ -79,6 +79,12 @@ hipError_t launch_debug_copy(const Dims&, const Ptrs&, hipStream_t, float*, int8
                              float*, int8_t*, float*, float*) {
   return hipSuccess;
 }
+double mfma_probe_ops(int, int iters) { return 1.0 * iters; }
+size_t mfma_probe_sink_bytes() { return 512 * 1024; }
+hipError_t launch_mfma_probe(int, int, float* sink, hipStream_t) {
+  touch(sink, mfma_probe_sink_bytes());
+  return hipSuccess;
+}
 }  // namespace sage
 
 namespace {
@@ -165,6 +171,16 @@ int main() {
     sage_problem_t p = fixed(2, 1, 1, 0, 64, 0, 8, 8, SAGE_LAYOUT_HND, SAGE_DTYPE_FP16);
     p.cu_seqlens = cu;
     CHECK(sage_attn_workspace_bytes_ex(&p, &n) != SAGE_OK);
+  }
+  // the rate probe's argument checks, and a call on a sink of exactly the minimum size
+  {
+    double ops = 0;
+    std::vector<unsigned char> sink(512 * 1024);
+    CHECK(sage_mfma_rate_probe(4, 10, sink.data(), sink.size(), &ops, nullptr) == SAGE_ERR_INVALID_ARG);
+    CHECK(sage_mfma_rate_probe(0, 0, sink.data(), sink.size(), &ops, nullptr) == SAGE_ERR_INVALID_ARG);
+    CHECK(sage_mfma_rate_probe(0, 10, nullptr, sink.size(), &ops, nullptr) == SAGE_ERR_INVALID_ARG);
+    CHECK(sage_mfma_rate_probe(0, 10, sink.data(), sink.size() - 1, &ops, nullptr) == SAGE_ERR_WORKSPACE);
+    CHECK(sage_mfma_rate_probe(1, 10, sink.data(), sink.size(), &ops, nullptr) == SAGE_OK && ops == 10.0);
   }
   if (g_fail) return 1;
   printf("ok\n");

@@ -48,6 +48,14 @@ def test_exact_attention_matches_torch_sdpa(causal):
     assert np.abs(e - t).max() < 1e-12
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_exact_attention_rows_is_a_row_slice(causal):
+    q, k, v = make_inputs(custom(1, 1, 1, 300, 32, q_bias_std=1.0), seed=22)
+    e = sage.exact_attention(q, k, v, causal)[0, 0]
+    rows = np.array([0, 1, 127, 128, 200, 299])
+    assert np.abs(sage.exact_attention_rows(q[0, 0], k[0, 0], v[0, 0], rows, causal) - e[rows]).max() < 1e-13
+
+
 def test_unquantized_ragged_close_to_exact():
     q, k, v = make_inputs(custom(2, 2, 1, 301, 64, q_bias_std=1.0), seed=11)
     for causal in (False, True):

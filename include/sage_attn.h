@@ -208,6 +208,28 @@ int sage_qk_tile_debug(const void* q, const void* k, const void* v, int B, int H
                        int32_t* tile_out);
 
 /*
+ * Allocation-free forward pass, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): sage_attn_fwd_ex for a
+ * fixed-length problem (p->cu_seqlens must be NULL), with the workspace taken from a device
+ * array inside the library instead of the caller.
+ *   The array holds 128 MiB (134217728 bytes) on every GPU the library runs on, from the first
+ *   call on that GPU until the process ends; problems whose sage_attn_workspace_bytes_ex exceeds
+ *   it return SAGE_ERR_WORKSPACE (sage_last_error() states both sizes) before anything is
+ *   enqueued.  Example: B1 H16 N8192 d128 non-causal needs about 85 MB.
+ *   The current device must be the device of q, k, v, o and stream (a stream on another device
+ *   returns SAGE_ERR_INVALID_ARG); its copy of the array is used.
+ *   Every call on one GPU shares that GPU's array, and the library makes no synchronisation:
+ *   calls on one GPU whose executions overlap (different streams, or host threads racing on one
+ *   stream) race on it and give meaningless output.  Calls ordered on one stream are safe.  The
+ *   array keeps the last call's contents; each call re-initialises what it reads.
+ *   No hipMalloc, hipFree or other allocating call is made; the first call on a device looks up
+ *   the array's device address (hipGetSymbolAddress) and keeps it.
+ * Errors as for sage_attn_fwd_ex.
+ */
+int sage_attn_fwd_noalloc(const sage_problem_t* p, const void* q, const void* k, const void* v, void* o,
+                          void* stream);
+
+/*
  * Measurement utility (not part of the method): enqueue a launch that keeps every SIMD's matrix
  * unit busy with one dense MFMA instruction, register operands only, two waves per SIMD, so that
  * timing it gives the sustained matrix rate at the clock the chip runs at.

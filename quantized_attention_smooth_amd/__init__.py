@@ -35,7 +35,8 @@ SAGE_ERR_HIP = -4
 EXPORTS = ("sage_get_config", "sage_attn_workspace_bytes", "sage_attn_fwd", "sage_attn_prologue",
            "sage_attn_attend", "sage_quant_debug", "sage_qk_tile_debug", "sage_status_string",
            "sage_last_error", "sage_attn_workspace_bytes_ex", "sage_attn_fwd_ex", "sage_attn_prologue_ex",
-           "sage_attn_attend_ex", "sage_quant_debug_ex", "sage_mfma_rate_probe")
+           "sage_attn_attend_ex", "sage_quant_debug_ex", "sage_mfma_rate_probe",
+           "sage_attn_fwd_noalloc")
 
 LAYOUTS = {"HND": 0, "NHD": 1}
 #: quant_mode names of the blog page's precision-control section (INT8 QK with FP8 or fp16 PV),
@@ -110,6 +111,7 @@ def _load() -> ctypes.CDLL:
     lib.sage_attn_attend_ex.argtypes = [PP, P, P, S, P]
     lib.sage_quant_debug_ex.argtypes = [PP, P, P, P, P, S, P] + [P] * 9
     lib.sage_mfma_rate_probe.argtypes = [I, I, P, S, ctypes.POINTER(ctypes.c_double), P]
+    lib.sage_attn_fwd_noalloc.argtypes = [PP, P, P, P, P, P]
     lib.sage_status_string.argtypes = [I]
     lib.sage_status_string.restype = ctypes.c_char_p
     lib.sage_last_error.argtypes = []
@@ -117,7 +119,7 @@ def _load() -> ctypes.CDLL:
     for name in ("sage_get_config", "sage_attn_workspace_bytes", "sage_attn_fwd", "sage_attn_prologue",
                  "sage_attn_attend", "sage_quant_debug", "sage_qk_tile_debug", "sage_attn_workspace_bytes_ex",
                  "sage_attn_fwd_ex", "sage_attn_prologue_ex", "sage_attn_attend_ex", "sage_quant_debug_ex",
-                 "sage_mfma_rate_probe"):
+                 "sage_mfma_rate_probe", "sage_attn_fwd_noalloc"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
 

@@ -7,10 +7,18 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <vector>
 
 #include "../../include/sage_attn.h"
 #include "sage_internal.h"
+
+// Workspace of sage_attn_fwd_noalloc: a file-scope device array, one copy on every GPU the library
+// runs on, held until the process ends.  In host code `scratch` is only a stand-in for the symbol:
+// its device address comes from hipGetSymbolAddress (per device, cached below) and only that
+// address is ever passed to kernels.
+constexpr size_t kScratchBytes = (size_t)128 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace {
 
@@ -149,9 +157,69 @@ int run(const sage_problem_t* p, const void* q, const void* k, const void* v, vo
   return SAGE_OK;
 }
 
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};      // device address of `scratch` on each device ordinal
+
+// The device address of `scratch` on the current device, looked up once per device.
+int scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) {
+    snprintf(g_last_error, sizeof(g_last_error), "device ordinal %d beyond the %d the library tracks", dev, kMaxDevices);
+    return SAGE_ERR_HIP;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_dev[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (ptr == nullptr || reinterpret_cast<uintptr_t>(ptr) % sage::WS_ALIGN != 0) {
+      snprintf(g_last_error, sizeof(g_last_error), "scratch symbol address %p is not 256-byte aligned", ptr);
+      return SAGE_ERR_HIP;
+    }
+    g_scratch_dev[dev] = ptr;
+  }
+  *out = g_scratch_dev[dev];
+  return SAGE_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int sage_attn_fwd_noalloc(const sage_problem_t* p, const void* q, const void* k, const void* v, void* o,
+                          void* stream) {
+  if (!q || !k || !v || !o || p == nullptr) return SAGE_ERR_INVALID_ARG;
+  if (p->cu_seqlens != nullptr) return SAGE_ERR_INVALID_ARG;      // fixed-length problems only
+  sage::Dims D;
+  int st = check_problem(p, &D, nullptr);
+  if (st != SAGE_OK) return st;
+  const size_t need = sage::make_layout(D).total;
+  if (need > kScratchBytes) {
+    snprintf(g_last_error, sizeof(g_last_error),
+             "problem needs %zu bytes of workspace; the allocation-free entry point has %zu", need, kScratchBytes);
+    return SAGE_ERR_WORKSPACE;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (s != nullptr) {                      // the scratch copy used is the current device's
+    int cur = -1, sdev = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    e = hipStreamGetDevice(s, &sdev);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamGetDevice");
+    if (sdev != cur) {
+      snprintf(g_last_error, sizeof(g_last_error), "stream is on device %d but device %d is current", sdev, cur);
+      return SAGE_ERR_INVALID_ARG;
+    }
+  }
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != SAGE_OK) return st;
+  return run(p, q, k, v, o, ws, kScratchBytes, stream, kBoth);
+}
+
 
 int sage_get_config(sage_config_t* out) {
   if (out == nullptr) return SAGE_ERR_INVALID_ARG;

@@ -229,7 +229,8 @@ def test_valid_call_without_a_device_reports_hip_error(pkg):
 
 def test_host_code_under_address_and_undefined_behavior_sanitizers(tmp_path):
     """The library's host code (csrc/api.hip: validation, workspace carve-up, varlen table) built
-    with AddressSanitizer and UndefinedBehaviorSanitizer, host side only, and driven by
+    with AddressSanitizer and UndefinedBehaviorSanitizer on the host side (the device side of
+    that file is only the allocation-free entry point's array) and driven by
     tests/abi_host_check.cpp with stand-in launchers that fill every workspace section and the
     output in host memory (sections tagged, so overlaps show too)."""
     import shutil
@@ -240,7 +241,7 @@ def test_host_code_under_address_and_undefined_behavior_sanitizers(tmp_path):
     exe = str(tmp_path / "abi_host_check")
     san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
            "-Xarch_host", "-fno-sanitize-recover=all"]
-    cmd = [hipcc, "-x", "hip", "--offload-host-only", "-std=c++17", "-O1", "-g", *san,
+    cmd = [hipcc, "-x", "hip", "--offload-arch=gfx950", "-std=c++17", "-O1", "-g", *san,
            os.path.join(ROOT, "quantized_attention_smooth_amd", "csrc", "api.hip"),
            os.path.join(ROOT, "tests", "abi_host_check.cpp"), "-o", exe]
     b = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
@@ -248,3 +249,28 @@ def test_host_code_under_address_and_undefined_behavior_sanitizers(tmp_path):
     env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:halt_on_error=1", UBSAN_OPTIONS="halt_on_error=1")
     r = subprocess.run([exe], capture_output=True, text=True, timeout=600, env=env)
     assert r.returncode == 0 and r.stdout.strip() == "ok", r.stdout + r.stderr
+
+
+def test_noalloc_entry_point_checks(pkg):
+    """The allocation-free entry point: fixed-length problems only, and problems whose workspace
+    exceeds its 128 MiB array are refused with SAGE_ERR_WORKSPACE before any HIP call."""
+    lib = pkg._lib
+    fake = ctypes.c_void_p(0x10000000)
+    big = pkg.Problem(1, 32, 8, 98304, 128, True, 8, 8, "HND")            # about 5.5 GB of workspace
+    assert lib.sage_attn_fwd_noalloc(big.ref, fake, fake, fake, fake, None) == -3
+    msg = lib.sage_last_error().decode()
+    assert "134217728" in msg and "allocation-free" in msg
+    var = pkg.Problem(2, 4, 2, 0, 64, True, 8, 8, "HND", cu_seqlens=[0, 5, 9])
+    assert lib.sage_attn_fwd_noalloc(var.ref, fake, fake, fake, fake, None) == -1
+    ok = pkg.Problem(1, 2, 2, 256, 64, False, 8, 8, "HND")
+    assert lib.sage_attn_fwd_noalloc(ok.ref, None, fake, fake, fake, None) == -1
+    assert lib.sage_attn_fwd_noalloc(None, fake, fake, fake, fake, None) == -1
+    bad = pkg.Problem(1, 2, 2, 256, 96, False, 8, 8, "HND")
+    assert lib.sage_attn_fwd_noalloc(bad.ref, fake, fake, fake, fake, None) == -2
+    # the benchmark's shape fits
+    n = ctypes.c_size_t(0)
+    bench = pkg.Problem(1, 16, 16, 8192, 128, False, 8, 8, "HND")
+    assert lib.sage_attn_workspace_bytes_ex(bench.ref, ctypes.byref(n)) == 0 and n.value <= 128 << 20
+    if _hip_device_count() == 0:            # no GPU: a valid call fails at the device lookup
+        assert lib.sage_attn_fwd_noalloc(ok.ref, fake, fake, fake, fake, None) == -4
+        assert len(lib.sage_last_error()) > 0

@@ -149,21 +149,45 @@ def environment() -> dict:
         pass
     env["cpu_model"] = cpu
     env["cpu_cores_affinity"] = len(os.sched_getaffinity(0))
-    # the GPU's clock as its management tool reports it right after the timed region (best effort)
-    clocks = None
-    for cmd in (["amd-smi", "metric", "-g", "0", "-c", "--json"], ["rocm-smi", "--showclocks", "--json"]):
-        try:
-            r = subprocess.run(cmd, capture_output=True, text=True, timeout=20)
-        except (OSError, subprocess.TimeoutExpired):
-            continue
-        if r.returncode == 0 and r.stdout.strip():
-            try:
-                clocks = json.loads(r.stdout)
-            except ValueError:
-                clocks = r.stdout.strip()[:2000]
-            break
-    env["clocks_after_run"] = clocks
     return env
+
+
+def smi_clocks() -> dict | None:
+    """The GPU's current graphics clocks (MHz, one per XCD) as its management tool reports them
+    (best effort: None when the tool is missing or fails)."""
+    import subprocess
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-g", "0", "-c", "--json"], capture_output=True, text=True,
+                           timeout=30)
+        if r.returncode != 0:
+            return None
+        d = json.loads(r.stdout)
+        d = d["gpu_data"][0] if isinstance(d, dict) and "gpu_data" in d else (d[0] if isinstance(d, list) else d)
+        clk = d["clock"]
+        vals = [v["clk"]["value"] for k, v in clk.items() if k.startswith("gfx") and isinstance(v, dict)]
+        mx = [v["max_clk"]["value"] for k, v in clk.items() if k.startswith("gfx") and isinstance(v, dict)]
+        return {"gfx_mhz": vals, "gfx_max_mhz": max(mx) if mx else None}
+    except Exception:  # pragma: no cover - reporting only
+        return None
+
+
+def clocks_under_load(step, seconds: float = 4.0) -> dict | None:
+    """Graphics clocks sampled while the step runs back to back (untimed): the management tool
+    runs in a thread while this thread keeps the GPU busy."""
+    import threading
+
+    import torch
+    box = {}
+    th = threading.Thread(target=lambda: box.setdefault("c", smi_clocks()))
+    t0 = time.perf_counter()
+    step()
+    th.start()
+    while th.is_alive() and time.perf_counter() - t0 < seconds + 30:
+        for _ in range(8):
+            step()
+        torch.cuda.synchronize()
+    th.join()
+    return box.get("c")
 
 
 def measured_peaks(dev, qk_bits: int, pv_bits: int, iters: int = 6000, reps: int = 3) -> dict:
@@ -373,6 +397,8 @@ def main() -> int:
                       "wall_s_timed": wall},
     }
     line["environment"] = environment()
+    line["environment"]["gpu_clocks_under_load"] = clocks_under_load(step)
+    line["environment"]["gpu_clocks_idle_after"] = smi_clocks()
     if not args.no_cpu_baseline:
         if varlen:                      # one head of the longest sequence
             s = int(np.argmax(w.lens))

@@ -7,14 +7,18 @@ bench.py ...` pass (its run_counter_collection.csv).  Counter values are average
 of each kernel of the library; every pass of one workload is merged into one table, and the
 derived figures below are printed when their counters are present:
 
-  MFMA busy   SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE * SIMDs): the share of the SIMDs'
-              cycles the matrix unit was busy during the dispatch (GRBM_GUI_ACTIVE counts the
-              cycles of the dispatch on one XCD, the busy cycles are summed over all SIMDs)
-  VALU busy   SQ_ACTIVE_INST_VALU * 4 / (GRBM_GUI_ACTIVE * SIMDs) -- wave-cycles the SQ reports
-              in quad cycles, one issuing wave per SIMD at a time
-  waits       SQ_WAIT_INST_ANY, SQ_WAIT_INST_LDS (quad cycles) as shares of SQ_WAVE_CYCLES
+  cycles      GRBM_GUI_ACTIVE / 8: the dispatch's length in GPU clocks (the counter is summed over
+              the 8 XCDs); with the dispatch's duration from the trace timestamps, the clock
+  MFMA busy   SQ_VALU_MFMA_BUSY_CYCLES / (cycles * 1024 SIMDs): the share of the SIMDs' cycles
+              the matrix unit was busy (the counter sums its busy cycles over all SIMDs)
+  VALU busy   SQ_ACTIVE_INST_VALU * 4 / (cycles * 1024): wave-cycles spent issuing vector
+              instructions (reported in quad cycles, summed over waves) per SIMD cycle
+  co-exec     SQ_VALU_MFMA_COEXEC_CYCLES / SQ_VALU_MFMA_BUSY_CYCLES: share of matrix-busy cycles
+              in which a vector instruction was issued as well
+  waits       SQ_WAIT_INST_ANY, SQ_WAIT_INST_LDS, SQ_ACTIVE_INST_* as shares of SQ_WAVE_CYCLES
+              (all in quad cycles)
   LDS bank conflict cycles per LDS instruction; TCC hit rate
-  MFMA ops    SQ_INSTS_VALU_MFMA_MOPS_{I8,F8} * 512 (the counters count 512-op units)
+  MFMA ops    SQ_INSTS_VALU_MFMA_MOPS_{I8,F8,F6F4} * 512 (the counters count 512-op units)
 """
 from __future__ import annotations
 
@@ -24,6 +28,7 @@ import os
 import sys
 
 SIMDS = 1024          # 256 CUs x 4 SIMDs
+XCDS = 8
 SHORT = {"attn_fwd": "attn_fwd", "stats_and_q": "stats_and_q", "kv_quant": "kv_quant", "delta_s": "delta_s",
          "init_stats": "init_stats"}
 
@@ -38,6 +43,7 @@ def _kernel(name: str) -> str | None:
 def load(dirs):
     """{kernel: {counter: mean value per dispatch}} over every run_counter_collection.csv."""
     per = collections.defaultdict(lambda: collections.defaultdict(dict))   # kernel -> counter -> dispatch -> v
+    dur = collections.defaultdict(dict)                                      # kernel -> dispatch -> ns
     for d in dirs:
         f = os.path.join(d, "run_counter_collection.csv")
         for r in csv.DictReader(open(f)):
@@ -45,26 +51,36 @@ def load(dirs):
             if k is None:
                 continue
             per[k][r["Counter_Name"]][(d, r["Dispatch_Id"])] = float(r["Counter_Value"])
+            dur[k][(d, r["Dispatch_Id"])] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
     out = {}
     for k, cs in per.items():
         out[k] = {c: sum(v.values()) / len(v) for c, v in cs.items()}
         out[k]["_dispatches"] = max(len(v) for v in cs.values())
+        out[k]["_duration_ns"] = sum(dur[k].values()) / len(dur[k])
     return out
 
 
 def derived(c: dict) -> dict:
     g = c.get
     d = {}
-    if g("GRBM_GUI_ACTIVE"):
-        cyc = g("GRBM_GUI_ACTIVE")
+    cyc = g("GRBM_GUI_ACTIVE") / XCDS if g("GRBM_GUI_ACTIVE") else None
+    if cyc:
+        d["dispatch cycles (per XCD)"] = cyc
+        if g("_duration_ns"):
+            d["clock during the dispatch, GHz"] = cyc / g("_duration_ns")
         if g("SQ_VALU_MFMA_BUSY_CYCLES") is not None:
             d["MFMA busy (of SIMD cycles)"] = g("SQ_VALU_MFMA_BUSY_CYCLES") / (cyc * SIMDS)
         if g("SQ_ACTIVE_INST_VALU") is not None:
-            d["VALU issue busy (of SIMD cycles)"] = 4 * g("SQ_ACTIVE_INST_VALU") / (cyc * SIMDS)
+            d["VALU issue (wave-cycles per SIMD cycle)"] = 4 * g("SQ_ACTIVE_INST_VALU") / (cyc * SIMDS)
+        if g("SQ_ACTIVE_INST_VALU2") is not None:
+            d["dual VALU issue (of SIMD cycles)"] = 4 * g("SQ_ACTIVE_INST_VALU2") / (cyc * SIMDS)
+    if g("SQ_VALU_MFMA_COEXEC_CYCLES") is not None and g("SQ_VALU_MFMA_BUSY_CYCLES"):
+        d["co-exec (of MFMA-busy cycles)"] = g("SQ_VALU_MFMA_COEXEC_CYCLES") / g("SQ_VALU_MFMA_BUSY_CYCLES")
     if g("SQ_WAVE_CYCLES"):
-        for key in ("SQ_WAIT_INST_ANY", "SQ_WAIT_INST_LDS", "SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_LDS"):
+        for key in ("SQ_WAIT_INST_ANY", "SQ_WAIT_INST_LDS", "SQ_WAIT_ANY", "SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_LDS",
+                    "SQ_ACTIVE_INST_VALU"):
             if g(key) is not None:
-                d[f"{key} (of wave cycles)"] = 4 * g(key) / g("SQ_WAVE_CYCLES")
+                d[f"{key} (of wave cycles)"] = g(key) / g("SQ_WAVE_CYCLES")
     if g("SQ_INSTS_LDS") and g("SQ_LDS_BANK_CONFLICT") is not None:
         d["LDS bank-conflict cycles per LDS instruction"] = g("SQ_LDS_BANK_CONFLICT") / g("SQ_INSTS_LDS")
     if g("TCC_HIT_sum") is not None and g("TCC_MISS_sum") is not None and g("TCC_HIT_sum") + g("TCC_MISS_sum") > 0:
@@ -75,7 +91,7 @@ def derived(c: dict) -> dict:
             d["MFMA instructions per wave"] = g("SQ_INSTS_MFMA") / g("SQ_WAVES")
         if g("SQ_INSTS_LDS") is not None:
             d["LDS instructions per wave"] = g("SQ_INSTS_LDS") / g("SQ_WAVES")
-    for t in ("I8", "F8"):
+    for t in ("I8", "F8", "F6F4"):
         if g(f"SQ_INSTS_VALU_MFMA_MOPS_{t}") is not None:
             d[f"MFMA {t} ops"] = 512 * g(f"SQ_INSTS_VALU_MFMA_MOPS_{t}")
     return d
@@ -91,6 +107,7 @@ def table(dirs, kernels=("attn_fwd", "stats_and_q", "kv_quant", "delta_s")) -> s
         lines.append(f"### {k} ({int(c['_dispatches'])} dispatches averaged)\n")
         lines.append("| counter | per dispatch |")
         lines.append("|---|---|")
+        lines.append(f"| (mean dispatch duration, us) | {c['_duration_ns'] / 1e3:.1f} |")
         for name in sorted(x for x in c if not x.startswith("_")):
             lines.append(f"| {name} | {c[name]:.6g} |")
         for name, v in derived(c).items():

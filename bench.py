@@ -152,10 +152,18 @@ def environment() -> dict:
     return env
 
 
+def under_profiler() -> bool:
+    """True inside a rocprofv3 run: its tool library is preloaded into every child process too,
+    so no other program is started from here then."""
+    return "ROCPROF_OUTPUT_PATH" in os.environ or "rocprofiler" in os.environ.get("LD_PRELOAD", "")
+
+
 def smi_clocks() -> dict | None:
     """The GPU's current graphics clocks (MHz, one per XCD) as its management tool reports them
-    (best effort: None when the tool is missing or fails)."""
+    (best effort: None when the tool is missing or fails, or under the profiler)."""
     import subprocess
+    if under_profiler():
+        return None
     try:
         r = subprocess.run(["amd-smi", "metric", "-g", "0", "-c", "--json"], capture_output=True, text=True,
                            timeout=30)
@@ -177,6 +185,8 @@ def clocks_under_load(step, seconds: float = 4.0) -> dict | None:
     import threading
 
     import torch
+    if under_profiler():
+        return None
     box = {}
     th = threading.Thread(target=lambda: box.setdefault("c", smi_clocks()))
     t0 = time.perf_counter()

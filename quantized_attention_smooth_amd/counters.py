@@ -1,6 +1,9 @@
-"""Summaries of rocprofv3 counter runs of this library's kernels (measurement tooling).
+"""Summaries of rocprofv3 runs of this library's kernels (measurement tooling).
 
-    python -m quantized_attention_smooth_amd.counters DIR [DIR ...]
+    python -m quantized_attention_smooth_amd.counters DIR [DIR ...]        counter table
+    python -m quantized_attention_smooth_amd.counters --trace DIR           kernel-trace table
+    python -m quantized_attention_smooth_amd.counters --traffic CALIB_FETCH_DIR CALIB_WRITE_DIR \
+        NAME=FETCH_DIR,WRITE_DIR [...]                                         HBM traffic (JSON)
 
 Each DIR is the output directory of one `rocprofv3 --pmc ... -f csv -d DIR -o run -- python3
 bench.py ...` pass (its run_counter_collection.csv).  Counter values are averaged per dispatch
@@ -116,5 +119,65 @@ def table(dirs, kernels=("attn_fwd", "stats_and_q", "kv_quant", "delta_s")) -> s
     return "\n".join(lines)
 
 
+def trace_table(d: str) -> str:
+    """The --kernel-trace --stats summary (run_kernel_stats.csv) as a markdown table, times in us."""
+    rows = list(csv.DictReader(open(os.path.join(d, "run_kernel_stats.csv"))))
+    out = ["| kernel | calls | avg us | min us | max us | % of GPU time |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        name = r["Name"].replace("void ", "").replace("sage::(anonymous namespace)::", "").split("(")[0]
+        if _kernel(name) is None and "mfma_probe" not in name:
+            continue
+        out.append(f"| {name} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
+                   f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f} |")
+    return "\n".join(out)
+
+
+def _counter_mean(d: str, counter: str, kernel: str | None) -> tuple[float, int]:
+    vals = []
+    for r in csv.DictReader(open(os.path.join(d, "run_counter_collection.csv"))):
+        if r["Counter_Name"] != counter:
+            continue
+        if kernel is None:
+            if "copyBuffer" not in r["Kernel_Name"] and "elementwise" not in r["Kernel_Name"]:
+                continue
+        elif _kernel(r["Kernel_Name"]) != kernel:
+            continue
+        vals.append(float(r["Counter_Value"]))
+    return (sum(vals) / len(vals) if vals else float("nan")), len(vals)
+
+
+def traffic(calib_fetch: str, calib_write: str, runs: dict, copy_bytes: int = 1 << 30) -> dict:
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of every library kernel, scaled by what the same
+    counters read for a plain device copy of copy_bytes (the copy's largest dispatch)."""
+    def biggest(d, counter):
+        vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(os.path.join(d, "run_counter_collection.csv")))
+                if r["Counter_Name"] == counter]
+        return max(vals)
+    fk, wk = biggest(calib_fetch, "FETCH_SIZE"), biggest(calib_write, "WRITE_SIZE")
+    out = {"fetch_factor": copy_bytes / 1024.0 / fk, "write_factor": copy_bytes / 1024.0 / wk,
+           "calibration": {"copy_bytes": copy_bytes, "fetch_kib_read": fk, "write_kib_read": wk}, "workloads": {}}
+    for name, (fd, wd) in runs.items():
+        e = {}
+        for k in SHORT.values():
+            f, nf = _counter_mean(fd, "FETCH_SIZE", k)
+            w, nw = _counter_mean(wd, "WRITE_SIZE", k)
+            if nf and nw:
+                e[k] = {"fetch_kib": f, "write_kib": w, "dispatches": [nf, nw],
+                        "bytes": (f * out["fetch_factor"] + w * out["write_factor"]) * 1024.0}
+        out["workloads"][name] = e
+    return out
+
+
 if __name__ == "__main__":
-    print(table(sys.argv[1:]))
+    import json
+    if sys.argv[1] == "--trace":
+        print(trace_table(sys.argv[2]))
+    elif sys.argv[1] == "--traffic":
+        runs = {}
+        for spec in sys.argv[4:]:
+            name, dirs = spec.split("=", 1)
+            fd, wd = dirs.split(",")
+            runs[name] = (fd, wd)
+        print(json.dumps(traffic(sys.argv[2], sys.argv[3], runs), indent=1))
+    else:
+        print(table(sys.argv[1:]))

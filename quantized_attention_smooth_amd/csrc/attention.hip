@@ -119,15 +119,16 @@ struct AttnArgs {
 
 // V stages: FP8 codes [64-key group][channel][64 slots], one per K stage; or fp16 V
 // [16-key group][channel][16 slots], one stage.  16-byte chunks swizzled in both.
-template <int D, bool PV16, int NSTAGES = (!PV16 && D == 64) ? 3 : 2>
+// GROUPS: Q blocks per workgroup (4 waves each) sharing every K/V tile; each has its Delta_S row.
+template <int D, bool PV16, int GROUPS = 1>
 struct Smem {
   // K (and FP8 V, Delta_S) stages: a ring of three at d = 64 in the FP8 mode, where a block's
   // arithmetic is short enough that a tile issued one block ahead can still be in flight
-  static constexpr int NST = NSTAGES;
+  static constexpr int NST = (!PV16 && D == 64) ? 3 : 2;
   static constexpr int VST = PV16 ? 1 : NST;
   __attribute__((aligned(16))) int8_t k[NST][BK * D];  // K tile rows, 16-byte chunks swizzled
   __attribute__((aligned(16))) uint8_t v[VST][BK * D * (PV16 ? 2 : 1)];
-  __attribute__((aligned(16))) float ds[NST][BK];
+  __attribute__((aligned(16))) float ds[NST][GROUPS][BK];
 };
 
 // int32 S^T accumulators to floats, exactly (|S| <= 127^2 * 128 < 2^21).  At d = 128 they start
@@ -191,26 +192,28 @@ constexpr int kTileInstrs = BK * D / 16 / 64 / WAVES;
 // The buffer builtins exist only for the GPU target: their code is compiled in the device pass
 // (in the host pass, kernels using them otherwise lost their launch stubs without a diagnostic).
 
-template <int D, bool PV16>
+template <int D, bool PV16, int GROUPS = 1>
 struct TileLoader {
-  static constexpr int NK = kTileInstrs<D>;                 // K (and FP8 V) instructions per wave
-  static constexpr int NV = kTileInstrs<D> * (PV16 ? 2 : 1);
+  static constexpr int WT = WAVES * GROUPS;                 // waves that load each K/V tile
+  static constexpr int NK = BK * D / 16 / 64 / WT;          // K (and FP8 V) instructions per wave
+  static constexpr int NV = NK * (PV16 ? 2 : 1);
   static constexpr int VB = PV16 ? 2 : 1;                   // V bytes per element
-  static constexpr int STEP = WAVES * 64 * 16;              // bytes per load instruction and workgroup
+  static constexpr int STEP = WT * 64 * 16;                 // bytes per load instruction and workgroup
   const void *kp, *vp, *dp;
   uint32_t kbytes, vbytes, dbytes;
   uint32_t koff, voff;   // this lane's offset for instruction m = 0; instruction m adds m * STEP
 
-  // kc, vc: the head's K codes / V rows; dsrow: the Q block's Delta_S row of ds_len floats
-  __device__ TileLoader(const int8_t* kc, const uint8_t* vc, const float* dsrow, int nkb, int ds_len, int w,
+  // kc, vc: the head's K codes / V rows; dsrow: the wave's Q block's Delta_S row of ds_len
+  // floats; wv: wave index in the workgroup
+  __device__ TileLoader(const int8_t* kc, const uint8_t* vc, const float* dsrow, int nkb, int ds_len, int wv,
                         int lane) {
     kp = kc; kbytes = (uint32_t)nkb * BK * D;
     vp = vc; vbytes = (uint32_t)nkb * BK * D * VB;
     dp = dsrow; dbytes = (uint32_t)ds_len * 4;
-    // 16-byte chunk p of the tile in LDS (instruction m, wave w, lane) holds the global chunk of
+    // 16-byte chunk p of the tile in LDS (instruction m, wave wv, lane) holds the global chunk of
     // row p / (chunks per row) at swizzled position: the LDS side of a load is linear in the lane
     constexpr int CPR = D / 16;                             // 16-byte chunks per K row
-    const int p = w * 64 + lane;
+    const int p = wv * 64 + lane;
     const int row = p / CPR, pc = p % CPR;
     koff = (uint32_t)(row * D + ((pc ^ kswz<D>(row)) * 16));
     constexpr int RB = PV16 ? 32 : VGROUP;                  // bytes per V LDS row (group, channel)
@@ -220,19 +223,20 @@ struct TileLoader {
     voff = (uint32_t)(vrow * RB + ((vpc ^ sw) * 16));
   }
 
-  // K codes of block kb and its Delta_S row slice into stage st (each wave a quarter of the
-  // slice, so every wave issues the same number of loads per block).  The Delta_S load goes
-  // first, so a wait for "all but the last kTileInstrs" loads leaves only K chunks outstanding.
+  // K codes of block kb into stage st, and the wave's group's Delta_S row slice (each of the
+  // group's 4 waves a quarter of it, so every wave issues the same number of loads per block).
+  // The Delta_S load goes first, so a wait for "all but the last NK" loads leaves only K chunks
+  // outstanding.  w: wave index in its group; gi: the group.
   template <class SM>
-  __device__ void issue_k(SM& sm, int st, int kb, int w, int lane) const {
+  __device__ void issue_k(SM& sm, int st, int kb, int wv, int w, int gi, int lane) const {
 #if defined(__HIP_DEVICE_COMPILE__)
     if (lane < BK / 4 / WAVES)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(dp, dbytes), (lds_void*)(sm.ds[st] + w * (BK / WAVES)), 16,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(dp, dbytes), (lds_void*)(sm.ds[st][gi] + w * (BK / WAVES)), 16,
                                                lane * 16 + w * (BK / WAVES) * 4, kb * BK * 4, 0, 0);
     const auto kr = make_rsrc(kp, kbytes);
 #pragma unroll
     for (int m = 0; m < NK; ++m)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(sm.k[st] + (m * WAVES + w) * 1024), 16, koff,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(sm.k[st] + (m * WT + wv) * 1024), 16, koff,
                                                kb * BK * D + m * STEP, 0, 0);
 #endif
   }
@@ -240,12 +244,12 @@ struct TileLoader {
   // V of block kb into stage st: FP8 codes (64-byte rows) or 16-bit V (32-byte rows, twice the
   // instructions).
   template <class SM>
-  __device__ void issue_v(SM& sm, int st, int kb, int w) const {
+  __device__ void issue_v(SM& sm, int st, int kb, int wv) const {
 #if defined(__HIP_DEVICE_COMPILE__)
     const auto vr = make_rsrc(vp, vbytes);
 #pragma unroll
     for (int m = 0; m < NV; ++m)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(sm.v[st] + (m * WAVES + w) * 1024), 16, voff,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(sm.v[st] + (m * WT + wv) * 1024), 16, voff,
                                                kb * BK * D * VB + m * STEP, 0, 0);
 #endif
   }
@@ -307,15 +311,24 @@ __device__ inline void qk_tiles(const SM& sm, int st, const v4i (&qreg)[D / 32],
   }
 }
 
-template <int D, bool CAUSAL, bool DUMP, bool QK4, bool PV16, bool BF>
-__global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
+// GROUPS = 2 (FP8 mode, d = 128, non-causal): one workgroup of 8 waves takes two Q blocks of the
+// same (sequence, head), 4 waves each, and every K/V tile is loaded once for both.  A CU then
+// holds one such workgroup instead of two independent ones, so its two Q blocks run in step and
+// finish together (two independent workgroups on a CU finish at different times, the older one
+// being served first, and the last one of a round then runs alone).
+template <int D, bool CAUSAL, bool DUMP, bool QK4, bool PV16, bool BF, int GROUPS>
+__global__ __launch_bounds__(256 * GROUPS, GROUPS == 1 ? 2 : 1) void attn_fwd(AttnArgs a) {
+  static_assert(GROUPS == 1 || (!PV16 && !DUMP && !CAUSAL && D == 128),
+                "two Q blocks per workgroup: FP8 mode, d = 128, non-causal");
   typedef PV16T<BF> PT;
-  __shared__ Smem<D, PV16> sm;
+  __shared__ Smem<D, PV16, GROUPS> sm;
   const int tid = threadIdx.x, lane = tid & 63, col = lane & 31, half = lane >> 5;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform: kept in a scalar
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform: kept in a scalar
+  const int gi = wv / WAVES, w = wv % WAVES;                 // Q-block group, wave in the group
 
   const int H = a.g.H, Hkv = a.g.Hkv;
   int b, h, qb;
+  bool idle = false;                            // this group has no Q block
   Seq sq;
   if (DUMP) {
     b = a.dbg_b; h = a.dbg_h; qb = a.dbg_qb;
@@ -325,15 +338,21 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
     // so varlen batches split evenly and a kv head's codes stay in one XCD's L2; within it the
     // query heads sharing the kv head come together for each Q block, so they stream the same
     // K/V tiles at the same time
-    const int total = a.B * H * a.nqb, G = H / Hkv;
+    const int nq = (a.nqb + GROUPS - 1) / GROUPS;            // workgroups per (sequence, head)
+    const int total = a.B * H * nq, G = H / Hkv;
     const int L = xcd_remap(blockIdx.x, total);
     const int g = L % G, r = L / G;
-    const int qi = r % a.nqb, kbi = r / a.nqb;
+    const int qi = r % nq, kbi = r / nq;
     b = kbi % a.B;
     h = (kbi / a.B) * G + g;
     sq = a.g.seq(b);
-    if (qi >= seq_blocks(sq)) return;           // beyond this sequence (varlen)
-    qb = CAUSAL ? seq_blocks(sq) - 1 - qi : qi;
+    const int sb = seq_blocks(sq);
+    if (qi * GROUPS >= sb) return;              // beyond this sequence (varlen)
+    // this group's Q block; a second group past the sequence's end repeats group 0's block in
+    // step with it (loading its share of the tiles, meeting the barriers) and stores nothing
+    const int qx = qi * GROUPS + gi;
+    idle = qx >= sb;
+    qb = idle ? qi * GROUPS : (CAUSAL ? sb - 1 - qx : qx);
   }
   const int hk = h / (H / Hkv);
   const int N = sq.n, nkb = seq_blocks(sq);
@@ -345,7 +364,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
   const uint8_t* vc = a.vcodes + krows * D * (PV16 ? 2 : 1);
   const float* kscl = a.kscale + blocks_off(sq, Hkv, hk) * 2;
   const float* dsrow = a.ds + ds_off(sq, a.g.causal, h) + ds_row_offset(a.g.causal, qb, nkb * BK);
-  const TileLoader<D, PV16> ld(kc, vc, dsrow, nkb, ds_row_len(a.g.causal, qb, nkb * BK), w, lane);
+  const TileLoader<D, PV16, GROUPS> ld(kc, vc, dsrow, nkb, ds_row_len(a.g.causal, qb, nkb * BK), wv, lane);
 
   // the wave's 32 query rows as the B operand of S^T = K Q^T (16 bytes per k-step)
   // (INT4 range: 32 bytes per 64-channel step, held as two consecutive v4i)
@@ -358,7 +377,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
   const float qd = a.qscale[qrows + i];
 
   if (DUMP) {
-    ld.issue_k(sm, 0, a.dbg_kb, w, lane);
+    ld.issue_k(sm, 0, a.dbg_kb, wv, w, 0, lane);
     wait_loads();
     __syncthreads();
     v16i sacc[BK / 32];
@@ -373,18 +392,18 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
     return;
   }
 
-  const int nblk = CAUSAL ? qb + 1 : nkb;
+  const int nblk = CAUSAL ? qb + 1 : nkb;       // KV blocks of this Q block (both groups: nkb)
   float m_run = -INFINITY, l_part = 0.f;
   v16f og[D / 32];
 #pragma unroll
   for (int ct = 0; ct < D / 32; ++ct) og[ct] = (v16f){};
   const v8i rsel = rowsum_selector(lane);     // A operand of the P~ row-sum instruction
 
-  constexpr int NST = Smem<D, PV16>::NST;
+  constexpr int NST = Smem<D, PV16, GROUPS>::NST;
   // blocks 0 .. NST - 2 into stages 0 .. NST - 2; wait for block 0
   for (int i = 0; i < NST - 1 && i < nblk; ++i) {
-    ld.issue_v(sm, i, i, w);
-    ld.issue_k(sm, i, i, w, lane);
+    ld.issue_v(sm, i, i, wv);
+    ld.issue_k(sm, i, i, wv, w, gi, lane);
   }
   if constexpr (NST == 3) {
     if (nblk > 1) wait_all_but_one_block<D>();
@@ -395,19 +414,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
   __syncthreads();
   int st = 0;                                   // stage of block kb: kb % NST
 
-  // One KV block: S^T on the int8 MFMA, dequantize + bias (+ mask), online softmax, P~ V on the
-  // FP8 MFMA (or P V on the fp16 MFMA).  MASK is set only for the last block of a row range
-  // (causal diagonal or ragged tail).
+  // One KV block of this wave's group: S^T on the int8 MFMA, dequantize + bias (+ mask), online
+  // softmax, P~ V on the FP8 MFMA (or P V on the fp16 MFMA).  MASK is set only for the causal
+  // diagonal block.
   auto block = [&](const int kb, auto mask_tag) {
     constexpr bool MASK = decltype(mask_tag)::value;
     const bool more = kb + 1 < nblk;
-    // block kb + NST - 1 into the stage block kb - 1 used (every wave is past its barrier)
-    const int stn = st == 0 ? NST - 1 : st - 1;
-    const bool issue = kb + NST - 1 < nblk;
-    if (issue) {
-      if (!PV16) ld.issue_v(sm, stn, kb + NST - 1, w);
-      ld.issue_k(sm, stn, kb + NST - 1, w, lane);
-    }
 
     v16i sacc[BK / 32];
     qk_tiles<D, QK4>(sm, st, qreg, col, half, sacc);
@@ -430,7 +442,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
       for (int qq = 0; qq < 4; ++qq) {
         const int j0 = 32 * t + 8 * qq + 4 * half;
         // read as an int vector: this stage was filled and waited for in the previous block
-        const v4i dsv = *reinterpret_cast<const v4i*>(&sm.ds[st][j0]);
+        const v4i dsv = *reinterpret_cast<const v4i*>(&sm.ds[st][gi][j0]);
         const float dsa[4] = {__int_as_float(dsv[0]), __int_as_float(dsv[1]), __int_as_float(dsv[2]), __int_as_float(dsv[3])};
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -501,11 +513,6 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       }
       l_part = fmaf(l_part, alpha, lsum);
-
-      wait_loads();
-      __syncthreads();
-      if (more) ld.issue_v(sm, 0, kb + 1, w);
-      st = st + 1 == NST ? 0 : st + 1;
       return;
     }
 
@@ -592,6 +599,21 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
       }
     }
 
+  };
+
+  // One step of the workgroup's stream of blocks: the loads of block kb + NST - 1, block kb
+  // (MODE 0: unmasked, 1: the masked causal diagonal), then the wait for block kb + 1 and the
+  // barrier.  Every wave loads its share of each tile and meets every barrier.
+  auto step = [&](const int kb, auto mode_tag) {
+    constexpr int MODE = decltype(mode_tag)::value;
+    // block kb + NST - 1 into the stage block kb - 1 used (every wave is past its barrier)
+    const int stn = st == 0 ? NST - 1 : st - 1;
+    const bool issue = kb + NST - 1 < nblk;
+    if (issue) {
+      if (!PV16) ld.issue_v(sm, stn, kb + NST - 1, wv);
+      ld.issue_k(sm, stn, kb + NST - 1, wv, w, gi, lane);
+    }
+    block(kb, std::integral_constant<bool, MODE == 1>{});
     // block kb + 1 has landed (the loads issued above, for block kb + NST - 1, may still fly)
     if constexpr (NST == 3) {
       if (issue) wait_all_but_one_block<D>();
@@ -600,21 +622,23 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a) {
       wait_loads();
     }
     __syncthreads();
+    // fp16 V has one stage: the next block's goes out once every wave is done with this one
+    if (PV16 && kb + 1 < nblk) ld.issue_v(sm, 0, kb + 1, wv);
     st = st + 1 == NST ? 0 : st + 1;
   };
-
-  // the last block needs masking when causal (the diagonal block); keys past N carry a Delta_S
-  // of -inf, so a ragged tail needs none
-  constexpr bool mask_last = CAUSAL;
-  const int nfull = mask_last ? nblk - 1 : nblk;
-  for (int kb = 0; kb < nfull; ++kb) block(kb, std::false_type{});
-  if (mask_last) block(nblk - 1, std::true_type{});
+  typedef std::integral_constant<int, 0> Full;
+  typedef std::integral_constant<int, 1> Diag;
+  // the last block is masked when causal (the diagonal block); keys past N carry a Delta_S of
+  // -inf, so a ragged tail needs no mask
+  const int nfull = CAUSAL ? nblk - 1 : nblk;
+  for (int kb = 0; kb < nfull; ++kb) step(kb, Full{});
+  if (CAUSAL) step(nblk - 1, Diag{});
 
   // epilogue: O = acc * delta_V / l   (FP8: l sums P~, so it carries the 1/P_r, and the row-sum
   // instruction has already added both lane halves; fp16: no V scale, per-lane partial sums)
   const float l = PV16 ? xhalf_sum(l_part) : l_part;
   const float inv_l = l > 0.f ? 1.f / l : 0.f;
-  if (i < N) {
+  if (!idle && i < N) {
     __half* orow = a.o + b * a.g.st.qb + (long long)(sq.tok0 + i) * a.g.st.qt + h * a.g.st.qh;
     const float* vs = a.vscale + ((size_t)b * Hkv + hk) * D;
 #pragma unroll
@@ -658,9 +682,15 @@ AttnArgs make_args(const Dims& D, const Ptrs& P) {
 
 template <int DD, bool QK4, bool PV16, bool BF>
 hipError_t launch_d(const Dims& D, const AttnArgs& a, hipStream_t s) {
+  // FP8 mode at d = 128, non-causal: two Q blocks per workgroup sharing every K/V tile (causal
+  // pairs measured slower: the second block is one shorter and idles on the last one)
+  if constexpr (!PV16 && DD == 128) {
+    if (!D.causal)
+      return launch(attn_fwd<DD, false, false, QK4, PV16, BF, 2>, dim3(D.B * D.H * ((D.nqb + 1) / 2)), dim3(512), s, a);
+  }
   const int grid = D.B * D.H * D.nqb;
-  if (D.causal) return launch(attn_fwd<DD, true, false, QK4, PV16, BF>, dim3(grid), dim3(256), s, a);
-  return launch(attn_fwd<DD, false, false, QK4, PV16, BF>, dim3(grid), dim3(256), s, a);
+  if (D.causal) return launch(attn_fwd<DD, true, false, QK4, PV16, BF, 1>, dim3(grid), dim3(256), s, a);
+  return launch(attn_fwd<DD, false, false, QK4, PV16, BF, 1>, dim3(grid), dim3(256), s, a);
 }
 
 template <bool QK4, bool PV16>
@@ -682,10 +712,10 @@ hipError_t launch_qk_tile(const Dims& D, const Ptrs& P, int b, int h, int qb, in
   a.dbg_b = b; a.dbg_h = h; a.dbg_qb = qb; a.dbg_kb = kb; a.dbg_out = out;
   const dim3 one(1), blk(256);
   if (D.qk_bits == 4)
-    return D.d == 128 ? launch(attn_fwd<128, false, true, true, false, false>, one, blk, s, a)
-                      : launch(attn_fwd<64, false, true, true, false, false>, one, blk, s, a);
-  return D.d == 128 ? launch(attn_fwd<128, false, true, false, false, false>, one, blk, s, a)
-                    : launch(attn_fwd<64, false, true, false, false, false>, one, blk, s, a);
+    return D.d == 128 ? launch(attn_fwd<128, false, true, true, false, false, 1>, one, blk, s, a)
+                      : launch(attn_fwd<64, false, true, true, false, false, 1>, one, blk, s, a);
+  return D.d == 128 ? launch(attn_fwd<128, false, true, false, false, false, 1>, one, blk, s, a)
+                    : launch(attn_fwd<64, false, true, false, false, false, 1>, one, blk, s, a);
 }
 
 }  // namespace sage

@@ -71,7 +71,7 @@ def _traffic(workload: str, pv_bits: int):
         t = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
-    e = t.get("workloads", {}).get(workload if pv_bits == 8 else f"{workload}-pv16")
+    e = t.get("workloads", {}).get(workload if pv_bits == 8 else f"{workload}-pv16", {}).get("attn_fwd")
     if not e or t.get("attention_src_sha256") != _src_hash():
         return None
     return (e["fetch_kib"] * t["fetch_factor"] + e["write_kib"] * t["write_factor"]) * 1024.0

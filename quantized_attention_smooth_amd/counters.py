@@ -27,6 +27,7 @@ from __future__ import annotations
 
 import collections
 import csv
+import hashlib
 import os
 import sys
 
@@ -148,13 +149,19 @@ def _counter_mean(d: str, counter: str, kernel: str | None) -> tuple[float, int]
 
 def traffic(calib_fetch: str, calib_write: str, runs: dict, copy_bytes: int = 1 << 30) -> dict:
     """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of every library kernel, scaled by what the same
-    counters read for a plain device copy of copy_bytes (the copy's largest dispatch)."""
+    counters read for a plain device copy of copy_bytes (the copy's largest dispatch).  The
+    SHA-256 of the attention and prologue sources in this tree are recorded with them: the
+    figures describe those sources only."""
     def biggest(d, counter):
         vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(os.path.join(d, "run_counter_collection.csv")))
                 if r["Counter_Name"] == counter]
         return max(vals)
     fk, wk = biggest(calib_fetch, "FETCH_SIZE"), biggest(calib_write, "WRITE_SIZE")
-    out = {"fetch_factor": copy_bytes / 1024.0 / fk, "write_factor": copy_bytes / 1024.0 / wk,
+    here = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
+    sha = {k: hashlib.sha256(open(os.path.join(here, f"{k}.hip"), "rb").read()).hexdigest()
+           for k in ("attention", "prologue")}
+    out = {"attention_src_sha256": sha["attention"], "prologue_src_sha256": sha["prologue"],
+           "fetch_factor": copy_bytes / 1024.0 / fk, "write_factor": copy_bytes / 1024.0 / wk,
            "calibration": {"copy_bytes": copy_bytes, "fetch_kib_read": fk, "write_kib_read": wk}, "workloads": {}}
     for name, (fd, wd) in runs.items():
         e = {}

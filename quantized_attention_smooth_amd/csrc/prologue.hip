@@ -8,7 +8,8 @@
 //
 // The codec kernels stream HBM: each reads its fp16 input once (K and V twice: statistics, then
 // quantization) and writes 1-byte codes plus a few scales.  Delta_S (the Q-smoothing bias,
-// mu_Q . gamma_K per Q block and key) reads K a third time and writes 4 bytes per (Q block, key).
+// mu_Q . gamma_K per Q block and key) is formed where K is quantized, from the rows just read,
+// and writes 4 bytes per (Q block, key).
 //
 // Bit-exactness: the channel means are exact sums.  Every fp16 value is an integer multiple of
 // 2^-24 below 2^16, so a sum of up to 256 of them is exact in fp64 (below 2^24, 48 bits of
@@ -166,9 +167,11 @@ __global__ void init_stats(unsigned long long* ksum, unsigned int* vamax, int n,
 // inputs in fp64 within a workgroup and int64 fixed point across; bf16 inputs in the limb
 // accumulator above (LDS within a workgroup, int64 atomics across).  VSTATS = false (V kept in
 // 16-bit floats) skips V entirely.
-// Workgroup (bx, by) of a (ceil(longest / 256), B*Hkv) tiling, 256 threads; thread = (row slot,
-// 8-channel chunk).  Runs inside stats_and_q.
+// Workgroup (bx, by) of a (ceil(longest / kStatsTok), B*Hkv) tiling, 256 threads; thread =
+// (row slot, 8-channel chunk).  Runs inside stats_and_q.
 // ---------------------------------------------------------------------------------------
+constexpr int kStatsTok = 128;    // tokens per statistics workgroup
+
 template <int D, typename T>
 struct KvStatsSmem {
   static constexpr int RPP = 256 / (D / 8);
@@ -185,7 +188,7 @@ __device__ inline void kv_stats_body(const T* __restrict__ k, const T* __restric
                                      const Geo& g, int bx, int by, KvStatsSmem<D, T>& sm) {
   constexpr int TPR = D / 8;      // threads per row
   constexpr int RPP = 256 / TPR;  // rows per pass
-  constexpr int TOK = 256;        // tokens per workgroup
+  constexpr int TOK = kStatsTok;  // tokens per workgroup
   constexpr bool BF = std::is_same<T, __bf16>::value;
   auto& ls = sm.ls;
   auto& lm = sm.lm;
@@ -211,9 +214,10 @@ __device__ inline void kv_stats_body(const T* __restrict__ k, const T* __restric
     __syncthreads();
   }
   const int tok0 = bx * TOK;
-  // 4 passes at a time, loads issued before use: rows past N read row N - 1 (in bounds) and are
-  // skipped afterwards, so no load waits behind its own branch
-  constexpr int CH = 4;
+  // every pass's loads issued before any is used (one memory round trip per workgroup): rows past
+  // N read row N - 1 (in bounds) and are skipped afterwards, so no load waits behind its own
+  // branch
+  constexpr int CH = TOK / RPP;
   for (int p0 = 0; p0 < TOK / RPP; p0 += CH) {
     In8<T> kr[CH], vr[CH];
 #pragma unroll
@@ -264,41 +268,34 @@ __device__ inline void kv_stats_body(const T* __restrict__ k, const T* __restric
 // fp16 V for the fp16 P V MFMA: the 128 keys of KV block kb, transposed into 8 groups of 16
 // keys, [group][channel][16 slots]; key kk of a group sits in slot 8 ((kk / 4) % 2) +
 // 4 (kk / 8) + kk % 4, the k-slot order of the fp16 MFMA B operand the attention kernel
-// builds from its S^T accumulators.  A thread takes 4 consecutive keys (4 consecutive slots:
+// builds from its S^T accumulators.  A thread holds 4 consecutive keys (4 consecutive slots:
 // one 8-byte LDS write per channel).  LDS rows (32 bytes) are XOR-permuted within each run of
 // 8 (row ^ (row / 8) % 8) so that the 8 channels 8 apart a wave writes at once fall on
 // distinct banks; the copy-out undoes it.
 // ---------------------------------------------------------------------------------------
 __device__ inline int v16_lds_row(int row) { return row ^ ((row >> 3) & 7); }
 
+// keys jl0 .. jl0 + 3 of the block (jl0 % 4 == 0), channels 8 cq .. 8 cq + 7, into the LDS image
 template <int D, typename T>
-__device__ inline void store_v16(const T* __restrict__ vbase, long long tstride, uint8_t* vt,
-                                 uint8_t* __restrict__ dst, int kb, int N, int tid, int cq, int r0) {
-  constexpr int TPR = D / 8, RPP = 256 / TPR, G4 = BK / 4 / RPP;
+__device__ inline void stage_v16(const In8<T> (&vr)[4], uint8_t* vt, int jl0, int nvalid, int cq) {
+  const int g = jl0 >> 4, kk = jl0 & 15;
+  const int quad = 2 * ((kk >> 2) & 1) + (kk >> 3);   // slots 4 quad .. 4 quad + 3
+  uint16_t x[4][8];
 #pragma unroll
-  for (int p = 0; p < G4; ++p) {
-    const int jl0 = 4 * (p * RPP + r0);        // first of the thread's 4 keys within the block
-    const int g = jl0 >> 4, kk = jl0 & 15;
-    const int quad = 2 * ((kk >> 2) & 1) + (kk >> 3);   // slots 4 quad .. 4 quad + 3
-    uint16_t x[4][8];
-    In8<T> vr[4];
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) vr[i] = load8(vbase + min(kb * BK + jl0 + i, N - 1) * tstride + cq * 8);
+    for (int e = 0; e < 8; ++e) x[i][e] = jl0 + i < nvalid ? vr[i].b[e] : (uint16_t)0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bool valid = kb * BK + jl0 + i < N;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[i][e] = valid ? vr[i].b[e] : (uint16_t)0;
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int row = g * D + cq * 8 + e;
-      const uint2 w2 = make_uint2((uint32_t)x[0][e] | ((uint32_t)x[1][e] << 16),
-                                  (uint32_t)x[2][e] | ((uint32_t)x[3][e] << 16));
-      *reinterpret_cast<uint2*>(vt + v16_lds_row(row) * 32 + quad * 8) = w2;
-    }
+  for (int e = 0; e < 8; ++e) {
+    const int row = g * D + cq * 8 + e;
+    const uint2 w2 = make_uint2((uint32_t)x[0][e] | ((uint32_t)x[1][e] << 16),
+                                (uint32_t)x[2][e] | ((uint32_t)x[3][e] << 16));
+    *reinterpret_cast<uint2*>(vt + v16_lds_row(row) * 32 + quad * 8) = w2;
   }
-  __syncthreads();
+}
+
+template <int D>
+__device__ inline void copyout_v16(const uint8_t* vt, uint8_t* __restrict__ dst, int tid) {
   for (int ch = tid; ch < BK * D * 2 / 16; ch += 256) {
     const int row = ch >> 1;
     *reinterpret_cast<uint4*>(dst + ch * 16) =
@@ -307,152 +304,352 @@ __device__ inline void store_v16(const T* __restrict__ vbase, long long tstride,
 }
 
 // ---------------------------------------------------------------------------------------
-// K smoothing + quantization and V FP8 quantization for one KV block of 128 keys.
-// grid (blocks of the longest sequence, B*Hkv), 256 threads.
-// K group: keys 8a + 4h + r of the block share the scale of lane half h (one scale per
-// lane of the 32x32 integer MFMA accumulator that holds those keys).
-// V codes are written transposed per 64-key group in the FP8 MFMA k-slot order; with PV16
-// V itself (fp16) is written transposed per 16-key group in the fp16 MFMA k-slot order.
+// Delta_S[qb, j] = sum_c mu_Q[qb, c] * gamma_K[j, c], stored times log2(e)/sqrt(d), is formed
+// inside kv_quant (below), where the workgroup has just read the keys' rows.
+//
+// A GEMM (Q blocks x keys x channels) on the bf16 MFMA at fp32-class accuracy: both fp32
+// factors are split exactly into three bf16 parts, x = x1 + x2 + x3 (8 significant bits each,
+// 24 in all), and the six cross products whose weight is at least 2^-16 of the leading one
+// are accumulated, smallest first (x3y1 + x2y2 + x1y3 + x2y1 + x1y2 + x1y1); the dropped
+// terms are below 2^-24 of it.  The bf16 MFMA accumulates in fp32 (unlike the FP8 one).
 // ---------------------------------------------------------------------------------------
-template <int D, bool PV16, typename T, bool QK4>
-__global__ __launch_bounds__(256) void kv_quant(const T* __restrict__ k, const T* __restrict__ v,
-                                                const unsigned long long* __restrict__ ksum,
-                                                const unsigned int* __restrict__ vamax,
-                                                int8_t* __restrict__ kcodes, uint8_t* __restrict__ vcodes,
-                                                float* __restrict__ kscale, float* __restrict__ muk_out,
-                                                float* __restrict__ vscale, Geo g, float R) {
-  constexpr int TPR = D / 8, RPP = 256 / TPR, PASSES = BK / RPP;
-  static_assert(RPP % 8 == 0, "a thread's rows must share (row % 8)");
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+struct Split3 {
+  bf16x8 p[3];
+};
+
+// x = x1 + x2 + x3 exactly, in pairs: the packed fp32 -> bf16 convert rounds two elements to
+// nearest even at once, and a bf16 pair widens back to fp32 by a shift (low) and a mask (high).
+// Each residual x - x1 and x - x1 - x2 is exact in fp32 (the rounding error of a narrower format).
+__device__ inline uint32_t bf16_pair(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
+}
+__device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ inline Split3 split3(const float (&x)[8]) {
+  uint32_t w[3][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float a = x[2 * i], b = x[2 * i + 1];
+    const uint32_t w1 = bf16_pair(a, b);
+    const float ra = a - bf16_lo(w1), rb = b - bf16_hi(w1);
+    const uint32_t w2 = bf16_pair(ra, rb);
+    w[0][i] = w1;
+    w[1][i] = w2;
+    w[2][i] = bf16_pair(ra - bf16_lo(w2), rb - bf16_hi(w2));   // at most 8 significant bits remain: exact
+  }
+  Split3 s;
+#pragma unroll
+  for (int p = 0; p < 3; ++p) s.p[p] = __builtin_bit_cast(bf16x8, (uint4){w[p][0], w[p][1], w[p][2], w[p][3]});
+  return s;
+}
+
+// Store v at byte offset off of [base, base + bytes) through a buffer resource: a store at or past
+// the end is dropped by the hardware's range check, so masked elements cost no branch.
+__device__ inline void store_or_drop(float* base, uint32_t bytes, uint32_t off, float v) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), make_rsrc(base, bytes), (int)off, 0, 0);
+#endif
+}
+constexpr uint32_t kDropOffset = 0xFFFFFF00u;   // past any resource here (all are below 2^31 bytes)
+
+
+// ---------------------------------------------------------------------------------------
+// One KV block of 128 keys of one (sequence, kv head): K smoothing + quantization, V FP8
+// quantization (or the fp16 V layout), and the Delta_S columns of these keys for every Q block
+// of the kv head's query heads that sees them (all Q blocks; causal: qb >= kb).
+// grid (blocks of the longest sequence * B*Hkv), 256 threads.  Workgroup ids are split into one
+// contiguous share per XCD (own L2) and decode KV block fastest, so each XCD holds whole kv
+// heads: the mu_Q parts their Delta_S columns read stay in that XCD's L2, and with causal masks
+// a kv head's workgroups start with the KV blocks the most Q blocks see.
+//
+// Every HBM load of the workgroup is issued first, V rows in the transposition layout (a thread
+// takes 4 consecutive keys of 8 channels) and K rows in the layout of the Delta_S MFMA operand
+// (wave w, lane (r, hl): key 32 w + r, channels 16 ks + 8 hl .. + 7 of k-step ks), so K is read
+// once and quantized in the registers that then feed the products.
+// K group: keys 8a + 4h + r of the block share the scale of lane half h (one scale per lane of
+// the 32x32 integer MFMA accumulator that holds those keys).
+// V codes are written transposed per 64-key group in the FP8 MFMA k-slot order; with PV16 V
+// itself (fp16) is written transposed per 16-key group in the fp16 MFMA k-slot order.
+// Delta_S: each wave splits its 32 keys' gamma_K once (the stationary B operand) and runs
+// through the Q blocks 32 at a time (32x32x16 bf16 MFMA tiles); the four waves read each
+// 32-block tile of mu_Q parts from LDS, double-buffered through registers.
+// ---------------------------------------------------------------------------------------
+template <int D, bool PV16, typename T, bool QK4, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void kv_quant(const T* __restrict__ k, const T* __restrict__ v,
+                                                   const unsigned long long* __restrict__ ksum,
+                                                   const unsigned int* __restrict__ vamax,
+                                                   int8_t* __restrict__ kcodes, uint8_t* __restrict__ vcodes,
+                                                   float* __restrict__ kscale, float* __restrict__ muk_out,
+                                                   float* __restrict__ vscale, const uint16_t* __restrict__ muqs,
+                                                   float* __restrict__ ds, Geo g, float R, int nkb, float k2) {
+  constexpr int TPR = D / 8, RPP = 256 / TPR;  // V layout: threads per key row, rows per pass
+  constexpr int G4 = BK / 4 / RPP;             // V layout: passes of 4-key groups
+  constexpr int KS = D / 16;                   // 16-channel MFMA k-steps
+  // one Q block's three bf16 parts of D channels, plus 16 bytes: the 32 lanes of an operand read
+  // (32 consecutive Q blocks, one 16-byte chunk each) then fall on distinct banks
+  constexpr int ROW = 3 * D * 2 + 16;
+  constexpr int AT = 32 * ROW;                 // a tile of 32 Q blocks
+  constexpr int VT = BK * D * (PV16 ? 2 : 1);  // V transposition buffer
+  constexpr int CPQ = 3 * D / 8;               // 16-byte chunks per Q block
+  constexpr int LPT = 32 * CPQ / 256;          // chunks per thread per tile
   __shared__ float red[WAVES][2];
-  __shared__ __attribute__((aligned(16))) uint8_t vt[BK * D * (PV16 ? 2 : 1)];
-  const int tid = threadIdx.x, cq = tid % TPR, r0 = tid / TPR, lane = tid % 64, w = tid / 64;
-  const int kb = blockIdx.x;
-  const size_t bh = blockIdx.y;                 // (sequence, kv head)
+  __shared__ __attribute__((aligned(16))) float smk[D];   // mu_K
+  __shared__ __attribute__((aligned(16))) float smv[D];   // V_r / max|V| (0 for an all-zero channel)
+  // the V buffer, then (after the V codes are out) the two mu_Q tile buffers
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * AT > VT ? 2 * AT : VT];
+  uint8_t* const vt = lds;
+  const int tid = threadIdx.x, cq = tid % TPR, r0 = tid / TPR, lane = tid % 64;
+  const int w = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int r = lane & 31, hl = lane >> 5;
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  const int kb = L % nkb;
+  const size_t bh = L / nkb;                   // (sequence, kv head)
   const int sidx = (int)bh / g.Hkv, hk = (int)bh % g.Hkv;
   const Seq sq = g.seq(sidx);
-  if (kb >= seq_blocks(sq)) return;
-  const int N = sq.n;
+  const int nqb = seq_blocks(sq);
+  if (kb >= nqb) return;
+  const int N = sq.n, nvalid = min(BK, N - kb * BK);   // keys of the block inside the sequence
   const long long ts = g.st.kt;
   const T* kbase = k + sidx * g.st.kb + (long long)sq.tok0 * ts + hk * g.st.kh;
   const T* vbase = v + sidx * g.st.kb + (long long)sq.tok0 * ts + hk * g.st.kh;
   const size_t rows = rows_off(sq, g.Hkv, hk);  // this head's padded rows in the code arrays
 
-  float mu[8], vinv[8];
-  // this thread's 8 channel sums and abs-maxima, loaded together (fp16: 64 + 32 contiguous bytes)
-  unsigned long long ks8[8];
-  uint32_t va8[8];
-  if (!std::is_same<T, __bf16>::value) {
-    const uint4* kp = reinterpret_cast<const uint4*>(ksum + bh * D + cq * 8);
+  // ---- loads (rows past N read row N - 1 and count as zero afterwards) ----
+  In8<T> vr[G4][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint4 w = kp[i];
-      ks8[2 * i] = ((unsigned long long)w.y << 32) | w.x;
-      ks8[2 * i + 1] = ((unsigned long long)w.w << 32) | w.z;
-    }
-  }
-  if (!PV16) {
-    const uint4* vp = reinterpret_cast<const uint4*>(vamax + bh * D + cq * 8);
-    const uint4 w0 = vp[0], w1 = vp[1];
-    va8[0] = w0.x; va8[1] = w0.y; va8[2] = w0.z; va8[3] = w0.w;
-    va8[4] = w1.x; va8[5] = w1.y; va8[6] = w1.z; va8[7] = w1.w;
-  }
+  for (int p = 0; p < G4; ++p)
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int c = cq * 8 + e;
+    for (int i = 0; i < 4; ++i)
+      vr[p][i] = load8(vbase + min(kb * BK + 4 * (p * RPP + r0) + i, N - 1) * ts + cq * 8);
+  const int jl = 32 * w + r;                   // this lane's key within the block
+  In8<T> kr[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) kr[ks] = load8(kbase + (long long)min(kb * BK + jl, N - 1) * ts + 16 * ks + 8 * hl);
+
+  // ---- per-channel mean of K and V scale, one channel per thread ----
+  if (tid < D) {
+    const int c = tid;
+    float mu;
     if (std::is_same<T, __bf16>::value) {
-      mu[e] = (float)(superacc_value(&ksum[(bh * D + c) * kLimbs]) / (double)N);
+      mu = (float)(superacc_value(&ksum[(bh * D + c) * kLimbs]) / (double)N);
     } else {
-      const long long S = (long long)ks8[e];
-      mu[e] = (float)((double)S / ((double)N * 16777216.0));
+      mu = (float)((double)(long long)ksum[bh * D + c] / ((double)N * 16777216.0));
     }
-    const float va = PV16 ? 0.f : __uint_as_float(va8[e]);
-    vinv[e] = va > 0.f ? V_RANGE / va : 0.f;
-    if (kb == 0 && r0 == 0) {
-      muk_out[bh * D + c] = mu[e];
+    smk[c] = mu;
+    const float va = PV16 ? 0.f : __uint_as_float(vamax[bh * D + c]);
+    smv[c] = va > 0.f ? V_RANGE / va : 0.f;
+    if (kb == 0) {
+      muk_out[bh * D + c] = mu;
       if (!PV16) vscale[bh * D + c] = va / V_RANGE;
     }
   }
+  __syncthreads();
 
-  // gamma_K = RN32(K - mu_K); every row of this thread has the same (row % 8)
-  // loads issued before use (rows past N read row N - 1 and are zeroed afterwards)
-  float gk[PASSES][8];
-  float am = 0.f;
-  In8<T> kr[PASSES];
+  // ---- V into the LDS image ----
 #pragma unroll
-  for (int p = 0; p < PASSES; ++p) kr[p] = load8(kbase + min(kb * BK + p * RPP + r0, N - 1) * ts + cq * 8);
+  for (int p = 0; p < G4; ++p) {
+    const int jl0 = 4 * (p * RPP + r0);        // first of the thread's 4 keys within the block
+    if (PV16) {
+      stage_v16<D>(vr[p], vt, jl0, nvalid, cq);
+    } else {
+      // per-channel FP8 into [group u][channel][slot]: the thread's 4 keys fill 4 consecutive
+      // slots, one 32-bit LDS write per channel.  The 16-byte chunk of a channel row is
+      // XOR-swizzled by channel bits 3-4 against bank conflicts (lanes of a wave differ in
+      // channel by multiples of 8) and unswizzled on the way out.
+      const int u = jl0 >> 6, jj = jl0 & 63;
+      const int base = 32 * ((jj >> 2) & 1) + 16 * (jj >> 5) + 4 * ((jj >> 3) & 3);   // slot of key jj
+      const float4 s0 = *reinterpret_cast<const float4*>(&smv[cq * 8]);
+      const float4 s1 = *reinterpret_cast<const float4*>(&smv[cq * 8 + 4]);
+      const float vinv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+      float x[4][8];
 #pragma unroll
-  for (int p = 0; p < PASSES; ++p) {
-    const bool valid = kb * BK + p * RPP + r0 < N;
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      gk[p][e] = valid ? kr[p].f(e) - mu[e] : 0.f;
-      am = fmaxf(am, fabsf(gk[p][e]));
+        for (int e = 0; e < 8; ++e)
+          x[i][e] = jl0 + i < nvalid ? fminf(fmaxf(vr[p][i].f(e) * vinv[e], -V_RANGE), V_RANGE) : 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int c = cq * 8 + e;
+        int word = __builtin_amdgcn_cvt_pk_fp8_f32(x[0][e], x[1][e], 0, false);
+        word = __builtin_amdgcn_cvt_pk_fp8_f32(x[2][e], x[3][e], word, true);
+        const int phys = (((base >> 4) ^ ((c >> 3) & 3)) << 4) | (base & 15);
+        *reinterpret_cast<int*>(&vt[(u * D + c) * VGROUP + phys]) = word;
+      }
     }
   }
-  const int hgrp = (r0 & 7) >> 2;
-  float a0 = wave_max(hgrp == 0 ? am : 0.f);
-  float a1 = wave_max(hgrp == 1 ? am : 0.f);
-  if (lane == 0) { red[w][0] = a0; red[w][1] = a1; }
   __syncthreads();
+  if (PV16) {
+    copyout_v16<D>(vt, vcodes + (rows + (size_t)kb * BK) * D * 2, tid);
+  } else {
+    uint8_t* dst = vcodes + (rows + (size_t)kb * BK) * D;
+    for (int ch = tid; ch < 2 * D * VGROUP / 16; ch += 256) {
+      const int rowc = ch >> 2, c = rowc % D;  // row = group * D + channel
+      const int src = rowc * VGROUP + (((ch & 3) ^ ((c >> 3) & 3)) << 4);
+      *reinterpret_cast<uint4*>(dst + ch * 16) = *reinterpret_cast<const uint4*>(vt + src);
+    }
+  }
+
+  // ---- K: gamma_K = RN32(K - mu_K) ----
+  float gk[KS][8];
+  float am = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const int c0 = 16 * ks + 8 * hl;
+    const float4 m0 = *reinterpret_cast<const float4*>(&smk[c0]);
+    const float4 m1 = *reinterpret_cast<const float4*>(&smk[c0 + 4]);
+    const float mm[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      gk[ks][e] = jl < nvalid ? kr[ks].f(e) - mm[e] : 0.f;
+      am = fmaxf(am, fabsf(gk[ks][e]));
+    }
+  }
+  // the key's maximum (both lane halves), then over the wave's keys of the same group: key bit 2
+  // (= bit 2 of r) picks the group, so the other bits of r are reduced
+  am = fmaxf(am, __shfl_xor(am, 32, 64));
+#pragma unroll
+  for (int m = 1; m <= 16; m <<= 1)
+    if (m != 4) am = fmaxf(am, __shfl_xor(am, m, 64));
+  if (lane == 0) red[w][0] = am;
+  if (lane == 4) red[w][1] = am;
+
+  // tiles of 32 consecutive Q blocks of one query head for Delta_S: G heads x ntq tiles, the
+  // first starting at the first Q block that sees this KV block.  A tile's rows are contiguous
+  // in muqs; rows past the sequence repeat its last Q block (never stored).
+  const int G = g.H / g.Hkv;
+  const int qs = CAUSAL ? kb : 0;
+  const int ntq = (nqb - qs + 31) / 32;
+  const int ntiles = G * ntq;
+  const int Npad = nqb * BQ;
+  auto tile_chunk = [&](int t, int it) -> const u32x4* {
+    const int c = it * 256 + tid;
+    const uint16_t* aq = muqs + blocks_off(sq, g.H, hk * G + t / ntq) * 3 * D;
+    return reinterpret_cast<const u32x4*>(aq + (size_t)min(qs + 32 * (t % ntq) + c / CPQ, nqb - 1) * 3 * D +
+                                          (c % CPQ) * 8);
+  };
+  auto lds_chunk = [&](int buf, int it) -> u32x4* {
+    const int c = it * 256 + tid;
+    return reinterpret_cast<u32x4*>(lds + buf * AT + (c / CPQ) * ROW + (c % CPQ) * 16);
+  };
+  u32x4 av[LPT];
+  if (ntiles > 0) {
+#pragma unroll
+    for (int it = 0; it < LPT; ++it) av[it] = *tile_chunk(0, it);
+  }
+  __syncthreads();                             // red complete; every read of the V image done
+
+  const int h4 = (r >> 2) & 1;
   float amax = 0.f;
 #pragma unroll
-  for (int i = 0; i < WAVES; ++i) amax = fmaxf(amax, red[i][hgrp]);
+  for (int i = 0; i < WAVES; ++i) amax = fmaxf(amax, red[i][h4]);
   const float inv = amax > 0.f ? R / amax : 0.f;
   if (tid < 2) {
     float a = 0.f;
     for (int i = 0; i < WAVES; ++i) a = fmaxf(a, red[i][tid]);
     kscale[(blocks_off(sq, g.Hkv, hk) + kb) * 2 + tid] = a / R;
   }
+  // codes of channels 16 ks + 8 hl .. + 7 (8-byte chunk 2 ks + hl of the row; rows past N get
+  // zero codes)
+  int8_t* const krow = kcodes + (rows + (size_t)kb * BK + jl) * D;
+  if (!QK4) {
 #pragma unroll
-  for (int p = 0; p < PASSES; ++p) {
-    const int row = kb * BK + p * RPP + r0;   // < Npad: rows past N get zero codes
-    float x[8];
+    for (int ks = 0; ks < KS; ++ks) {
+      union { int8_t c[8]; uint2 u; } out;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = fminf(fmaxf(rintf(gk[p][e] * inv), -R), R);
-    store_codes<QK4>(kcodes + (rows + row) * D, cq, x);
+      for (int e = 0; e < 8; ++e) out.c[e] = (int8_t)(int)fminf(fmaxf(rintf(gk[ks][e] * inv), -R), R);
+      *reinterpret_cast<uint2*>(krow + 16 * ks + 8 * hl) = out.u;
+    }
+  } else {
+    // FP6 E2M3: a 32-channel slot (k-steps 2 m and 2 m + 1) holds the 48-bit packs of its four
+    // 8-channel chunks back to back in 24 bytes, then 8 zero bytes.  Lane half 0 holds chunks 0
+    // and 2 of the slot, half 1 chunks 1 and 3; one swap gives half 0 bytes 0-15 (packs 0, 1 and
+    // the low half of 2) and half 1 bytes 16-31 (the rest of pack 2, pack 3, padding).
+#pragma unroll
+    for (int m = 0; m < KS / 2; ++m) {
+      unsigned long long pk[2];
+#pragma unroll
+      for (int o = 0; o < 2; ++o) {
+        pk[o] = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          pk[o] |= (unsigned long long)e2m3_bits(fminf(fmaxf(rintf(gk[2 * m + o][e] * inv), -R), R)) << (6 * e);
+      }
+      const unsigned long long got = __shfl_xor(hl == 0 ? pk[1] : pk[0], 32, 64);
+      // half 0: pk = {pack 0, pack 2}, got = pack 1;  half 1: pk = {pack 1, pack 3}, got = pack 2
+      const unsigned long long lo = hl == 0 ? pk[0] | (got << 48) : (got >> 32) | (pk[1] << 16);
+      const unsigned long long hi = hl == 0 ? (got >> 16) | (pk[1] << 32) : 0ull;
+      *reinterpret_cast<uint4*>(krow + 32 * m + 16 * hl) =
+          make_uint4((uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32));
+    }
   }
 
-  if (PV16) {
-    store_v16<D>(vbase, ts, vt, vcodes + (rows + (size_t)kb * BK) * D * 2, kb, N, tid, cq, r0);
-    return;
-  }
-
-  // V: per-channel FP8, transposed into [group u][channel][slot] in LDS, then streamed out.
-  // A thread takes 4 consecutive keys: their codes fill 4 consecutive slots, one 32-bit LDS
-  // write per channel.  The 16-byte chunk of a channel row is XOR-swizzled by channel bits 3-4
-  // against bank conflicts (lanes of a wave differ in channel by multiples of 8) and unswizzled
-  // on the way out.
-  constexpr int G4 = BK / 4 / RPP;             // passes of 4-key groups
+  // ---- Delta_S columns of this block ----
+  // B operand: this lane's gamma_K split in three, held for the whole Q-block loop (keys past
+  // the sequence count as zero; their columns are stored as -inf)
+  Split3 bs[KS];
 #pragma unroll
-  for (int p = 0; p < G4; ++p) {
-    const int jl0 = 4 * (p * RPP + r0);        // first of the thread's 4 keys within the block
-    const int u = jl0 >> 6, jj = jl0 & 63;
-    const int base = 32 * ((jj >> 2) & 1) + 16 * (jj >> 5) + 4 * ((jj >> 3) & 3);   // slot of key jj
-    float x[4][8];
-    In8<T> vr[4];
+  for (int ks = 0; ks < KS; ++ks) bs[ks] = split3(gk[ks]);
+  if (ntiles > 0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) vr[i] = load8(vbase + min(kb * BK + jl0 + i, N - 1) * ts + cq * 8);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bool valid = kb * BK + jl0 + i < N;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[i][e] = valid ? fminf(fmaxf(vr[i].f(e) * vinv[e], -V_RANGE), V_RANGE) : 0.f;
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int c = cq * 8 + e;
-      int word = __builtin_amdgcn_cvt_pk_fp8_f32(x[0][e], x[1][e], 0, false);
-      word = __builtin_amdgcn_cvt_pk_fp8_f32(x[2][e], x[3][e], word, true);
-      const int phys = (((base >> 4) ^ ((c >> 3) & 3)) << 4) | (base & 15);
-      *reinterpret_cast<int*>(&vt[(u * D + c) * VGROUP + phys]) = word;
-    }
+    for (int it = 0; it < LPT; ++it) *lds_chunk(0, it) = av[it];
   }
   __syncthreads();
-  uint8_t* dst = vcodes + (rows + (size_t)kb * BK) * D;
-  for (int ch = tid; ch < 2 * D * VGROUP / 16; ch += 256) {
-    const int rowc = ch >> 2, c = rowc % D;    // row = group * D + channel
-    const int src = rowc * VGROUP + (((ch & 3) ^ ((c >> 3) & 3)) << 4);
-    *reinterpret_cast<uint4*>(dst + ch * 16) = *reinterpret_cast<const uint4*>(vt + src);
+  const int jd = kb * BK + jl;                 // this lane's key (Delta_S column)
+  for (int t = 0; t < ntiles; ++t) {
+    if (t + 1 < ntiles) {
+#pragma unroll
+      for (int it = 0; it < LPT; ++it) av[it] = *tile_chunk(t + 1, it);
+    }
+    const uint8_t* a = lds + (t & 1) * AT;
+    f32x16 acc = {};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int c0 = 16 * ks + 8 * hl;
+      bf16x8 A[3];
+#pragma unroll
+      for (int p = 0; p < 3; ++p)
+        A[p] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const s16x8*>(a + r * ROW + (p * D + c0) * 2));
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[2], bs[ks].p[0], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[1], bs[ks].p[1], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[0], bs[ks].p[2], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[1], bs[ks].p[0], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[0], bs[ks].p[1], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[0], bs[ks].p[0], acc, 0, 0, 0);
+    }
+    // lane holds Q blocks q0 + 8 a + 4 hl + e (a, e < 4) of key column jd.  The stores go through
+    // one buffer resource over rows q0 .. qlast of the head: fewer than 2^31 bytes (32 rows of
+    // at most 2^23 keys), so 32-bit offsets reach every element, and a Q block past the
+    // sequence takes an offset past the end.  Every key of the block is < (qb + 1) * 128 for
+    // the Q blocks here, so causal rows hold it.
+    const int q0 = qs + 32 * (t % ntq), qlast = min(q0 + 31, nqb - 1);
+    const size_t row0 = ds_row_offset(CAUSAL, q0, Npad);
+    float* const dsr = ds + ds_off(sq, CAUSAL, hk * G + t / ntq) + row0;
+    const uint32_t span = (uint32_t)((ds_row_offset(CAUSAL, qlast + 1, Npad) - row0) * 4);
+#pragma unroll
+    for (int a4 = 0; a4 < 4; ++a4)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int qb = q0 + 8 * a4 + 4 * hl + e;
+        // row qb's first element relative to row q0's (causal rows hold (qb + 1) * 128 keys)
+        const uint32_t rel = CAUSAL ? 64u * (uint32_t)((qb - q0) * (qb + q0 + 1)) : (uint32_t)(qb - q0) * (uint32_t)Npad;
+        // keys past the sequence (the zero-padded tail of its last block) get -inf: the
+        // attention kernel adds Delta_S to the logits, so they drop out without a mask
+        store_or_drop(dsr, span, qb < nqb ? (rel + (uint32_t)jd) * 4u : kDropOffset,
+                      jd < N ? acc[4 * a4 + e] * k2 : -INFINITY);
+      }
+    if (t + 1 < ntiles) {
+#pragma unroll
+      for (int it = 0; it < LPT; ++it) *lds_chunk((t + 1) & 1, it) = av[it];
+    }
+    __syncthreads();
   }
 }
 
@@ -594,231 +791,6 @@ __global__ __launch_bounds__(256) void stats_and_q(const T* __restrict__ k, cons
 }
 
 // ---------------------------------------------------------------------------------------
-// Delta_S[qb, j] = sum_c mu_Q[qb, c] * gamma_K[j, c], stored times log2(e)/sqrt(d).
-//
-// A GEMM (Q blocks x keys x channels) on the bf16 MFMA at fp32-class accuracy: both fp32
-// factors are split exactly into three bf16 parts, x = x1 + x2 + x3 (8 significant bits each,
-// 24 in all), and the six cross products whose weight is at least 2^-16 of the leading one
-// are accumulated, smallest first (x3y1 + x2y2 + x1y3 + x2y1 + x1y2 + x1y1); the dropped
-// terms are below 2^-24 of it.  The bf16 MFMA accumulates in fp32 (unlike the FP8 one).
-//
-// One workgroup per (32 NU Q blocks of one query head, 256 keys), 256 threads, NU = 1 or 2.
-// The Q blocks' mu_Q parts (split by the Q prologue) are copied to LDS once and read there by
-// all four waves; wave w owns keys 64 w .. 64 w + 63 of the tile, loads their rows up front
-// (one memory round trip), forms gamma_K = RN32(K - mu_K) and its split one 16-channel k-step
-// at a time, and accumulates NU x 2 MFMA tiles of 32 Q blocks x 32 keys.  Workgroup ids run over
-// (Q-block tile, query head of the group, key tile, sequence, kv head), fastest first, split into
-// one contiguous share per XCD (own L2): the workgroups that read one key tile are adjacent
-// and on one XCD, so the keys come from HBM about once however many Q blocks and query heads
-// use them, and each XCD's share holds whole kv heads of every sequence (even varlen shares).
-// Causal: Q block qb stores keys j < (qb + 1) * 128; workgroups and waves whose keys no row of
-// theirs stores exit early, and a 32-row tile with no such row is multiplied but not stored.
-// ---------------------------------------------------------------------------------------
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef short s16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-
-constexpr int DS_KT = 256;    // keys per workgroup: 64 per wave, two 32-column MFMA tiles
-
-// QT Q blocks per workgroup (NU = QT / 32 MFMA row tiles)
-template <int D, int QT>
-struct DsSmem {
-  // one Q block's three bf16 parts of D channels, plus 16 bytes: the 32 lanes of an operand
-  // read (32 consecutive Q blocks, one 16-byte chunk each) then fall on distinct banks
-  static constexpr int ROW = 3 * D * 2 + 16;
-  __attribute__((aligned(16))) uint8_t a[QT * ROW];
-  __attribute__((aligned(16))) float muk[D];
-};
-
-struct Split3 {
-  bf16x8 p[3];
-};
-
-// x = x1 + x2 + x3 exactly, in pairs: the packed fp32 -> bf16 convert rounds two elements to
-// nearest even at once, and a bf16 pair widens back to fp32 by a shift (low) and a mask (high).
-// Each residual x - x1 and x - x1 - x2 is exact in fp32 (the rounding error of a narrower format).
-__device__ inline uint32_t bf16_pair(float a, float b) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
-}
-__device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
-__device__ inline Split3 split3(const float (&x)[8]) {
-  uint32_t w[3][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float a = x[2 * i], b = x[2 * i + 1];
-    const uint32_t w1 = bf16_pair(a, b);
-    const float ra = a - bf16_lo(w1), rb = b - bf16_hi(w1);
-    const uint32_t w2 = bf16_pair(ra, rb);
-    w[0][i] = w1;
-    w[1][i] = w2;
-    w[2][i] = bf16_pair(ra - bf16_lo(w2), rb - bf16_hi(w2));   // at most 8 significant bits remain: exact
-  }
-  Split3 s;
-#pragma unroll
-  for (int p = 0; p < 3; ++p) s.p[p] = __builtin_bit_cast(bf16x8, (uint4){w[p][0], w[p][1], w[p][2], w[p][3]});
-  return s;
-}
-
-// Store v at byte offset off of [base, base + bytes) through a buffer resource: a store at or past
-// the end is dropped by the hardware's range check, so masked elements cost no branch.
-__device__ inline void store_or_drop(float* base, uint32_t bytes, uint32_t off, float v) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), make_rsrc(base, bytes), (int)off, 0, 0);
-#endif
-}
-constexpr uint32_t kDropOffset = 0xFFFFFF00u;   // past any resource here (all are below 2^31 bytes)
-
-// grid (nqt * H * nkt * B), nqt = Q-block tiles and nkt = key tiles of the longest sequence
-template <int D, bool CAUSAL, typename T, int NU>
-__global__ __launch_bounds__(256) void delta_s(const T* __restrict__ k, const float* __restrict__ muk,
-                                               const uint16_t* __restrict__ muqs, float* __restrict__ ds,
-                                               Geo g, int B, int nqt, int nkt, float k2) {
-  constexpr int QT = 32 * NU;                          // Q blocks of the tile
-  __shared__ DsSmem<D, QT> sm;
-  constexpr int KS = D / 16;                            // 16-channel MFMA k-steps
-  constexpr int ROW = DsSmem<D, QT>::ROW;
-  const int tid = threadIdx.x, lane = tid & 63, r = lane & 31, hl = lane >> 5;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int H = g.H, Hkv = g.Hkv, G = H / Hkv;
-  const int L = xcd_remap(blockIdx.x, nqt * H * nkt * B);
-  int rest = L;
-  const int qt = rest % nqt; rest /= nqt;
-  const int gq = rest % G; rest /= G;
-  const int kt = rest % nkt; rest /= nkt;
-  const int b = rest % B, hk = rest / B;
-  const int h = hk * G + gq;
-  const Seq sq = g.seq(b);
-  const int N = sq.n, nqb = seq_blocks(sq), Npad = nqb * BQ;
-  const int q0 = qt * QT, k0 = kt * DS_KT;
-  if (q0 >= nqb || k0 >= Npad) return;                 // beyond this sequence
-  const int qlast = min(q0 + QT, nqb) - 1;
-  if (CAUSAL && k0 >= (qlast + 1) * BQ) return;        // every row of the tile stops earlier
-
-  // the tile's Q blocks' mu_Q parts (rows past the sequence repeat its last block and are never
-  // stored) and mu_K -> LDS.  Their loads go out first, so the LDS fill waits for them alone
-  // while this wave's key rows are still arriving.
-  constexpr int CPQ = 3 * D / 8;                       // 16-byte chunks per Q block
-  const uint16_t* aq = muqs + blocks_off(sq, H, h) * 3 * D;
-  uint4 av[QT * CPQ / 256];
-#pragma unroll
-  for (int it = 0; it < QT * CPQ / 256; ++it) {
-    const int c = it * 256 + tid;
-    av[it] = *reinterpret_cast<const uint4*>(aq + (size_t)min(q0 + c / CPQ, nqb - 1) * 3 * D + (c % CPQ) * 8);
-  }
-  float4 mk = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (tid < D / 4) mk = *reinterpret_cast<const float4*>(muk + ((size_t)b * Hkv + hk) * D + 4 * tid);
-  __builtin_amdgcn_sched_barrier(0);                   // keep these loads ahead of the key rows
-
-  // this wave's key rows, all k-steps (rows past the sequence read its last row and count as
-  // zero)
-  const long long ts = g.st.kt;
-  const T* kbase = k + b * g.st.kb + (long long)sq.tok0 * ts + hk * g.st.kh;
-  const int j0 = k0 + 64 * w;                          // this wave's first key
-  In8<T> kr[2][KS];
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      kr[t][ks] = load8(kbase + (long long)min(j0 + 32 * t + r, N - 1) * ts + 16 * ks + 8 * hl);
-
-#pragma unroll
-  for (int it = 0; it < QT * CPQ / 256; ++it) {
-    const int c = it * 256 + tid;
-    *reinterpret_cast<uint4*>(sm.a + (c / CPQ) * ROW + (c % CPQ) * 16) = av[it];
-  }
-  if (tid < D / 4) *reinterpret_cast<float4*>(&sm.muk[4 * tid]) = mk;
-  __syncthreads();
-  if (j0 >= Npad || (CAUSAL && j0 >= (qlast + 1) * BQ)) return;   // no key of this wave is stored
-
-  // A tile u (Q blocks q0 + 32 u ..) is live if it has a Q block that stores key j0.  Both tiles
-  // are multiplied either way (a branch per tile would split the MFMA schedule); a dead one is
-  // just not stored.
-  bool live[NU];
-#pragma unroll
-  for (int u = 0; u < NU; ++u) {
-    const int qa = q0 + 32 * u;
-    live[u] = qa < nqb && (!CAUSAL || j0 < (min(qa + 31, nqb - 1) + 1) * BQ);
-  }
-
-  // the 2 x 2 tile products, one k-step at a time; TAIL: the wave holds keys j >= N, which
-  // count as zero (only the last wave of a sequence takes that path)
-  f32x16 acc[NU][2] = {};
-  auto gemm = [&](auto tail_tag) {
-    constexpr bool TAIL = decltype(tail_tag)::value;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int c0 = 16 * ks + 8 * hl;                 // this lane's 8 channels of the k-step
-      const float4 m0 = *reinterpret_cast<const float4*>(&sm.muk[c0]);
-      const float4 m1 = *reinterpret_cast<const float4*>(&sm.muk[c0 + 4]);
-      const float mm[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
-      bf16x8 A[NU][3];
-#pragma unroll
-      for (int u = 0; u < NU; ++u)
-#pragma unroll
-        for (int p = 0; p < 3; ++p)
-          A[u][p] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const s16x8*>(sm.a + (32 * u + r) * ROW + (p * D + c0) * 2));
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        float xb[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float x = kr[t][ks].f(e) - mm[e];      // gamma_K, RN32
-          xb[e] = TAIL && j0 + 32 * t + r >= N ? 0.f : x;
-        }
-        const Split3 Bv = split3(xb);
-#pragma unroll
-        for (int u = 0; u < NU; ++u) {
-          f32x16 c = acc[u][t];
-          c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[u][2], Bv.p[0], c, 0, 0, 0);
-          c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[u][1], Bv.p[1], c, 0, 0, 0);
-          c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[u][0], Bv.p[2], c, 0, 0, 0);
-          c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[u][1], Bv.p[0], c, 0, 0, 0);
-          c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[u][0], Bv.p[1], c, 0, 0, 0);
-          c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[u][0], Bv.p[0], c, 0, 0, 0);
-          acc[u][t] = c;
-        }
-      }
-    }
-  };
-  if (j0 + 64 > N) gemm(std::true_type{});
-  else gemm(std::false_type{});
-
-  // lane holds Q blocks q0 + 32 u + 8 a + 4 hl + e (a, e < 4) of key column j0 + 32 t + r.  The
-  // stores go through one buffer resource over rows q0 .. qlast of this head: fewer than 2^31
-  // bytes (at most 64 rows of at most 2^23 keys), so 32-bit offsets reach every element and
-  // an element that is not stored (Q block past the sequence, key past a causal row) takes
-  // an offset past the end.
-  const size_t row0 = ds_row_offset(CAUSAL, q0, Npad);
-  float* const dsr = ds + ds_off(sq, CAUSAL, h) + row0;
-  const uint32_t span = (uint32_t)((ds_row_offset(CAUSAL, qlast + 1, Npad) - row0) * 4);
-#pragma unroll
-  for (int u = 0; u < NU; ++u) {
-    if (!live[u]) continue;
-#pragma unroll
-    for (int a4 = 0; a4 < 4; ++a4)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int qb = q0 + 32 * u + 8 * a4 + 4 * hl + e;
-        // row qb's first element relative to row q0's (causal rows hold (qb + 1) * 128 keys)
-        const uint32_t rel = CAUSAL ? 64u * (uint32_t)((qb - q0) * (qb + q0 + 1)) : (uint32_t)(qb - q0) * (uint32_t)Npad;
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int j = j0 + 32 * t + r;
-          const bool ok = qb < nqb && (!CAUSAL || (j >> 7) <= qb);
-          // keys past the sequence (the zero-padded tail of its last block) get -inf: the
-          // attention kernel adds Delta_S to the logits, so they drop out without a mask
-          store_or_drop(dsr, span, ok ? (rel + (uint32_t)j) * 4u : kDropOffset,
-                        j < N ? acc[u][t][4 * a4 + e] * k2 : -INFINITY);
-        }
-      }
-  }
-}
-
-// ---------------------------------------------------------------------------------------
 // debug: internal layouts -> plain layouts
 // ---------------------------------------------------------------------------------------
 __global__ void copy_rows_i8(const int8_t* __restrict__ src, int8_t* __restrict__ dst, int heads, int N,
@@ -901,12 +873,7 @@ hipError_t launch_prologue_d(const Dims& Dm, const Ptrs& P, hipStream_t s) {
   const dim3 blk(256);
   hipError_t e = launch(init_stats, dim3((nkv + 255) / 256), blk, s, P.ksum, P.vamax, nkv, Dm.bf16 ? kLimbs : 1);
   if (e != hipSuccess) return e;
-  const dim3 gs((Dm.N + 255) / 256, Dm.B * Dm.Hkv), gq(Dm.nkb, Dm.B * Dm.Hkv);
-  // INT4-range codes (R = 7) are stored as FP6: a compile-time switch of the code store
-  auto kvq = [&](auto pv16, auto qk4) {
-    return launch(kv_quant<D, decltype(pv16)::value, T, decltype(qk4)::value>, gq, blk, s,
-                  k, v, P.ksum, P.vamax, P.kcodes, P.vcodes, P.kscale, P.muk, P.vscale, g, R);
-  };
+  const dim3 gs((Dm.N + kStatsTok - 1) / kStatsTok, Dm.B * Dm.Hkv);
   const bool qk4 = Dm.qk_bits == 4;
   // statistics (K, and V unless it stays 16-bit) and the Q prologue: one launch
   const int nks = (int)(gs.x * gs.y), nsq = nks + Dm.nqb * Dm.B * Dm.H;
@@ -918,21 +885,20 @@ hipError_t launch_prologue_d(const Dims& Dm, const Ptrs& P, hipStream_t s) {
   if (vstats) e = qk4 ? sq(std::true_type{}, std::true_type{}) : sq(std::true_type{}, std::false_type{});
   else e = qk4 ? sq(std::false_type{}, std::true_type{}) : sq(std::false_type{}, std::false_type{});
   if (e != hipSuccess) return e;
-  if (Dm.pv_bits == 16) e = qk4 ? kvq(std::true_type{}, std::true_type{}) : kvq(std::true_type{}, std::false_type{});
-  else e = qk4 ? kvq(std::false_type{}, std::true_type{}) : kvq(std::false_type{}, std::false_type{});
-  if (e != hipSuccess) return e;
+  // K and V codes and Delta_S.  INT4-range codes (R = 7) are stored as FP6: a compile-time switch
+  // of the code store.
   const float k2 = (float)(1.4426950408889634 / sqrt((double)D));
-  // 64 Q blocks per workgroup when sequences are long (the key split is shared by more MFMAs),
-  // 32 when they are short on average (varlen prefill batches: less work on rows past the end)
-  auto dsl = [&](auto nu) {
-    constexpr int NU = decltype(nu)::value;
-    const int nqt = (Dm.nqb + 32 * NU - 1) / (32 * NU), nkt = (Dm.Npad + DS_KT - 1) / DS_KT;
-    const dim3 gds(nqt * Dm.H * nkt * Dm.B);
-    if (Dm.causal) return launch(delta_s<D, true, T, NU>, gds, blk, s, k, P.muk, P.muqs, P.ds, g, Dm.B, nqt, nkt, k2);
-    return launch(delta_s<D, false, T, NU>, gds, blk, s, k, P.muk, P.muqs, P.ds, g, Dm.B, nqt, nkt, k2);
+  const dim3 gq(Dm.nkb * Dm.B * Dm.Hkv);
+  auto kvq = [&](auto pv16, auto qk4c, auto causal) {
+    return launch(kv_quant<D, decltype(pv16)::value, T, decltype(qk4c)::value, decltype(causal)::value>, gq, blk,
+                  s, k, v, P.ksum, P.vamax, P.kcodes, P.vcodes, P.kscale, P.muk, P.vscale, P.muqs, P.ds, g, R,
+                  Dm.nkb, k2);
   };
-  if (Dm.tot_pad >= 48LL * BQ * Dm.B) return dsl(std::integral_constant<int, 2>{});
-  return dsl(std::integral_constant<int, 1>{});
+  auto kvq_c = [&](auto pv16, auto qk4c) {
+    return Dm.causal ? kvq(pv16, qk4c, std::true_type{}) : kvq(pv16, qk4c, std::false_type{});
+  };
+  auto kvq_q = [&](auto pv16) { return qk4 ? kvq_c(pv16, std::true_type{}) : kvq_c(pv16, std::false_type{}); };
+  return Dm.pv_bits == 16 ? kvq_q(std::true_type{}) : kvq_q(std::false_type{});
 }
 
 }  // namespace

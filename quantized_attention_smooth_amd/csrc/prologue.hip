@@ -318,7 +318,9 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ inline void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 struct Split3 {
   bf16x8 p[3];
@@ -380,10 +382,10 @@ constexpr uint32_t kDropOffset = 0xFFFFFF00u;   // past any resource here (all a
 // itself (fp16) is written transposed per 16-key group in the fp16 MFMA k-slot order.
 // Delta_S: each wave splits its 32 keys' gamma_K once (the stationary B operand) and runs
 // through the Q blocks 32 at a time (32x32x16 bf16 MFMA tiles); the four waves read each
-// 32-block tile of mu_Q parts from LDS, double-buffered through registers.
+// 32-block tile of mu_Q parts from LDS, double-buffered and loaded straight to LDS.
 // ---------------------------------------------------------------------------------------
 template <int D, bool PV16, typename T, bool QK4, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void kv_quant(const T* __restrict__ k, const T* __restrict__ v,
+__global__ __launch_bounds__(256, 3) void kv_quant(const T* __restrict__ k, const T* __restrict__ v,
                                                    const unsigned long long* __restrict__ ksum,
                                                    const unsigned int* __restrict__ vamax,
                                                    int8_t* __restrict__ kcodes, uint8_t* __restrict__ vcodes,
@@ -398,8 +400,9 @@ __global__ __launch_bounds__(256, 2) void kv_quant(const T* __restrict__ k, cons
   constexpr int ROW = 3 * D * 2 + 16;
   constexpr int AT = 32 * ROW;                 // a tile of 32 Q blocks
   constexpr int VT = BK * D * (PV16 ? 2 : 1);  // V transposition buffer
-  constexpr int CPQ = 3 * D / 8;               // 16-byte chunks per Q block
-  constexpr int LPT = 32 * CPQ / 256;          // chunks per thread per tile
+  constexpr int CPQ = 3 * D / 8;               // 16-byte chunks of data per Q block
+  constexpr int CPR = ROW / 16;                // 16-byte chunks per LDS row (the last is padding)
+  constexpr int NLI = (32 * CPR + 255) / 256;  // tile load instructions per wave
   __shared__ float red[WAVES][2];
   __shared__ __attribute__((aligned(16))) float smk[D];   // mu_K
   __shared__ __attribute__((aligned(16))) float smv[D];   // V_r / max|V| (0 for an all-zero channel)
@@ -529,22 +532,29 @@ __global__ __launch_bounds__(256, 2) void kv_quant(const T* __restrict__ k, cons
   const int ntq = (nqb - qs + 31) / 32;
   const int ntiles = G * ntq;
   const int Npad = nqb * BQ;
-  auto tile_chunk = [&](int t, int it) -> const u32x4* {
-    const int c = it * 256 + tid;
+  // A tile image is filled by buffer loads straight to LDS: instruction m of wave w writes the 64
+  // consecutive 16-byte chunks (4 m + w) * 64 .. + 63 of it, so chunk p = (row, pc) comes from
+  // chunk pc of the row's Q block.  The resource spans the head's Q blocks: rows past the
+  // sequence, and the padding chunk of each row, read past its end and get zeros.
+  auto issue_tile = [&](int t, int buf) {
+#if defined(__HIP_DEVICE_COMPILE__)
     const uint16_t* aq = muqs + blocks_off(sq, g.H, hk * G + t / ntq) * 3 * D;
-    return reinterpret_cast<const u32x4*>(aq + (size_t)min(qs + 32 * (t % ntq) + c / CPQ, nqb - 1) * 3 * D +
-                                          (c % CPQ) * 8);
-  };
-  auto lds_chunk = [&](int buf, int it) -> u32x4* {
-    const int c = it * 256 + tid;
-    return reinterpret_cast<u32x4*>(lds + buf * AT + (c / CPQ) * ROW + (c % CPQ) * 16);
-  };
-  u32x4 av[LPT];
-  if (ntiles > 0) {
+    const auto rs = make_rsrc(aq, (uint32_t)nqb * 3 * D * 2);
+    const int q0 = qs + 32 * (t % ntq);
 #pragma unroll
-    for (int it = 0; it < LPT; ++it) av[it] = *tile_chunk(0, it);
-  }
+    for (int m = 0; m < NLI; ++m) {
+      const int p = (4 * m + w) * 64 + lane;
+      if (m + 1 < NLI || p < 32 * CPR) {
+        const int row = p / CPR, pc = p % CPR;
+        const uint32_t off = pc < CPQ ? (uint32_t)(row * 3 * D * 2 + pc * 16) : kDropOffset;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + buf * AT + (4 * m + w) * 64 * 16), 16, off,
+                                                 q0 * 3 * D * 2, 0, 0);
+      }
+    }
+#endif
+  };
   __syncthreads();                             // red complete; every read of the V image done
+  issue_tile(0, 0);                            // lands while the codes are formed
 
   const int h4 = (r >> 2) & 1;
   float amax = 0.f;
@@ -597,17 +607,11 @@ __global__ __launch_bounds__(256, 2) void kv_quant(const T* __restrict__ k, cons
   Split3 bs[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) bs[ks] = split3(gk[ks]);
-  if (ntiles > 0) {
-#pragma unroll
-    for (int it = 0; it < LPT; ++it) *lds_chunk(0, it) = av[it];
-  }
+  wait_vm();                                   // tile 0 is in LDS
   __syncthreads();
   const int jd = kb * BK + jl;                 // this lane's key (Delta_S column)
   for (int t = 0; t < ntiles; ++t) {
-    if (t + 1 < ntiles) {
-#pragma unroll
-      for (int it = 0; it < LPT; ++it) av[it] = *tile_chunk(t + 1, it);
-    }
+    if (t + 1 < ntiles) issue_tile(t + 1, (t + 1) & 1);
     const uint8_t* a = lds + (t & 1) * AT;
     f32x16 acc = {};
 #pragma unroll
@@ -645,10 +649,7 @@ __global__ __launch_bounds__(256, 2) void kv_quant(const T* __restrict__ k, cons
         store_or_drop(dsr, span, qb < nqb ? (rel + (uint32_t)jd) * 4u : kDropOffset,
                       jd < N ? acc[4 * a4 + e] * k2 : -INFINITY);
       }
-    if (t + 1 < ntiles) {
-#pragma unroll
-      for (int it = 0; it < LPT; ++it) *lds_chunk((t + 1) & 1, it) = av[it];
-    }
+    wait_vm();                                 // tile t + 1 is in LDS
     __syncthreads();
   }
 }

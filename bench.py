@@ -356,7 +356,6 @@ def main() -> int:
         cold.append((c0, c1))
     torch.cuda.synchronize()
     pro_cold_ms = float(np.mean([c0.elapsed_time(c1) for c0, c1 in cold]))
-    del flush
     ops = w.ops
     value = ops / (ms_step * 1e-3) / 1e12
     achieved = ops / (att_ms * 1e-3) / 1e12
@@ -369,6 +368,22 @@ def main() -> int:
         ds_elems += w.H * (128 * nqb * (nqb + 1) // 2 if w.causal else nqb * nqb * 128)
     # read q, k, v once (fp16); write Q/K codes (1 byte), V as FP8 codes or fp16, Delta_S rows
     pro_bytes = 2 * (n_q + 2 * n_kv) + (n_q + n_kv) + n_kv * (pv // 8) + 4 * ds_elems
+    # the practical HBM rate for that much traffic: a plain device copy moving the same bytes
+    # (half read, half written), timed like the flushed prologue
+    copy_src = torch.empty(pro_bytes // 2 // 4, dtype=torch.float32, device=dev)
+    copy_dst = torch.empty_like(copy_src)
+    copy_src.fill_(1.0)
+    copies = []
+    for _ in range(min(K, 10)):
+        flush.fill_(0.0)
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record()
+        copy_dst.copy_(copy_src)
+        c1.record()
+        copies.append((c0, c1))
+    torch.cuda.synchronize()
+    copy_cold_ms = float(np.mean([c0.elapsed_time(c1) for c0, c1 in copies]))
+    del flush, copy_src, copy_dst
     traffic = _traffic(args.workload, pv)
     peak = attn_peak(w.qk_bits, pv)
     meas = measured_peaks(dev, w.qk_bits, pv)
@@ -404,6 +419,11 @@ def main() -> int:
                       "prologue_frac_hbm": pro_bytes / (pro_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
                       "prologue_ms_caches_flushed": pro_cold_ms,
                       "prologue_GBps_algorithmic_caches_flushed": pro_bytes / (pro_cold_ms * 1e-3) / 1e9,
+                      # K (and V when it is quantized) is read a second time for its codes
+                      "prologue_GBps_two_reads_caches_flushed":
+                          (pro_bytes + 2 * n_kv * (2 if pv == 8 else 1)) / (pro_cold_ms * 1e-3) / 1e9,
+                      "copy_same_bytes_ms_caches_flushed": copy_cold_ms,
+                      "prologue_vs_copy_caches_flushed": copy_cold_ms / pro_cold_ms,
                       "wall_s_timed": wall},
     }
     line["environment"] = environment()

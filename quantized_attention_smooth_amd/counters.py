@@ -33,8 +33,7 @@ import sys
 
 SIMDS = 1024          # 256 CUs x 4 SIMDs
 XCDS = 8
-SHORT = {"attn_fwd": "attn_fwd", "stats_and_q": "stats_and_q", "kv_quant": "kv_quant", "delta_s": "delta_s",
-         "init_stats": "init_stats"}
+SHORT = {"attn_fwd": "attn_fwd", "stats_and_q": "stats_and_q", "kv_quant": "kv_quant", "init_stats": "init_stats"}
 
 
 def _kernel(name: str) -> str | None:
@@ -101,7 +100,7 @@ def derived(c: dict) -> dict:
     return d
 
 
-def table(dirs, kernels=("attn_fwd", "stats_and_q", "kv_quant", "delta_s")) -> str:
+def table(dirs, kernels=("attn_fwd", "stats_and_q", "kv_quant")) -> str:
     data = load(dirs)
     lines = []
     for k in kernels:

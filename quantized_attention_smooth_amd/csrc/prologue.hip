@@ -368,9 +368,10 @@ constexpr uint32_t kDropOffset = 0xFFFFFF00u;   // past any resource here (all a
 // quantization (or the fp16 V layout), and the Delta_S columns of these keys for every Q block
 // of the kv head's query heads that sees them (all Q blocks; causal: qb >= kb).
 // grid (blocks of the longest sequence * B*Hkv), 256 threads.  Workgroup ids are split into one
-// contiguous share per XCD (own L2) and decode KV block fastest, so each XCD holds whole kv
-// heads: the mu_Q parts their Delta_S columns read stay in that XCD's L2, and with causal masks
-// a kv head's workgroups start with the KV blocks the most Q blocks see.
+// contiguous share per XCD (own L2) and decode KV block fastest, then sequence, then kv head, so
+// each XCD holds whole kv heads of every sequence: the mu_Q parts their Delta_S columns read
+// stay in that XCD's L2, a batch of unequal sequences splits evenly over the XCDs, and with
+// causal masks a sequence's workgroups start with the KV blocks the most Q blocks see.
 //
 // Every HBM load of the workgroup is issued first, V rows in the transposition layout (a thread
 // takes 4 consecutive keys of 8 channels) and K rows in the layout of the Delta_S MFMA operand
@@ -413,9 +414,10 @@ __global__ __launch_bounds__(256, 3) void kv_quant(const T* __restrict__ k, cons
   const int w = __builtin_amdgcn_readfirstlane(tid / 64);
   const int r = lane & 31, hl = lane >> 5;
   const int L = xcd_remap(blockIdx.x, gridDim.x);
-  const int kb = L % nkb;
-  const size_t bh = L / nkb;                   // (sequence, kv head)
-  const int sidx = (int)bh / g.Hkv, hk = (int)bh % g.Hkv;
+  const int kb = L % nkb, hs = L / nkb;        // hs = kv head * B + sequence
+  const int nseq = (int)(gridDim.x / ((unsigned)nkb * g.Hkv));
+  const int hk = hs / nseq, sidx = hs % nseq;
+  const size_t bh = (size_t)sidx * g.Hkv + hk;  // (sequence, kv head) of the statistics
   const Seq sq = g.seq(sidx);
   const int nqb = seq_blocks(sq);
   if (kb >= nqb) return;

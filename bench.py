@@ -429,6 +429,11 @@ def main() -> int:
     line["environment"] = environment()
     line["environment"]["gpu_clocks_under_load"] = clocks_under_load(step)
     line["environment"]["gpu_clocks_idle_after"] = smi_clocks()
+    line["environment"]["gpu_clocks_note"] = (
+        "clocks as amd-smi reports them (one per XCD) while steps run back to back and after; on the "
+        "boxes measured so far it reported ~100 MHz in both cases, so these values do not track the "
+        "kernels' clock.  The hardware counters do: GRBM_GUI_ACTIVE per XCD over the dispatch time gives "
+        "1.8-2.0 GHz during the attention kernel (profiles/attn_fwd_counters.md).")
     if not args.no_cpu_baseline:
         if varlen:                      # one head of the longest sequence
             s = int(np.argmax(w.lens))

@@ -73,12 +73,10 @@ int check_problem(const sage_problem_t* p, sage::Dims* D, std::vector<sage::Seq>
     if ((double)tot_pad * H * d > 9.0e18 || (double)tot_ds * 4.0 > 9.0e18) return SAGE_ERR_INVALID_ARG;
   }
   const long long npad = (nmax + 127) / 128 * 128;
-  // 1-D grids: the attention kernel (Q blocks of every head) and the statistics + Q prologue
-  // launch (256-token tiles of every kv head, then the Q blocks)
-  if ((double)B * H * (double)(npad / 128) + (double)B * Hkv * (double)((nmax + 255) / 256) > 2147483647.0)
-    return SAGE_ERR_INVALID_ARG;
-  // the Delta_S launch: (32 or 64 Q blocks, 256 keys) tiles of every head
-  if ((double)B * H * (double)((npad / 128 + 31) / 32) * (double)((npad + 255) / 256) > 2147483647.0)
+  // 1-D grids: the statistics + Q prologue launch (128-token tiles of every kv head, then the Q
+  // blocks of every head) is the largest; the attention launch (Q blocks of every head) and the
+  // K/V codes + Delta_S launch (KV blocks of every kv head) are parts of it
+  if ((double)B * H * (double)(npad / 128) + (double)B * Hkv * (double)((nmax + 127) / 128) > 2147483647.0)
     return SAGE_ERR_INVALID_ARG;
   D->B = B; D->H = H; D->Hkv = Hkv; D->N = (int)nmax; D->d = d; D->causal = p->causal;
   D->qk_bits = p->qk_bits; D->pv_bits = p->pv_bits;

@@ -460,9 +460,9 @@ def test_varlen_full_size_sampled(sa):
 
 
 def test_varlen_long_and_short_sequences(sa):
-    """Mostly long sequences (the Delta_S launch takes 64-Q-block tiles) next to a short one:
-    every sequence bit-identical to its fixed-length call (whose launch may tile differently),
-    sampled Q blocks of both heads against the oracle."""
+    """Mostly long sequences (their early KV blocks take four 32-Q-block Delta_S tiles per query
+    head) next to a short one: every sequence bit-identical to its fixed-length call (whose
+    launch orders the work differently), sampled Q blocks of both heads against the oracle."""
     from workloads import VarlenWorkload, make_varlen_inputs
     w = VarlenWorkload("varlen-long", (13000, 5000, 200), 2, 1, 64, True, 8, q_bias_std=1.0)
     _say(f"[case varlen-long] lens {w.lens} H{w.H} Hkv{w.Hkv} d{w.d} causal={w.causal}")

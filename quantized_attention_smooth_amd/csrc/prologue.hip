@@ -37,17 +37,13 @@ struct In8 {
   __device__ float f(int e) const { return bits_to_float<T>(b[e]); }
 };
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 template <typename T>
 __device__ inline In8<T> load8(const T* p) {
   In8<T> r;
   *reinterpret_cast<uint4*>(r.b) = *reinterpret_cast<const uint4*>(p);
   return r;
-}
-
-__device__ inline float wave_max(float x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m, 64));
-  return x;
 }
 
 // INT4-range codes (|code| <= 7) go to the attention kernel as OCP FP6 E2M3 numbers, which hold
@@ -62,21 +58,36 @@ __device__ inline uint32_t e2m3_bits(float x) {        // x integer in [-7, 7]
   return mag | (x < 0.f ? 0x20u : 0u);
 }
 
-// Store the 8 codes of channels 8 cq .. 8 cq + 7 of one row (row points at its d code bytes).
-// FP6: the four threads of a 32-channel slot are consecutive lanes (cq & 3 = 0..3); they swap
-// their 48-bit packs so that each writes one aligned 8-byte word of the slot.
+// INT8 code of gamma: round half to even of v = RN32(gamma * inv) (|v| <= 127 up to that rounding)
+// and clamp to [-127, 127].  Adding 1.5 * 2^23 to v rounds it to an integer held in the low
+// mantissa bits (the fp32 spacing there is 1), so the clamp is an integer one and the code is the
+// low byte.  The product is rounded on its own first: fused into the addition it could round a
+// value just off a half-integer the other way.
+__device__ inline int8_t int8_code(float gamma, float inv) {
+#pragma clang fp contract(off)
+  const float v = gamma * inv;
+  constexpr int M = 0x4B400000;                  // bits of 1.5 * 2^23
+  const int b = __float_as_int(v + 12582912.0f);
+  return (int8_t)(min(max(b, M - 127), M + 127) - M);
+}
+
+// Store the codes of channels 8 cq .. 8 cq + 7 of one row (row points at its d code bytes): gamma
+// times inv = R / max|gamma|, R = 127 (INT8) or 7 (FP6), rounded half to even and clamped to
+// [-R, R].  FP6: the four threads of a 32-channel slot are consecutive lanes (cq & 3 = 0..3); they
+// swap their 48-bit packs so that each writes one aligned 8-byte word of the slot.
 template <bool FP6>
-__device__ inline void store_codes(int8_t* row, int cq, const float (&x)[8]) {
+__device__ inline void store_codes(int8_t* row, int cq, const float (&gamma)[8], float inv) {
   if (!FP6) {
     union { int8_t c[8]; uint2 u; } out;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) out.c[e] = (int8_t)(int)x[e];
+    for (int e = 0; e < 8; ++e) out.c[e] = int8_code(gamma[e], inv);
     *reinterpret_cast<uint2*>(row + cq * 8) = out.u;
     return;
   }
   unsigned long long mine = 0;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) mine |= (unsigned long long)e2m3_bits(x[e]) << (6 * e);
+  for (int e = 0; e < 8; ++e)
+    mine |= (unsigned long long)e2m3_bits(__builtin_amdgcn_fmed3f(rintf(gamma[e] * inv), -7.f, 7.f)) << (6 * e);
   const int j = cq & 3;
   // slot bits [48 t, 48 t + 48) hold thread t's pack; word j covers bits [64 j, 64 j + 64)
   const unsigned long long nxt = __shfl_down(mine, 1, 4);   // pack of thread j + 1 (same slot)
@@ -305,7 +316,7 @@ __device__ inline void copyout_v16(const uint8_t* vt, uint8_t* __restrict__ dst,
 
 // ---------------------------------------------------------------------------------------
 // Delta_S[qb, j] = sum_c mu_Q[qb, c] * gamma_K[j, c], stored times log2(e)/sqrt(d), is formed
-// inside kv_quant (below), where the workgroup has just read the keys' rows.
+// inside kv_quant (below), from the gamma_K that workgroup computes for the K codes.
 //
 // A GEMM (Q blocks x keys x channels) on the bf16 MFMA at fp32-class accuracy: both fp32
 // factors are split exactly into three bf16 parts, x = x1 + x2 + x3 (8 significant bits each,
@@ -362,7 +373,6 @@ __device__ inline void store_or_drop(float* base, uint32_t bytes, uint32_t off, 
 }
 constexpr uint32_t kDropOffset = 0xFFFFFF00u;   // past any resource here (all are below 2^31 bytes)
 
-
 // ---------------------------------------------------------------------------------------
 // One KV block of 128 keys of one (sequence, kv head): K smoothing + quantization, V FP8
 // quantization (or the fp16 V layout), and the Delta_S columns of these keys for every Q block
@@ -401,9 +411,11 @@ __global__ __launch_bounds__(256, 3) void kv_quant(const T* __restrict__ k, cons
   constexpr int ROW = 3 * D * 2 + 16;
   constexpr int AT = 32 * ROW;                 // a tile of 32 Q blocks
   constexpr int VT = BK * D * (PV16 ? 2 : 1);  // V transposition buffer
-  constexpr int CPQ = 3 * D / 8;               // 16-byte chunks of data per Q block
-  constexpr int CPR = ROW / 16;                // 16-byte chunks per LDS row (the last is padding)
-  constexpr int NLI = (32 * CPR + 255) / 256;  // tile load instructions per wave
+  // 16-byte chunks of data per Q block, per LDS row (the last one padding), and the tile load
+  // instructions per wave (used by device code only)
+  [[maybe_unused]] constexpr int CPQ = 3 * D / 8;
+  [[maybe_unused]] constexpr int CPR = ROW / 16;
+  [[maybe_unused]] constexpr int NLI = (32 * CPR + 255) / 256;
   __shared__ float red[WAVES][2];
   __shared__ __attribute__((aligned(16))) float smk[D];   // mu_K
   __shared__ __attribute__((aligned(16))) float smv[D];   // V_r / max|V| (0 for an all-zero channel)
@@ -479,7 +491,7 @@ __global__ __launch_bounds__(256, 3) void kv_quant(const T* __restrict__ k, cons
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          x[i][e] = jl0 + i < nvalid ? fminf(fmaxf(vr[p][i].f(e) * vinv[e], -V_RANGE), V_RANGE) : 0.f;
+          x[i][e] = jl0 + i < nvalid ? __builtin_amdgcn_fmed3f(vr[p][i].f(e) * vinv[e], -V_RANGE, V_RANGE) : 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int c = cq * 8 + e;
@@ -576,7 +588,7 @@ __global__ __launch_bounds__(256, 3) void kv_quant(const T* __restrict__ k, cons
     for (int ks = 0; ks < KS; ++ks) {
       union { int8_t c[8]; uint2 u; } out;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) out.c[e] = (int8_t)(int)fminf(fmaxf(rintf(gk[ks][e] * inv), -R), R);
+      for (int e = 0; e < 8; ++e) out.c[e] = int8_code(gk[ks][e], inv);
       *reinterpret_cast<uint2*>(krow + 16 * ks + 8 * hl) = out.u;
     }
   } else {
@@ -592,7 +604,8 @@ __global__ __launch_bounds__(256, 3) void kv_quant(const T* __restrict__ k, cons
         pk[o] = 0;
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          pk[o] |= (unsigned long long)e2m3_bits(fminf(fmaxf(rintf(gk[2 * m + o][e] * inv), -R), R)) << (6 * e);
+          pk[o] |= (unsigned long long)e2m3_bits(__builtin_amdgcn_fmed3f(rintf(gk[2 * m + o][e] * inv), -R, R))
+                   << (6 * e);
       }
       const unsigned long long got = __shfl_xor(hl == 0 ? pk[1] : pk[0], 32, 64);
       // half 0: pk = {pack 0, pack 2}, got = pack 1;  half 1: pk = {pack 1, pack 3}, got = pack 2
@@ -687,8 +700,7 @@ __device__ inline void q_quant_body(const T* __restrict__ q, int8_t* __restrict_
   const Seq sq = g.seq(sidx);
   if (qb >= seq_blocks(sq)) return;
   const int N = sq.n;
-  const long long ts = g.st.qt;
-  const T* qbase = q + sidx * g.st.qb + (long long)sq.tok0 * ts + h * g.st.qh;
+  [[maybe_unused]] const long long ts = g.st.qt;   // token stride (device code only)
   const size_t rows = rows_off(sq, g.H, h), blk = blocks_off(sq, g.H, h) + qb;
   const int nvalid = min(BQ, N - qb * BQ);
 
@@ -702,21 +714,30 @@ __device__ inline void q_quant_body(const T* __restrict__ q, int8_t* __restrict_
     for (int i = tid; i < D * kLimbs; i += 256) acc[i] = 0ull;
     __syncthreads();
   }
-  // every load is issued before any is used: rows past N read row N - 1 (in bounds) and are
-  // zeroed afterwards, so no load sits behind a branch that would wait for it on its own
+  // every load is issued before any is used, through one buffer resource over the block's rows:
+  // rows past the sequence read as zeros, so they add nothing to the sums (their codes are formed
+  // like the others', and no output row reads them).  The block spans under 2^31 bytes (127 row
+  // strides of at most 2^16 heads x 128 channels).
   In8<T> raw[PASSES];
+#if defined(__HIP_DEVICE_COMPILE__)
+  {
+    const T* bbase = q + sidx * g.st.qb + ((long long)sq.tok0 + (long long)qb * BQ) * ts + h * g.st.qh;
+    const auto rs = make_rsrc(bbase, (uint32_t)(((long long)(nvalid - 1) * ts + D) * 2));
 #pragma unroll
-  for (int p = 0; p < PASSES; ++p)
-    raw[p] = load8(qbase + min(qb * BQ + p * RPP + r0, N - 1) * ts + cq * 8);
+    for (int p = 0; p < PASSES; ++p) {
+      const uint32_t off = (uint32_t)(((long long)(p * RPP + r0) * ts + cq * 8) * 2);
+      *reinterpret_cast<u32x4*>(raw[p].b) = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+    }
+  }
+#endif
 #pragma unroll
   for (int p = 0; p < PASSES; ++p) {
-    const bool valid = qb * BQ + p * RPP + r0 < N;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      x[p][e] = valid ? raw[p].f(e) : 0.f;
+      x[p][e] = raw[p].f(e);
       if (!BF) s[e] += (double)x[p][e];
     }
-    if (BF && valid) {
+    if (BF && p * RPP + r0 < nvalid) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) superacc_add(&acc[(cq * 8 + e) * kLimbs], raw[p].b[e]);
     }
@@ -750,24 +771,38 @@ __device__ inline void q_quant_body(const T* __restrict__ q, int8_t* __restrict_
   float mu[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) mu[e] = lmu[cq * 8 + e];
+  // gamma_Q = RN32(Q - mu_Q) and each row's max |gamma_Q| (over the row's TPR lanes)
+  float am[PASSES];
 #pragma unroll
   for (int p = 0; p < PASSES; ++p) {
-    const int row = qb * BQ + p * RPP + r0;
-    const bool valid = row < N;
-    float am = 0.f;
+    float a = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      x[p][e] = valid ? x[p][e] - mu[e] : 0.f;   // gamma_Q = RN32(Q - mu_Q)
-      am = fmaxf(am, fabsf(x[p][e]));
+      x[p][e] -= mu[e];
+      a = fmaxf(a, fabsf(x[p][e]));
     }
 #pragma unroll
-    for (int m = TPR / 2; m >= 1; m >>= 1) am = fmaxf(am, __shfl_xor(am, m, 64));
-    const float inv = am > 0.f ? R / am : 0.f;
-    float y[8];
+    for (int m = TPR / 2; m >= 1; m >>= 1) a = fmaxf(a, __shfl_xor(a, m, 64));
+    am[p] = a;
+  }
+  // One correctly rounded R / max and max / R per row, not per pass and lane: a wave holds G rows
+  // per pass, PASSES * G = 32 rows in all, and lane l < 32 takes row group l % G of pass l / G
+  // (its maximum from that group's first lane), then hands its quotient back to the row's lanes.
+  constexpr int G = 64 / TPR;
+  static_assert(PASSES * G == 32, "32 rows per wave");
+  const int lane = tid % 64, w = tid / 64;
+  float own = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) y[e] = fminf(fmaxf(rintf(x[p][e] * inv), -R), R);
-    store_codes<QK4>(qcodes + (rows + row) * D, cq, y);
-    if (cq == 0) qscale[rows + row] = am / R;
+  for (int p = 0; p < PASSES; ++p) {
+    const float a = __shfl(am[p], (lane % G) * TPR, 64);
+    if (lane / G == p) own = a;
+  }
+  const float own_inv = own > 0.f ? R / own : 0.f;
+  if (lane < 32) qscale[rows + qb * BQ + (lane / G) * RPP + w * G + lane % G] = own / R;
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const float inv = __shfl(own_inv, p * G + lane / TPR, 64);
+    store_codes<QK4>(qcodes + (rows + qb * BQ + p * RPP + r0) * D, cq, x[p], inv);
   }
 }
 

@@ -199,8 +199,9 @@ int sage_quant_debug_ex(const sage_problem_t* p, const void* q, const void* k, c
 /*
  * Test/debug: run the prologue, then the attention kernel's own integer-MFMA QK^T code
  * path for query block qb of (b, h) against KV block kb, and copy the raw int32
- * accumulators to tile_out (device, int32 [bq, bk], row = query, column = key; rows
- * past N and keys past N hold the products of the zero padding codes).
+ * accumulators to tile_out (device, int32 [bq, bk], row = query, column = key; keys past N
+ * hold products with K's zero padding codes, rows past N products of the padded query rows'
+ * codes, which no output reads).
  */
 int sage_qk_tile_debug(const void* q, const void* k, const void* v, int B, int H, int Hkv, int N,
                        int d, int causal, int qk_bits, int pv_bits, void* workspace,

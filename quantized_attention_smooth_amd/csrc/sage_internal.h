@@ -66,7 +66,8 @@ struct Dims {
 //           pv_bits 16: fp16 per s: [Hkv][Npad_s/16][d][16]  V itself, transposed per 16-key
 //           group; slot 8*((kk/4)%2) + 4*(kk/8) + kk%4 holds key kk of the group: the k-slot
 //           order of the fp16 MFMA B operand built from the S^T accumulators
-//  qcodes : int8  per s: [H][Npad_s][d]        (INT4 range: packed FP6 E2M3, as kcodes)
+//  qcodes : int8  per s: [H][Npad_s][d]        (INT4 range: packed FP6 E2M3, as kcodes); rows
+//           past n hold codes of -mu_Q that no output reads
 //  kscale : fp32  per s: [Hkv][nb_s][2]        delta_K per (KV block, lane half)
 //  qscale : fp32  per s: [H][Npad_s]           delta_Q per query row
 //  muk    : fp32  [B][Hkv][d]

@@ -311,15 +311,16 @@ __device__ inline void qk_tiles(const SM& sm, int st, const v4i (&qreg)[D / 32],
   }
 }
 
-// GROUPS = 2 (FP8 mode, d = 128, non-causal): one workgroup of 8 waves takes two Q blocks of the
-// same (sequence, head), 4 waves each, and every K/V tile is loaded once for both.  A CU then
+// GROUPS = 2 (FP8 mode, d = 128): one workgroup of 8 waves, two groups of 4, and every K/V tile is
+// loaded once for both groups.  Non-causal: two Q blocks of the same (sequence, head).  A CU then
 // holds one such workgroup instead of two independent ones, so its two Q blocks run in step and
 // finish together (two independent workgroups on a CU finish at different times, the older one
-// being served first, and the last one of a round then runs alone).
+// being served first, and the last one of a round then runs alone).  Causal (fixed-length GQA
+// batches): the same Q block of two query heads of one kv head, whose work is identical, so the
+// K/V tiles of a kv head are fetched once per pair of query heads.
 template <int D, bool CAUSAL, bool DUMP, bool QK4, bool PV16, bool BF, int GROUPS>
 __global__ __launch_bounds__(256 * GROUPS, GROUPS == 1 ? 2 : 1) void attn_fwd(AttnArgs a) {
-  static_assert(GROUPS == 1 || (!PV16 && !DUMP && !CAUSAL && D == 128),
-                "two Q blocks per workgroup: FP8 mode, d = 128, non-causal");
+  static_assert(GROUPS == 1 || (!PV16 && !DUMP && D == 128), "two groups per workgroup: FP8 mode, d = 128");
   typedef PV16T<BF> PT;
   __shared__ Smem<D, PV16, GROUPS> sm;
   const int tid = threadIdx.x, lane = tid & 63, col = lane & 31, half = lane >> 5;
@@ -333,6 +334,17 @@ __global__ __launch_bounds__(256 * GROUPS, GROUPS == 1 ? 2 : 1) void attn_fwd(At
   if (DUMP) {
     b = a.dbg_b; h = a.dbg_h; qb = a.dbg_qb;
     sq = a.g.seq(b);
+  } else if (GROUPS == 2 && CAUSAL) {
+    // query-head pairs, in the order below with pairs in place of single heads
+    const int G = H / Hkv, pairs = G / 2;
+    const int total = a.B * (H / 2) * a.nqb;
+    const int L = xcd_remap(blockIdx.x, total);
+    const int pr = L % pairs, r = L / pairs;
+    const int qi = r % a.nqb, kbi = r / a.nqb;
+    b = kbi % a.B;
+    h = (kbi / a.B) * G + 2 * pr + gi;
+    sq = a.g.seq(b);
+    qb = seq_blocks(sq) - 1 - qi;               // longest rows first
   } else {
     // kv-head-major order: each XCD's contiguous share holds whole kv heads of every sequence,
     // so varlen batches split evenly and a kv head's codes stay in one XCD's L2; within it the
@@ -683,10 +695,14 @@ AttnArgs make_args(const Dims& D, const Ptrs& P) {
 template <int DD, bool QK4, bool PV16, bool BF>
 hipError_t launch_d(const Dims& D, const AttnArgs& a, hipStream_t s) {
   // FP8 mode at d = 128, non-causal: two Q blocks per workgroup sharing every K/V tile (causal
-  // pairs measured slower: the second block is one shorter and idles on the last one)
+  // Q-block pairs measured slower: the second block is one shorter and idles on the last one)
   if constexpr (!PV16 && DD == 128) {
     if (!D.causal)
       return launch(attn_fwd<DD, false, false, QK4, PV16, BF, 2>, dim3(D.B * D.H * ((D.nqb + 1) / 2)), dim3(512), s, a);
+    // causal GQA with an even number of query heads per kv head, fixed-length batches (in varlen
+    // batches the pairs measured slower): two query heads of a kv head per workgroup
+    if (!D.varlen && (D.H / D.Hkv) % 2 == 0)
+      return launch(attn_fwd<DD, true, false, QK4, PV16, BF, 2>, dim3(D.B * (D.H / 2) * D.nqb), dim3(512), s, a);
   }
   const int grid = D.B * D.H * D.nqb;
   if (D.causal) return launch(attn_fwd<DD, true, false, QK4, PV16, BF, 1>, dim3(grid), dim3(256), s, a);

@@ -126,6 +126,7 @@ SMALL = [
     ("n129-causal", custom(1, 2, 1, 129, 128, True, 8, q_bias_std=1.0)),
     ("d128-int4", custom(1, 2, 2, 520, 128, False, 4, q_bias_std=1.0)),
     ("d64-causal-int8", custom(1, 2, 1, 520, 64, True, 8, q_bias_std=1.0)),
+    ("gqa-d128-causal-int4", custom(1, 4, 2, 520, 128, True, 4, q_bias_std=1.0)),
 ]
 
 

@@ -183,6 +183,36 @@ def test_small_case_full_parity(sa, name, w, pv_bits):
     _full_parity(sa, name, q, k, v, w.causal, w.qk_bits, pv_bits)
 
 
+def _random_cases(n=24, seed=2024):
+    """Seeded random small configurations over every switch of the path: batch, GQA group size,
+    ragged length (including 1 and block multiples), head dim, causal, QK code width, P V width,
+    and the channel-bias strengths of the input recipe."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        B, Hkv, G = int(rng.integers(1, 3)), int(rng.integers(1, 3)), int(rng.choice([1, 2, 3, 4]))
+        N = int(rng.integers(2, 700)) if rng.random() < 0.5 else int(rng.choice([1, 127, 128, 129, 256]))
+        d, causal = int(rng.choice([64, 128])), bool(rng.integers(0, 2))
+        bits, pv = int(rng.choice([4, 8])), int(rng.choice([8, 16]))
+        kb, qbias = float(rng.choice([0.0, 1.0, 4.0])), float(rng.choice([0.0, 1.0]))
+        w = custom(B, Hkv * G, Hkv, N, d, causal, bits, k_bias_std=kb, q_bias_std=qbias)
+        name = f"r{i}-B{B}-H{Hkv * G}-Hkv{Hkv}-N{N}-d{d}-{'c' if causal else 'f'}-int{bits}-pv{pv}"
+        out.append((name, w, pv))
+    return out
+
+
+RANDOM = _random_cases()
+
+
+@pytest.mark.parametrize("name,w,pv_bits", RANDOM, ids=[c[0] for c in RANDOM])
+def test_random_shapes_full_parity(sa, name, w, pv_bits):
+    """Every prologue tensor, every output element and every raw S tile of the last head, against
+    the oracle, on seeded random shapes."""
+    _say(f"[case {name}]")
+    q, k, v = make_inputs(w, seed=5)
+    _full_parity(sa, name, q, k, v, w.causal, w.qk_bits, pv_bits)
+
+
 def _degenerate(name):
     """Inputs for the method's degenerate cases (seed 11): all zero; zero V; every key equal (so
     gamma_K = 0: zero K groups, scales and Delta_S) with one Q block of equal rows (zero Q

@@ -6,11 +6,13 @@
 // of P~V.  zhaifeiyue.github.io commentary on arXiv 2411.10958: the paper's Sec. 3.4 finds the
 // FP8 matrix-instruction accumulator narrower than fp32 and accumulates each block locally
 // before an fp32 global sum; per-thread scales must follow the matrix-instruction layout.
-// pith.science verdict on arXiv 2505.21136, keys "key_machinery" (static delta_P = 1/P_r
-// since max P~ = 1 per block; per-channel delta_V) and "supporting_citations" (online
-// softmax and FlashAttention tiling).
+// pith.science verdict on arXiv 2505.21136, keys "key_machinery" (delta_P and per-channel
+// delta_V; here the static delta_P = 1/P_r: every p = 2^(z - m) with the running maximum m is at
+// most 1, so p * P_r never exceeds P_r) and "supporting_citations" (online softmax and
+// FlashAttention tiling).
 //
-// Design (one workgroup = 128 queries of one (b, h); 4 waves x 32 queries):
+// Design (a group of 4 waves x 32 queries = the 128 queries of one Q block of one (b, h); a
+// workgroup holds one group, or two that share every K/V tile, see attn_fwd):
 //   * S^T = K Q^T on v_mfma_i32_32x32x32_i8 (the full-rate int8 shape on gfx950): A = K tile
 //     from LDS, B = the wave's 32 query rows held in VGPRs for the whole KV loop.  Lane l owns
 //     query column i = l % 32 and keys 8a + 4(l / 32) + r of every 32-key tile, so one

@@ -127,6 +127,11 @@ SMALL = [
     ("d128-int4", custom(1, 2, 2, 520, 128, False, 4, q_bias_std=1.0)),
     ("d64-causal-int8", custom(1, 2, 1, 520, 64, True, 8, q_bias_std=1.0)),
     ("gqa-d128-causal-int4", custom(1, 4, 2, 520, 128, True, 4, q_bias_std=1.0)),
+    # one kv head for many query heads (16: the causal query-head pairs; 12 at d = 64), and a
+    # batch of eight short causal sequences
+    ("mqa-d128-causal-int8", custom(1, 16, 1, 300, 128, True, 8, q_bias_std=1.0)),
+    ("mqa-d64-int8", custom(2, 12, 1, 260, 64, False, 8)),
+    ("batch8-n65-d128-causal", custom(8, 2, 2, 65, 128, True, 8)),
 ]
 
 
@@ -423,6 +428,10 @@ VARLEN = [
     ("varlen-d64-int4", [200, 64, 700], 2, 1, 64, False, 4, 8),
     ("varlen-d128-causal-pv16", [130, 257, 5], 2, 2, 128, True, 8, 16),
     ("varlen-d64-int4-pv16", [384, 33], 4, 4, 64, False, 4, 16),
+    ("varlen-20-short-d128-causal", [1, 1, 2, 3, 5, 8, 13, 21, 34, 55, 89, 144, 233, 1, 128, 129, 64, 65, 300, 7],
+     4, 2, 128, True, 8, 8),
+    ("varlen-20-short-d64-int4", [7, 300, 65, 64, 129, 128, 1, 233, 144, 89, 55, 34, 21, 13, 8, 5, 3, 2, 1, 1],
+     2, 1, 64, False, 4, 8),
 ]
 
 

@@ -43,7 +43,6 @@ int check_problem(const sage_problem_t* p, sage::Dims* D, std::vector<sage::Seq>
   if (d != 64 && d != 128) return SAGE_ERR_UNSUPPORTED;
   if (p->qk_bits != 4 && p->qk_bits != 8) return SAGE_ERR_UNSUPPORTED;
   if (p->pv_bits != 8 && p->pv_bits != 16) return SAGE_ERR_UNSUPPORTED;
-  if ((double)B * Hkv > 65535.0 || (double)B * H > 65535.0) return SAGE_ERR_INVALID_ARG;   // grid.y/z limits
 
   // per-sequence lengths: one N for all, or the differences of cu_seqlens
   long long nmax = 0, tot_pad = 0, tot_ds = 0, total = 0;

@@ -63,6 +63,8 @@ def test_workspace_bytes(pkg):
     # codes (K, V, Q) + Delta_S dominate: 3 * 256*64*2 + 2*2*256*4 bytes at least
     assert n1 >= 3 * 256 * 64 * 2 + 2 * 2 * 256 * 4
     assert pkg.workspace_bytes(1, 2, 2, 257, 64, False, 8) > n1           # one more 128-row block
+    # every launch is a 1-D grid: batch x heads beyond 65535 is a valid problem
+    assert pkg.workspace_bytes(1100, 64, 8, 3, 64, True, 8) > 0
     # causal stores only the Delta_S triangle: about half of the non-causal 9.7 GB
     causal, full = pkg.workspace_bytes(1, 32, 8, 98304, 128, True, 8), pkg.workspace_bytes(1, 32, 8, 98304, 128, False, 8)
     assert 4.5 * 2 ** 30 < causal < 6 * 2 ** 30 < 9 * 2 ** 30 < full

@@ -352,6 +352,26 @@ def test_full_size_sampled_parity(sa, name, pv_bits):
     torch.cuda.empty_cache()
 
 
+def test_batch_times_heads_beyond_65535(sa):
+    """1100 sequences x 64 query heads (70400 (sequence, head) pairs, past any 16-bit grid
+    dimension) of 3 tokens: sampled heads' prologue tensors and outputs against the oracle."""
+    w = custom(1100, 64, 8, 3, 64, True, 8, q_bias_std=1.0)
+    _say(f"[case batch-heads] B{w.B} H{w.H} Hkv{w.Hkv} N{w.N} d{w.d} causal")
+    q, k, v = make_inputs(w, seed=3)
+    qd, kd, vd = _to_dev(q, k, v)
+    o = sa.sageattn(qd, kd, vd, is_causal=True, qk_bits=8, pv_bits=8)
+    dbg = {n: t for n, t in sa.quant_debug(qd, kd, vd, True, 8, 8).items() if t is not None}
+    torch.cuda.synchronize()
+    for b, h in [(0, 0), (0, 63), (549, 37), (1099, 0), (1099, 63)]:
+        hk = h // (w.H // w.Hkv)
+        ph = osage.prologue(*_head_slice(q, k, v, b, h, w.H, w.Hkv), True, 8)
+        sub = {n: t[b:b + 1, (hk if n in ("mu_k", "k_codes", "k_scales", "v_codes", "v_scales") else h):][:, :1].cpu().numpy()
+               for n, t in dbg.items()}
+        _check_prologue(sub, ph, 0, 0, 0, f"batch-heads b{b} h{h}")
+        _check_o(o[b, h].cpu().numpy(), osage.attend_block(ph, 0, 0, 0), f"batch-heads b{b} h{h}",
+                 _slack(ph, 0, 0, 0, 8))
+
+
 def test_int4_extreme_codes_exact(sa):
     """INT4-range QK^T runs on the FP6 MFMA with E2M3 codes.  Inputs of +-1 whose block and
     sequence means are zero make every code +-7, so S reaches its largest magnitude 49 d; the

@@ -3,16 +3,18 @@
 Every mutation is applied to the oracle on the CPU (monkeypatch), the pins below are run,
 and the test passes only if some pin fails.  This shows that the pins constrain the parts
 of the oracle they claim to pin: a dropped or sign-flipped Delta_S, a wrong GQA head map,
-an off-by-one causal mask, a wrong softmax scale, a lost V scale, a wrong K group shape and
-a missed rescale of the running row sum.
+an off-by-one causal mask, a wrong softmax scale, a lost V scale, a wrong K group shape, a
+missed rescale of the running row sum, a mean divided by n + 1, codes truncated instead of
+rounded, an FP8 codec that saturates at 240, and smoothing skipped while its bias is kept.
 """
 import math
 
 import numpy as np
 import pytest
 
-from oracle import sage
+from oracle import fp8, sage
 import test_oracle_attention as A
+import test_oracle_fp8 as F
 import test_oracle_quant as Qt
 
 
@@ -24,6 +26,10 @@ def _pins():
     yield lambda: A.test_brute_force_tiny(True, 7)
     yield lambda: A.test_k_shift_invariance_exact_and_bitwise()
     yield lambda: Qt.test_default_groups_follow_lane_layout()
+    yield lambda: Qt.test_mean_is_order_free_and_within_one_ulp()
+    yield lambda: Qt.test_dequant_error_bound_and_code_range()
+    yield lambda: F.test_rne_ties_and_saturation(432.0, 0x7E)
+    yield lambda: F.test_nearest_by_brute_force()
 
 
 def _caught():
@@ -57,7 +63,17 @@ MUTATIONS = {
     "k_group_too_wide": lambda mp: _wrap(
         mp, "group_ids", lambda f, n, s, p, r: f(n, s, p, r * 2)),
     "row_sum_not_rescaled": lambda mp: mp.setattr(np, "exp", _exp_one_for_alpha),
+    "mean_divides_by_n_plus_1": lambda mp: _wrap(
+        mp, "exact_mean", lambda f, x: (f(x) * np.float32(x.shape[0] / (x.shape[0] + 1))).astype(np.float32)),
+    "codes_truncated": lambda mp: mp.setattr(np, "rint", np.trunc),
+    "fp8_saturates_at_240": lambda mp: _wrap_fp8(mp, lambda f, x: f(np.clip(np.asarray(x), -240.0, 240.0))),
+    "smoothing_skipped": lambda mp: _wrap(mp, "smooth", lambda f, x, mu: f(x, 0 * np.asarray(mu))),
 }
+
+
+def _wrap_fp8(mp, fn):
+    orig = fp8.encode_sat
+    mp.setattr(fp8, "encode_sat", lambda *a, **kw: fn(orig, *a, **kw))
 
 
 def _mask_diag(z, pro, qb):

@@ -26,6 +26,7 @@ Other modes:
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import math
@@ -269,6 +270,8 @@ def main() -> int:
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--seq-len", type=int, default=None,
+                    help="sequence length N in place of a fixed-length workload's own (the metric spans N = 8K-32K)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -292,12 +295,17 @@ def main() -> int:
 
     pv = args.pv_bits
     varlen = args.workload in VARLEN_WORKLOADS
+    if varlen and args.seq_len:
+        print("--seq-len applies to fixed-length workloads only", file=sys.stderr)
+        return 2
     if varlen:
         w = VARLEN_WORKLOADS[args.workload]
         q, k, v = make_varlen_inputs(w, seed=0)
         pb = sa.Problem(w.B, w.H, w.Hkv, 0, w.d, w.causal, w.qk_bits, pv, "HND", cu_seqlens=w.cu_seqlens)
     else:
         w = WORKLOADS[args.workload]
+        if args.seq_len:
+            w = dataclasses.replace(w, N=args.seq_len, name=f"{w.name}@N{args.seq_len}")
         q, k, v = make_inputs(w, seed=0)
         pb = sa.Problem(w.B, w.H, w.Hkv, w.N, w.d, w.causal, w.qk_bits, pv, "HND")
     dev = torch.device("cuda:0")
@@ -384,7 +392,7 @@ def main() -> int:
     torch.cuda.synchronize()
     copy_cold_ms = float(np.mean([c0.elapsed_time(c1) for c0, c1 in copies]))
     del flush, copy_src, copy_dst
-    traffic = _traffic(args.workload, pv)
+    traffic = _traffic(w.name if args.seq_len else args.workload, pv)
     peak = attn_peak(w.qk_bits, pv)
     meas = measured_peaks(dev, w.qk_bits, pv)
     qk_t = "int8" if w.qk_bits == 8 else "fp6 (INT4-range codes)"

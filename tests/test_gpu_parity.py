@@ -372,6 +372,38 @@ def test_batch_times_heads_beyond_65535(sa):
                  _slack(ph, 0, 0, 0, 8))
 
 
+def test_long_causal_sequence_delta_s_beyond_4gib(sa):
+    """2^19 + 77 tokens, causal, two query heads on one kv head: each head's Delta_S triangle is
+    4.3 GB, so the second head's lies more than 4 GiB past the workspace section's start (64-bit
+    offsets; 32-bit offsets only inside a 32-row store tile).  The first Q block of both heads
+    and the ragged last one of the second against the oracle, and raw int32 tiles of the second."""
+    N = (1 << 19) + 77
+    w = custom(1, 2, 1, N, 64, True, 8, q_bias_std=1.0)
+    _say(f"[case long-causal] B1 H2 Hkv1 N{N} d64 causal")
+    q, k, v = make_inputs(w, seed=11)
+    qd, kd, vd = _to_dev(q, k, v)
+    assert sa.workspace_bytes(1, 2, 1, N, 64, True, 8) > 2 * 4.29e9
+    o = sa.sageattn(qd, kd, vd, is_causal=True, qk_bits=8, pv_bits=8)
+    torch.cuda.synchronize()
+    nqb = -(-N // 128)
+    _say("  oracle prologue")
+    pro = osage.prologue(q, k, v, True, 8)
+    for h, qb in ((0, 0), (1, 0), (1, nqb - 1)):
+        _say(f"  h{h} qb{qb}")
+        r0, r1 = qb * 128, min(N, qb * 128 + 128)
+        _check_o(o[0, h, r0:r1].cpu().numpy(), osage.attend_block(pro, 0, h, qb), f"long-causal h{h} qb{qb}",
+                 _slack(pro, 0, h, qb))
+    for qb, kb in ((nqb - 1, 0), (nqb - 1, nqb - 1), (nqb // 2, nqb // 3)):
+        tile = sa.qk_tile_debug(qd, kd, vd, 0, 1, qb, kb, True, 8, 8).cpu().numpy()
+        r0, r1 = qb * 128, min(N, qb * 128 + 128)
+        c0, c1 = kb * 128, min(N, kb * 128 + 128)
+        np.testing.assert_array_equal(tile[:r1 - r0, :c1 - c0],
+                                      osage.scores_int(pro, 0, 1, slice(r0, r1), slice(c0, c1)),
+                                      err_msg=f"long-causal tile {qb},{kb}")
+    del o, qd, kd, vd
+    torch.cuda.empty_cache()
+
+
 def test_int4_extreme_codes_exact(sa):
     """INT4-range QK^T runs on the FP6 MFMA with E2M3 codes.  Inputs of +-1 whose block and
     sequence means are zero make every code +-7, so S reaches its largest magnitude 49 d; the

@@ -76,7 +76,7 @@ def attend_block_fp16acc(pro: sage.Prologue, b: int, h: int, qb: int) -> np.ndar
     for kb in range(pro.nkb):
         c0, c1 = kb * g.bk, min(pro.N, (kb + 1) * g.bk)
         zb = z[:, c0:c1]
-        m_new = np.maximum(m, zb.max(axis=1))
+        m_new = np.maximum(m, sage.block_top(zb, pro.max_ref))
         finite = np.isfinite(m_new)
         alpha = np.where(np.isfinite(m), np.exp(m - np.where(finite, m_new, 0.0)), 0.0)
         p = np.where(finite[:, None], np.exp(zb - np.where(finite, m_new, 0.0)[:, None]), 0.0)

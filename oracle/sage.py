@@ -35,7 +35,8 @@ What is computed, per (batch b, query head h); kv(h) = h div (H / Hkv):
   O8  V: per-channel amax over all N keys; delta_V = RN32(amax / V_r);
       V_q = E4M3sat(RN32(V * RN32(V_r / amax))) [SA2pp key_machinery].
   O9  online softmax over KV blocks of bk keys (FlashAttention tiling with the online
-      normalizer [SA2pp supporting_citations]): m' = max(m, blockmax z); alpha = e^(m - m');
+      normalizer [SA2pp supporting_citations]): m' = max(m, blockmax z) (reading: see
+      block_top); alpha = e^(m - m');
       p = e^(z - m'); P~_q = E4M3sat(RN32(p * P_r)) with the static range delta_P = 1 / P_r,
       valid because p <= 1 everywhere (reading: [SA2pp key_machinery] describes a per-block
       scale max(P~) / P_r instead, which equals 1 / P_r only in the block holding the running
@@ -217,6 +218,7 @@ class Prologue:
     smooth_q: bool
     smooth_k: bool
     row_sum: str               # "weights" (default) or "unquantized": see attend_block
+    max_ref: str               # "exact" (default) or "pow2": see block_top
     # per (b, kv head)
     mu_k: np.ndarray = field(repr=False)       # f32 [B, Hkv, d]
     gamma_k: np.ndarray = field(repr=False)    # f32 [B, Hkv, N, d]
@@ -246,17 +248,19 @@ class Prologue:
 
 def prologue(q, k, v, causal: bool = False, qk_bits: int = 8, geom: Geometry = DEFAULT, *,
              quant_qk: bool = True, quant_pv: bool = True, smooth_q: bool = True,
-             smooth_k: bool = True, row_sum: str = "weights") -> Prologue:
+             smooth_k: bool = True, row_sum: str = "weights", max_ref: str = "exact") -> Prologue:
     """Steps O1-O4 and O8 on fp16 inputs q [B,H,N,d], k/v [B,Hkv,N,d] (numpy float16), or on
     bf16 inputs (float32 arrays of bf16 values, see is_bf16).
 
     The switches turn parts of the method off; they exist so that tests can reduce the
     oracle to textbook attention (all off) and check each part against it.  row_sum selects
     the reading of the softmax row sum (see attend_block); only tests comparing the two
-    readings change it.
+    readings change it; max_ref likewise selects the running maximum's reading (see block_top).
     """
     if row_sum not in ("weights", "unquantized"):
         raise ValueError("row_sum must be 'weights' or 'unquantized'")
+    if max_ref not in ("pow2", "exact"):
+        raise ValueError("max_ref must be 'pow2' or 'exact'")
     q = np.asarray(q)
     k = np.asarray(k)
     v = np.asarray(v)
@@ -300,7 +304,7 @@ def prologue(q, k, v, causal: bool = False, qk_bits: int = 8, geom: Geometry = D
             q_codes[b, h], q_delta[b, h], _ = quantize_groups(gamma_q[b, h], qgid, R)
 
     return Prologue(B, H, Hkv, N, d, bool(causal), qk_bits, g, quant_qk, quant_pv, smooth_q,
-                    smooth_k, row_sum, mu_k, gamma_k, k_codes, k_delta, v_codes, v_delta, v_amax, v,
+                    smooth_k, row_sum, max_ref, mu_k, gamma_k, k_codes, k_delta, v_codes, v_delta, v_amax, v,
                     mu_q, gamma_q, q_codes, q_delta)
 
 
@@ -345,6 +349,32 @@ def logits(pro: Prologue, b: int, h: int, qb: int) -> np.ndarray:
 # --------------------------------------------------------------------------------------
 # O9 / O10
 # --------------------------------------------------------------------------------------
+LOG2E = 1.4426950408889634
+LN2 = 0.6931471805599453
+
+
+def block_top(zb: np.ndarray, max_ref: str) -> np.ndarray:
+    """O9: what a KV block contributes to the running maximum that the softmax subtracts: fp64
+    [rows] from the block's logits zb [rows, keys] (natural units, -inf where masked).
+
+    Reading (the pages name an online softmax with a running maximum [SA2pp supporting_citations]
+    and a static P~ range that needs p <= 1, but not which maximum): "exact", the default, is the
+    plain row maximum, so the largest weight of the block that sets it is p = 1 and its P~ is
+    exactly P_r.  "pow2" rounds it up to ln2 * ceil(log2(e) * max z), so that e^(z - m) =
+    2^(log2(e) z - k) with an integer k: the same unquantized softmax (any m at or above the row
+    maximum gives it, with every p <= 1), but the quantized weights P~ = E4M3(p * P_r) of that
+    block then scale by 2^(exact - pow2) in (1/2, 1] and its largest one is rounded too.  It is
+    kept for the test that holds both against exact attention (a GPU form of it would need no
+    per-element subtraction of the maximum).  The running maximum is the largest block top seen
+    so far (a ceiling of a maximum is the maximum of the ceilings).
+    """
+    top = zb.max(axis=1)
+    if max_ref == "exact":
+        return top
+    fin = np.isfinite(top)
+    return np.where(fin, np.ceil(np.where(fin, top, 0.0) * LOG2E) * LN2, top)
+
+
 def attend_block(pro: Prologue, b: int, h: int, qb: int, return_state: bool = False):
     """O9-O10 for the rows of Q block qb: output fp64 [rows, d].
 
@@ -374,7 +404,7 @@ def attend_block(pro: Prologue, b: int, h: int, qb: int, return_state: bool = Fa
     for kb in range(pro.nkb):
         c0, c1 = kb * g.bk, min(pro.N, (kb + 1) * g.bk)
         zb = z[:, c0:c1]
-        m_new = np.maximum(m, zb.max(axis=1))
+        m_new = np.maximum(m, block_top(zb, pro.max_ref))
         finite = np.isfinite(m_new)
         alpha = np.where(np.isfinite(m), np.exp(m - np.where(finite, m_new, 0.0)), 0.0)
         p = np.where(finite[:, None], np.exp(zb - np.where(finite, m_new, 0.0)[:, None]), 0.0)
@@ -395,7 +425,8 @@ def attend_block(pro: Prologue, b: int, h: int, qb: int, return_state: bool = Fa
     return out
 
 
-def fp8_midpoint_slack(pro: Prologue, b: int, h: int, qb: int, rel: float = 2.0 ** -14) -> np.ndarray:
+def fp8_midpoint_slack(pro: Prologue, b: int, h: int, qb: int, rel: float = 2.0 ** -14,
+                       int_rel: float | None = None) -> np.ndarray:
     """How far O of Q block qb may move when P~ decisions that sit on an E4M3 rounding midpoint go
     the other way: fp64 [rows, d].
 
@@ -406,7 +437,17 @@ def fp8_midpoint_slack(pro: Prologue, b: int, h: int, qb: int, rel: float = 2.0 
     codes moving by gaps g_j give O' - O = sum g_j (v_j - O) / (L + sum g_j), so
     |O' - O| <= sum g_j (|V_q[j] delta_V| + |O|) / (L - sum g_j); later rescalings scale the g_j
     of an earlier block by factors <= 1.  Zero where no decision is ambiguous (almost everywhere).
+
+    With the power-of-two running maximum (block_top), the integer k = ceil(log2(e) max z) is a
+    decision too: where a block's log2-unit maximum lies within `rel` of an integer that the
+    running maximum would take, k may come out one higher or lower.  That scales every later p
+    of the row by exactly 2 or 1/2, which E4M3 rounding commutes with except in its subnormal
+    range; acc and l scale alike, so O moves only through entries with p * P_r < 2^-5, each by
+    at most one subnormal step at the smaller scale (2^-8 in P~ units).  Those entries get that
+    gap from the ambiguous block on.  int_rel (default: rel) is that decision's tolerance.
     """
+    if int_rel is None:
+        int_rel = rel
     g = pro.geom
     hk = pro.kv_head(h)
     z = logits(pro, b, h, qb)
@@ -420,10 +461,18 @@ def fp8_midpoint_slack(pro: Prologue, b: int, h: int, qb: int, rel: float = 2.0 
     m = np.full(rows, -np.inf)
     gv = np.zeros((rows, pro.d))                       # sum g_j |V_q[j] delta_V|
     gs = np.zeros(rows)                                # sum g_j
+    shifted = np.zeros(rows, bool)                     # rows whose integer maximum was ambiguous
     for kb in range(pro.nkb):
         c0, c1 = kb * g.bk, min(pro.N, (kb + 1) * g.bk)
         zb = z[:, c0:c1]
-        m_new = np.maximum(m, zb.max(axis=1))
+        if pro.max_ref == "pow2":
+            t = zb.max(axis=1) * LOG2E                 # block maximum in log2 units
+            tf = np.isfinite(t)
+            n = np.rint(np.where(tf, t, 0.0))
+            k_run = np.where(np.isfinite(m), np.rint(np.where(np.isfinite(m), m, 0.0) * LOG2E), -np.inf)
+            near = tf & (np.abs(t - n) <= int_rel * np.maximum(1.0, np.abs(t))) & (n >= k_run)
+            shifted |= near
+        m_new = np.maximum(m, block_top(zb, pro.max_ref))
         finite = np.isfinite(m_new)
         p = np.where(finite[:, None], np.exp(zb - np.where(finite, m_new, 0.0)[:, None]), 0.0)
         x = p * p_r
@@ -433,6 +482,8 @@ def fp8_midpoint_slack(pro: Prologue, b: int, h: int, qb: int, rel: float = 2.0 
             jj = np.clip(j, 0, len(mids) - 1)
             hit = np.abs(x - mids[jj]) <= rel * np.maximum(x, mids[jj])
             gap = np.where(hit, np.maximum(gap, gaps[jj]), gap)
+        sub = shifted[:, None] & (p > 0) & (x < 2.0 ** -5)
+        gap = np.where(sub, np.maximum(gap, 2.0 ** -8), gap)
         gv += gap @ vmag[c0:c1]
         gs += gap.sum(axis=1)
         m = m_new
@@ -446,8 +497,9 @@ def p_quant_stats(pro: Prologue, b: int, h: int, qb: int) -> dict:
     """How the static range treats the probabilities of Q block qb (FP8 mode).
 
     Static range: P~ = E4M3sat(RN32(p * P_r)) with the fixed scale delta_P = 1 / P_r, because
-    0 < p <= 1 everywhere (p = e^(z - m) with m the running maximum).  Only a block that holds
-    its row's running maximum has max p = 1; in later blocks max p < 1, and an entry with
+    0 < p <= 1 everywhere (p = e^(z - m) with m the running maximum of block_top).  Only a block
+    that holds its row's running maximum has max p = 1 (max p in (1/2, 1] when the maximum is
+    rounded to a power of two); in later blocks max p is smaller, and an entry with
     p * P_r below half the smallest E4M3 subnormal (2^-10) is coded as zero.  The per-block
     form of the scale, delta_P = max(P~) / P_r, would code each block's entries relative to
     the block's own maximum instead; `zero_block_scale` counts the zeros that form would give
@@ -467,7 +519,7 @@ def p_quant_stats(pro: Prologue, b: int, h: int, qb: int) -> dict:
     for kb in range(pro.nkb):
         c0, c1 = kb * g.bk, min(pro.N, (kb + 1) * g.bk)
         zb = z[:, c0:c1]
-        m_new = np.maximum(m, zb.max(axis=1))
+        m_new = np.maximum(m, block_top(zb, pro.max_ref))
         live = np.isfinite(zb)
         p = np.where(live, np.exp(zb - np.where(np.isfinite(m_new), m_new, 0.0)[:, None]), 0.0)
         pt = fp8.round_sat((p * g.p_range).astype(F32))
@@ -499,7 +551,7 @@ def p_flushed_mass(pro: Prologue, b: int, h: int, qb: int) -> np.ndarray:
     for kb in range(pro.nkb):
         c0, c1 = kb * g.bk, min(pro.N, (kb + 1) * g.bk)
         zb = z[:, c0:c1]
-        m = np.maximum(m, zb.max(axis=1))
+        m = np.maximum(m, block_top(zb, pro.max_ref))
         live = np.isfinite(zb)
         p = np.where(live, np.exp(zb - m[:, None]), 0.0)
         pt = fp8.round_sat((p * g.p_range).astype(F32))

@@ -105,13 +105,21 @@ def test_weights_normalised(causal):
 
 def test_online_softmax_state():
     """l * e^m of the online pass equals the two-pass sum of e^z (P V unquantized, so the
-    weights are p itself)."""
+    weights are p itself); m is the row maximum, or (default reading) the smallest m >= it with
+    e^m a power of two."""
     q, k, v = make_inputs(custom(1, 1, 1, 384, 64), seed=16)
-    pro = sage.prologue(q, k, v, False, 8, quant_pv=False)
-    _, m, l = sage.attend_block(pro, 0, 0, 1, return_state=True)
-    z = sage.logits(pro, 0, 0, 1)
-    assert np.allclose(l * np.exp(m - z.max(axis=1)), np.exp(z - z.max(axis=1, keepdims=True)).sum(axis=1), rtol=1e-12)
-    assert np.array_equal(m, z.max(axis=1))
+    for max_ref in ("exact", "pow2"):
+        pro = sage.prologue(q, k, v, False, 8, quant_pv=False, max_ref=max_ref)
+        _, m, l = sage.attend_block(pro, 0, 0, 1, return_state=True)
+        z = sage.logits(pro, 0, 0, 1)
+        top = z.max(axis=1)
+        assert np.allclose(l * np.exp(m - top), np.exp(z - top[:, None]).sum(axis=1), rtol=1e-12)
+        if max_ref == "exact":
+            assert np.array_equal(m, top)
+        else:
+            e = m / math.log(2.0)                       # an integer, at most one above log2(e) max z
+            assert np.allclose(e, np.rint(e), rtol=0, atol=1e-9)
+            assert np.all(m >= top) and np.all(m - top < math.log(2.0))
 
 
 def test_quantized_accuracy_is_near_exact():
@@ -210,7 +218,7 @@ def _attend_perturbed(pro, b, h, qb, eps):
     acc = np.zeros((z.shape[0], pro.d))
     for kb in range(pro.nkb):
         zb = z[:, kb * g.bk:min(pro.N, (kb + 1) * g.bk)]
-        m_new = np.maximum(m, zb.max(axis=1))
+        m_new = np.maximum(m, sage.block_top(zb, pro.max_ref))
         alpha = np.where(np.isfinite(m), np.exp(m - m_new), 0.0)
         p = np.exp(zb - m_new[:, None])
         pt = fp8.round_sat((p * (1.0 + eps) * g.p_range).astype(np.float32))
@@ -236,4 +244,53 @@ def test_fp8_midpoint_slack_bounds_flipped_decisions():
                 d = np.abs(_attend_perturbed(pro, 0, h, qb, eps) - base)
                 assert np.all(d <= slack + 1e-12)
                 moved += int(np.count_nonzero(d > 1e-12))
+    assert moved > 0
+
+
+def _attend_shifted(pro, b, h, qb, flip, up):
+    """The online softmax and FP8 P~V of one Q block under the power-of-two running maximum,
+    where the rows flip[r] take, in every block, the integer maximum one higher (up) or one lower
+    than the oracle's: the alternative that a computation of the logits in fp32 can reach where
+    a maximum sits on an integer."""
+    g = pro.geom
+    hk = pro.kv_head(h)
+    z = sage.logits(pro, b, h, qb)
+    vq = fp8.decode(pro.v_codes[b, hk])
+    rows = z.shape[0]
+    m = np.full(rows, -np.inf)
+    l = np.zeros(rows)
+    acc = np.zeros((rows, pro.d))
+    off = np.zeros(rows)
+    for kb in range(pro.nkb):
+        zb = z[:, kb * g.bk:min(pro.N, (kb + 1) * g.bk)]
+        m_true = np.maximum(m, sage.block_top(zb, "pow2"))
+        off = np.where(flip, (1.0 if up else -1.0) * math.log(2.0), 0.0)
+        m_new = m_true + off
+        alpha = np.where(np.isfinite(m), np.exp(m - m_new), 0.0)
+        p = np.exp(zb - m_new[:, None])
+        pt = fp8.round_sat((p * g.p_range).astype(np.float32))
+        l = l * alpha + pt.sum(axis=1) / g.p_range
+        acc = acc * alpha[:, None] + pt @ vq[kb * g.bk:min(pro.N, (kb + 1) * g.bk)]
+        m = m_new
+    return acc * pro.v_delta[b, hk].astype(np.float64)[None, :] / (g.p_range * l[:, None])
+
+
+def test_fp8_slack_bounds_a_shifted_integer_maximum():
+    """With a tolerance wide enough that the integer-maximum decision counts as ambiguous in every
+    row (int_rel 1/2) and the midpoint tolerance switched off (rel 2^-60), a run whose rows all
+    take the integer maximum one higher from the start must stay within fp8_midpoint_slack: such a
+    shift scales every p by 1/2 and only the E4M3 subnormal range rounds differently.  (One lower
+    is an alternative only where the maximum sits on an integer, so p still stays <= 1; that is
+    the same scaling the other way.)  Wide logits put entries in the subnormal range."""
+    q, k, v = make_inputs(custom(1, 1, 1, 384, 64, False, 8, q_bias_std=1.0), seed=41)
+    q = (q.astype(np.float32) * 4).astype(np.float16)
+    pro = sage.prologue(q, k, v, False, 8, max_ref="pow2")
+    moved = 0
+    for qb in range(pro.nqb):
+        base = sage.attend_block(pro, 0, 0, qb)
+        slack = sage.fp8_midpoint_slack(pro, 0, 0, qb, rel=2.0 ** -60, int_rel=0.5)
+        flip = np.ones(base.shape[0], bool)
+        d = np.abs(_attend_shifted(pro, 0, 0, qb, flip, True) - base)
+        assert np.all(d <= slack + 1e-12)
+        moved += int(np.count_nonzero(d > 1e-12))
     assert moved > 0

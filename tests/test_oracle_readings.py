@@ -8,9 +8,19 @@ accurate: strictly lower RMSE where the P~V quantization dominates the error (IN
 within 1e-4 (relative) where the INT4-range QK quantization dominates it.
 
 Static range of P~.  P~ = E4M3sat(RN32(p * P_r)) with delta_P = 1 / P_r (a static range,
-valid because p <= 1).  Only the block holding a row's running maximum reaches p = 1, and
-entries with p * P_r at or below 2^-10 are coded as zero; p_quant_stats counts them.  Pinned
-here against scalar loops and the E4M3 grid.
+valid because p <= 1).  Only the block holding a row's running maximum reaches its largest p
+(in (1/2, 1] with the power-of-two maximum below), and entries with p * P_r at or below 2^-10
+are coded as zero; p_quant_stats counts them.  Pinned here against scalar loops and the E4M3
+grid.
+
+Running maximum.  The pages do not say which maximum the online softmax subtracts; any m at or
+above the row maximum gives the same unquantized softmax and keeps p <= 1.  The oracle takes
+the plain maximum; the maximum rounded up so that e^m is a power of two (block_top) is kept
+behind prologue(max_ref="pow2").  Against exact fp64 attention on the same four stand-ins and
+three seeds, the chosen reading must be at least as accurate: strictly lower RMSE where the
+P~V quantization dominates the error (INT8 QK) -- there the plain maximum codes the block's
+largest weight exactly as P_r -- and within 2e-3 (relative) under INT4-range QK, where the
+two differ by noise of that size either way.
 """
 import math
 
@@ -51,6 +61,30 @@ def test_row_sum_reading_no_less_accurate(name):
         assert rw < ru
 
 
+@pytest.mark.parametrize("name", list(SAMPLES))
+def test_running_max_reading_no_less_accurate(name):
+    w, causal, bits, pv_dominated = SAMPLES[name]
+    for seed in range(3):
+        q, k, v = make_inputs(w, seed=seed)
+        e = sage.exact_attention(q, k, v, causal)
+        rx, _, cx = _err(sage.sage_attention(q, k, v, causal, bits, max_ref="exact"), e)
+        rp, _, cp = _err(sage.sage_attention(q, k, v, causal, bits, max_ref="pow2"), e)
+        print(f"{name} seed {seed}: RMSE {rx:.6g} (plain maximum) vs {rp:.6g} (power of two); "
+              f"cos {cx:.7f} vs {cp:.7f}")
+        assert rx <= rp * (1 + 2e-3)
+        if pv_dominated:
+            assert rx < rp and cx > cp
+
+
+def test_running_max_readings_agree_without_pv_quantization():
+    """With P V unquantized nothing is rounded at the maximum's scale: both readings give the same
+    output up to fp64 rounding."""
+    q, k, v = make_inputs(custom(1, 2, 1, 300, 64, True, 8, q_bias_std=1.0), seed=3)
+    a = sage.sage_attention(q, k, v, True, 8, quant_pv=False, max_ref="exact")
+    b = sage.sage_attention(q, k, v, True, 8, quant_pv=False, max_ref="pow2")
+    assert np.abs(a - b).max() <= 1e-12 * np.abs(a).max()
+
+
 def test_row_sum_readings_agree_without_pv_quantization():
     """With P V unquantized the weights are p itself: both readings give the same output."""
     q, k, v = make_inputs(custom(1, 2, 1, 300, 64, True, 8, q_bias_std=1.0), seed=3)
@@ -63,6 +97,8 @@ def test_row_sum_switch_rejects_unknown_reading():
     q, k, v = make_inputs(custom(1, 1, 1, 8, 16), seed=0)
     with pytest.raises(ValueError):
         sage.prologue(q, k, v, row_sum="l1")
+    with pytest.raises(ValueError):
+        sage.prologue(q, k, v, max_ref="mean")
 
 
 def _scalar_counts(pro, b, h, qb):
@@ -114,25 +150,35 @@ def test_p_quant_stats_match_scalar_loops(causal):
     assert 0 < tot["rows_blocks_below_one"] < tot["rows_blocks"]
 
 
-def test_static_range_reaches_p_range_only_in_the_running_max_block():
-    """In the block that raises (or first sets) a row's running maximum the largest p is 1 and its
-    P~ is exactly P_r = 448; in every other block every p is below 1 (P~ may still round up to
-    448 from p > 432/448, the E4M3 midpoint below 448), so the static scale 1/P_r never saturates."""
+@pytest.mark.parametrize("max_ref", ["exact", "pow2"])
+def test_static_range_reaches_p_range_only_in_the_running_max_block(max_ref):
+    """Plain maximum: in the block that raises (or first sets) a row's running maximum the largest
+    p is 1 and its P~ is exactly P_r = 448; in every other block every p is below 1 (P~ may still
+    round up to 448 from p > 432/448, the E4M3 midpoint below 448), so the static scale 1/P_r
+    never saturates.  Power-of-two maximum: the largest p of the block that sets it lies in
+    (1/2, 1], so its P~ in [224, 448]; every p stays <= 1 and P~ <= 448."""
     w = custom(1, 1, 1, 512, 32, False, 8, q_bias_std=1.0)
     q, k, v = make_inputs(w, seed=9)
-    pro = sage.prologue(q, k, v, False, 8)
+    pro = sage.prologue(q, k, v, False, 8, max_ref=max_ref)
     g = pro.geom
     z = sage.logits(pro, 0, 0, 0)
     m = np.full(z.shape[0], -np.inf)
     others = 0
     for kb in range(pro.nkb):
         zb = z[:, kb * g.bk:(kb + 1) * g.bk]
-        m_new = np.maximum(m, zb.max(axis=1))
+        top = sage.block_top(zb, max_ref)
+        m_new = np.maximum(m, top)
         p = np.exp(zb - m_new[:, None])
         pt = fp8.round_sat((p * g.p_range).astype(np.float32)).max(axis=1)
-        holds = zb.max(axis=1) == m_new
-        assert np.all(p.max(axis=1)[holds] == 1.0) and np.all(pt[holds] == 448.0)
-        assert np.all(p.max(axis=1)[~holds] < 1.0) and np.all(pt <= 448.0)
+        holds = top == m_new
+        if max_ref == "exact":
+            assert np.all(p.max(axis=1)[holds] == 1.0) and np.all(pt[holds] == 448.0)
+            assert np.all(p.max(axis=1)[~holds] < 1.0)
+        else:
+            pm = p.max(axis=1)[holds]
+            assert np.all(pm > 0.5) and np.all(pm <= 1.0) and np.all(pt[holds] >= 224.0)
+            assert np.all(p.max(axis=1) <= 1.0)
+        assert np.all(pt <= 448.0)
         others += int(np.count_nonzero(~holds))
         m = m_new
     assert others > 0

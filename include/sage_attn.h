@@ -6,7 +6,8 @@
  *           Per-thread INT4 Quantization" (mlsanity.com page for arXiv 2411.10958),
  *           section "Abstract (arXiv)".
  *   [SA2c]  zhaifeiyue.github.io commentary on arXiv 2411.10958: the paragraphs on the
- *           paper's Sec. 3.4 (two-level accumulation) and on per-thread quantization.
+ *           paper's Sec. 3.4 (two-level accumulation), on per-thread quantization and on
+ *           smoothing K.
  *   [SA2pp] pith.science verdict on arXiv 2505.21136 (SageAttention2++), JSON keys
  *           "key_machinery" and "supporting_citations".
  *   [BLOG]  "SageAttention：大模型量化注意力加速实践指南" (blog.gitcode.com), sections on the
@@ -128,11 +129,15 @@ typedef struct {
   const int* cu_seqlens;  /* host int32 [B + 1] or NULL */
 } sage_problem_t;
 
-/* Workspace bytes for *p (written to *bytes); the _ex calls below take at least this much. */
+/* Workspace bytes for *p (written to *bytes); the _ex calls below take at least this much.
+ * (A sizing helper: the pages define no workspace; it holds the codes, scales, means and
+ * Delta_S of the steps cited above.)  Errors as for the _ex calls' validation. */
 int sage_attn_workspace_bytes_ex(const sage_problem_t* p, size_t* bytes);
 
 /* sage_attn_fwd / sage_attn_prologue / sage_attn_attend for any problem *p (same error and
- * stream rules).  The prologue and attend halves must be given the same *p and workspace. */
+ * stream rules): the same method on varlen batches, the NHD layout and bf16 inputs, which the
+ * blog page [BLOG] names in its precision-control tips (the arithmetic per sequence is that of
+ * [SA2]).  The prologue and attend halves must be given the same *p and workspace. */
 int sage_attn_fwd_ex(const sage_problem_t* p, const void* q, const void* k, const void* v,
                      void* o, void* workspace, size_t workspace_bytes, void* stream);
 int sage_attn_prologue_ex(const sage_problem_t* p, const void* q, const void* k, const void* v,
@@ -140,7 +145,8 @@ int sage_attn_prologue_ex(const sage_problem_t* p, const void* q, const void* k,
 int sage_attn_attend_ex(const sage_problem_t* p, void* o, void* workspace,
                         size_t workspace_bytes, void* stream);
 
-/* Bytes of workspace sage_attn_fwd needs for this problem (written to *bytes). */
+/* Bytes of workspace sage_attn_fwd needs for this problem (written to *bytes).  A sizing helper
+ * (no passage defines it); SAGE_ERR_INVALID_ARG / SAGE_ERR_UNSUPPORTED as for sage_attn_fwd. */
 int sage_attn_workspace_bytes(int B, int H, int Hkv, int N, int d, int causal, int qk_bits,
                               int pv_bits, size_t* bytes);
 
@@ -156,7 +162,9 @@ int sage_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, i
 /*
  * The two halves of sage_attn_fwd, for callers that time or schedule them separately.
  * sage_attn_prologue smooths and quantizes q, k, v into `workspace` (K/Q/V codes, scales,
- * means and the Delta_S bias).  sage_attn_attend runs the fused attention kernel on a
+ * means and the Delta_S bias: [SA2] abstract on smoothing Q and thread-granular quantization,
+ * [SA2c] on smoothing K, [SA2pp key_machinery] on per-channel FP8 V); sage_attn_attend is
+ * the online softmax, FP8 P~ and two-level P~V of [SA2] and [SA2c].  sage_attn_attend runs the fused attention kernel on a
  * workspace the prologue filled for the same (B, H, Hkv, N, d, causal, qk_bits, pv_bits) and writes
  * o; a workspace filled for another problem gives meaningless output.  Stream ordered;
  * same argument and error rules as sage_attn_fwd.
@@ -169,7 +177,9 @@ int sage_attn_attend(void* o, int B, int H, int Hkv, int N, int d, int causal, i
 
 /*
  * Test/debug: run the prologue only and copy its results, in plain layouts, to the
- * caller's device buffers (any pointer may be NULL to skip it):
+ * caller's device buffers (any pointer may be NULL to skip it).  The quantities are those of
+ * [SA2] (smoothing, thread-granular codes and scales, the mean(q) gamma(K)^T correction),
+ * [SA2c] (K smoothing) and [SA2pp key_machinery] (per-channel V):
  *   mu_k     fp32 [B, Hkv, d]            mean of K over all N keys
  *   k_codes  int8 [B, Hkv, N, d]         quantized smoothed K
  *   k_scales fp32 [B, Hkv, N]            scale of each key's group
@@ -198,7 +208,8 @@ int sage_quant_debug_ex(const sage_problem_t* p, const void* q, const void* k, c
 
 /*
  * Test/debug: run the prologue, then the attention kernel's own integer-MFMA QK^T code
- * path for query block qb of (b, h) against KV block kb, and copy the raw int32
+ * path ([SA2] abstract: QK^T on the low-bit integer codes) for query block qb of (b, h)
+ * against KV block kb, and copy the raw int32
  * accumulators to tile_out (device, int32 [bq, bk], row = query, column = key; keys past N
  * hold products with K's zero padding codes, rows past N products of the padded query rows'
  * codes, which no output reads).
@@ -244,10 +255,10 @@ int sage_attn_fwd_noalloc(const sage_problem_t* p, const void* q, const void* k,
  */
 int sage_mfma_rate_probe(int kind, int iters, void* sink, size_t sink_bytes, double* ops, void* stream);
 
-/* Static text for a status code. */
+/* Static text for a status code (library plumbing; no passage). */
 const char* sage_status_string(int status);
 
-/* Detail of the last SAGE_ERR_HIP on the calling thread ("" if none). */
+/* Detail of the last SAGE_ERR_HIP on the calling thread ("" if none; library plumbing). */
 const char* sage_last_error(void);
 
 #ifdef __cplusplus

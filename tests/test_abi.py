@@ -276,3 +276,24 @@ def test_noalloc_entry_point_checks(pkg):
     if _hip_device_count() == 0:            # no GPU: a valid call fails at the device lookup
         assert lib.sage_attn_fwd_noalloc(ok.ref, fake, fake, fake, fake, None) == -4
         assert len(lib.sage_last_error()) > 0
+
+
+def test_package_fails_loudly_without_its_library(tmp_path):
+    """A copy of the package without libsage_mi355x.so must refuse to import (ImportError naming
+    the missing library): there is no CPU or PyTorch fallback for the attention path."""
+    import shutil
+    import subprocess
+    import sys
+    dst = tmp_path / "quantized_attention_smooth_amd"
+    dst.mkdir()
+    for f in ("__init__.py", "build.py", "counters.py"):
+        shutil.copy(os.path.join(ROOT, "quantized_attention_smooth_amd", f), dst / f)
+    code = ("import sys; sys.path.insert(0, sys.argv[1])\n"
+            "try:\n"
+            "    import quantized_attention_smooth_amd\n"
+            "except ImportError as e:\n"
+            "    print('ImportError:', e); sys.exit(3)\n"
+            "sys.exit(0)\n")
+    r = subprocess.run([sys.executable, "-c", code, str(tmp_path)], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 3, r.stdout + r.stderr
+    assert "libsage_mi355x.so" in r.stdout and "not built" in r.stdout
